@@ -1,0 +1,229 @@
+"""Benchmark of the memory-aware MoE expert backward (LRMoE) on one MI355X.
+
+One step = one pass of the whole path (score -> select -> compact -> grouped GEMM
+backward -> scatter) over one layer invocation of the workload, inputs resident in
+HBM. Prints ONE JSON line. Default workload: the Qwen3-30B-A3B-shaped single-GPU
+expert share (32,768 tokens x top-8 = 262,144 pairs over 16 local experts, D=2048,
+intermediate 768, retention 0.6, bf16 with fp32 accumulation), seeded synthetic data.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "retained pairs/s through MoE expert backward; grouped-GEMM % of bf16 MFMA peak"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="qwen3_30b_a3b_share")
+    ap.add_argument("--rho", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-masked", action="store_true")
+    ap.add_argument("--cpu-sample-frac", type=float, default=0.4,
+                    help="fraction of the pairs (smallest experts first) the oracle runs on")
+    return ap.parse_args()
+
+
+def to_dev(np_mod, torch, a, dtype, dev):
+    a = np_mod.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np_mod.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(a).to(dev)
+
+
+def algorithmic_bytes(cfg, N, K_tot):
+    """Bytes each step reads once and writes once (storage dtype e; f32 scores/outputs)."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    T, D, F = cfg.T, cfg.D, cfg.F
+    score = (T * D + N * F) * e + N * (4 + 4 + 4)            # G, Phi, alpha, tok -> R
+    if cfg.swiglu:
+        compact = K_tot * (2 * D + 3 * F) * e * 2             # read + write Dlt, X, Phi, H rows
+    else:
+        compact = K_tot * (D + F) * e * 2
+    width = D if cfg.swiglu else F
+    scatter = K_tot * width * e + T * width * 4
+    return {"score": score, "compact": compact, "scatter": scatter}
+
+
+def gemm_flops(cfg, rows):
+    return (12 if cfg.swiglu else 4) * cfg.D * cfg.F * rows
+
+
+def cpu_baseline(pr, frac):
+    """The oracle, as it stands, on the smallest experts holding ~frac of the pairs."""
+    import numpy as np
+    import oracle
+    import synth
+
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) or 1
+    except Exception:  # pragma: no cover
+        threads = 1
+    r = pr.routing
+    cfg = pr.cfg
+    counts = np.diff(r.seg_off)
+    order = np.argsort(counts, kind="stable")
+    chosen, tot = [], 0
+    for e in order:
+        if tot >= frac * r.seg_off[-1]:
+            break
+        chosen.append(int(e))
+        tot += int(counts[e])
+    chosen.sort()
+    idx = np.concatenate([np.arange(r.seg_off[e], r.seg_off[e + 1]) for e in chosen])
+    seg = np.concatenate([[0], np.cumsum(counts[chosen])]).astype(np.int64)
+    q = pr.quota[chosen]
+    W1 = pr.W1[chosen] if pr.W1 is not None else None
+    t0 = time.perf_counter()
+    out = oracle.backward(G=pr.G, Phi=pr.Phi[idx], alpha=r.alpha[idx], tok=r.tok[idx], slot=r.slot[idx],
+                          seg_off=seg, quota=q, dtype=cfg.dtype, T=cfg.T, W2=pr.W2[chosen],
+                          X=pr.X, H=pr.H[idx] if pr.H is not None else None, W1=W1)
+    dt = time.perf_counter() - t0
+    kt = int(q.sum())
+    return {"value": kt / dt, "unit": "pairs/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(chosen)} smallest of {cfg.E} experts: {tot} pairs, {kt} retained, full T={cfg.T} token "
+                      f"rows; all five steps in fp64 ({dt:.1f} s)",
+            "seconds": dt, "retained_pairs": kt, "_out": out}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's expert share; --gpus {args.gpus} is not supported "
+              f"(multi-GPU sharding is described in DESIGN.md, not run).", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import load_recalibrated_expert_amd as lr
+    import synth
+
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.config]
+    rho = args.rho or cfg.rhos[0]
+    t0 = time.time()
+    pr = synth.make_problem(cfg, rho=rho)
+    gen_s = time.time() - t0
+    r = pr.routing
+    dt = cfg.dtype
+    P = lr.Problem(E=cfg.E, T=cfg.T, K=cfg.K, D=cfg.D, F=cfg.F, swiglu=cfg.swiglu,
+                   dtype=lr.BF16 if dt == "bf16" else lr.F32, seg_off=r.seg_off, quota=pr.quota, device=dev)
+    T_ = lambda a: to_dev(np, torch, a, dt, dev)  # noqa: E731
+    ins = dict(G=T_(pr.G), Phi=T_(pr.Phi), W2=T_(pr.W2), X=T_(pr.X) if pr.X is not None else None,
+               H=T_(pr.H) if pr.H is not None else None, W1=T_(pr.W1) if pr.W1 is not None else None,
+               alpha=torch.from_numpy(r.alpha).to(dev), tok=torch.from_numpy(r.tok).to(dev),
+               slot=torch.from_numpy(r.slot).to(dev))
+    print(f"# workload {cfg.name} rho={rho} N={P.N} K_tot={P.K_tot} generated in {gen_s:.1f}s", file=sys.stderr,
+          flush=True)
+
+    def run(mode, bufs, timing=None):
+        """One step; with `timing`, HIP events bracket each step's call on the launch stream."""
+        G, Phi, alpha, tok, slot = ins["G"], ins["Phi"], ins["alpha"], ins["tok"], ins["slot"]
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)] if timing is not None else None
+        rec = (lambda i: ev[i].record()) if ev else (lambda i: None)
+        rec(0)
+        R = lr.score(P, G, Phi, alpha, tok, R=bufs.get("R"))
+        bufs["R"] = R
+        rec(1)
+        sel, keep = lr.select(P, R, sel=bufs.get("sel"), keep=bufs.get("keep"))
+        bufs.setdefault("sel", sel)
+        bufs.setdefault("keep", keep)
+        rec(2)
+        c = lr.compact(P, G, Phi, alpha, tok, slot, sel=sel, keep=keep, X=ins["X"], H=ins["H"], mode=mode,
+                       out=bufs.get("c"))
+        bufs.setdefault("c", c)
+        rec(3)
+        PhiC = c["PhiC"] if mode == lr.COMPACT_PHYSICAL else Phi
+        HC = c.get("HC") if mode == lr.COMPACT_PHYSICAL else ins["H"]
+        g = lr.grouped_gemm_bwd(P, c["Dlt"], PhiC, ins["W2"], XC=c.get("XC"), HC=HC, W1=ins["W1"], mode=mode,
+                                out=bufs.get("g"))
+        bufs.setdefault("g", g)
+        rec(4)
+        ctok, cslot = (c["ctok"], c["cslot"]) if mode == lr.COMPACT_PHYSICAL else (tok, slot)
+        out = lr.scatter(P, g["dIn"], ctok, cslot, n_rows=P.rows(mode), out=bufs.get("out"))
+        bufs.setdefault("out", out)
+        rec(5)
+        if ev:
+            timing.append(ev)
+
+    def measure(mode):
+        bufs = {}
+        for _ in range(args.warmup):
+            run(mode, bufs)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(args.steps):
+            run(mode, bufs)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t
+        # second pass: per-step HIP events (same stream as the launches)
+        timing = []
+        for _ in range(args.steps):
+            run(mode, bufs, timing)
+        torch.cuda.synchronize()
+        names = ["score", "select", "compact", "grouped_gemm_bwd", "scatter"]
+        per = {n: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in timing])) for i, n in enumerate(names)}
+        return wall, per
+
+    wall, per = measure(lr.COMPACT_PHYSICAL)
+    ms = wall / args.steps * 1e3
+    value = P.K_tot * args.steps / wall
+    bytes_ = algorithmic_bytes(cfg, P.N, P.K_tot)
+    fl = gemm_flops(cfg, P.K_tot)
+    peak = BF16_PEAK_TFLOPS if dt == "bf16" else FP32_PEAK_TFLOPS
+    gemm_tf = fl / (per["grouped_gemm_bwd"] * 1e-3) / 1e12
+    kernels = {
+        "score": {"ms": per["score"], "GB/s": bytes_["score"] / per["score"] / 1e6,
+                  "hbm_frac": bytes_["score"] / per["score"] / 1e6 / HBM_PEAK_GBS},
+        "select": {"ms": per["select"]},
+        "compact": {"ms": per["compact"], "GB/s": bytes_["compact"] / per["compact"] / 1e6,
+                    "hbm_frac": bytes_["compact"] / per["compact"] / 1e6 / HBM_PEAK_GBS},
+        "grouped_gemm_bwd": {"ms": per["grouped_gemm_bwd"], "TFLOP/s": gemm_tf, "mfma_frac": gemm_tf / peak},
+        "scatter": {"ms": per["scatter"], "GB/s": bytes_["scatter"] / per["scatter"] / 1e6,
+                    "hbm_frac": bytes_["scatter"] / per["scatter"] / 1e6 / HBM_PEAK_GBS},
+    }
+    result = {
+        "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dt, "data": "synthetic (seeded; pages' shapes, no dataset)",
+        "config": {"workload": cfg.name, "T": cfg.T, "top_k": cfg.K, "local_experts": cfg.E, "D": cfg.D,
+                   "F": cfg.F, "swiglu": cfg.swiglu, "rho": rho, "pairs": P.N, "retained_pairs": P.K_tot,
+                   "mode": "physical compaction"},
+        "roofline": {"bound": "mfma", "achieved": gemm_tf, "peak": peak, "unit": "TFLOP/s",
+                     "frac": gemm_tf / peak, "traffic": None,
+                     "kernel": "lrmoe_grouped_gemm_bwd (FC2 dgrad+SwiGLU, FC1 dgrad, FC1+FC2 wgrad launches)",
+                     "flops_per_launch": fl},
+        "kernels": kernels,
+    }
+    if not args.no_masked:
+        mwall, mper = measure(lr.COMPACT_ZERO_MASKED)
+        mfl = gemm_flops(cfg, P.N)
+        result["masked_baseline"] = {
+            "ms_per_step": mwall / args.steps * 1e3, "retained_pairs_per_s": P.K_tot * args.steps / mwall,
+            "grouped_gemm_ms": mper["grouped_gemm_bwd"], "gemm_rows": P.N, "compact_rows": P.K_tot,
+            "gemm_flops": mfl, "speedup_of_compaction": (mwall / args.steps * 1e3) / ms,
+        }
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(pr, args.cpu_sample_frac)
+        cb.pop("_out", None)
+        result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

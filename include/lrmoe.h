@@ -1,0 +1,170 @@
+/*
+ * lrmoe.h - C ABI of the memory-aware MoE expert backward on one MI355X (gfx950).
+ *
+ * The library implements the backward-time calibration of the LRMoE paper
+ * ("LRMoE: Demand-Side Load Re-Calibration for Efficient MoE Training on
+ * Memory-Constrained Nodes"): its Algorithm 1 (section 3.3) scores every routed
+ * token-expert pair, keeps a fixed per-expert quota of the best pairs, packs the
+ * retained rows, runs the expert backward on the packed rows and maps the input
+ * gradients back. One call per step:
+ *
+ *   lrmoe_score            LRM score of every pair           (section 3.2, Eq. 3)
+ *   lrmoe_select           per-expert top-q under quotas      (section 3.3; appendix 7.2)
+ *   lrmoe_compact          packing into expert segments       (sections 3.1, 3.4, Figure 4)
+ *   lrmoe_grouped_gemm_bwd variable-size grouped GEMMs        (section 3.4)
+ *   lrmoe_scatter          inverse mapping to token order     (section 3.1)
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pairs are stored expert-major: expert e owns pair rows [seg_off[e], seg_off[e+1]).
+ * - Packed ("compact") rows are expert-major too: expert e owns packed rows
+ *   [cseg_off[e], cseg_off[e+1]) with cseg_off = exclusive prefix sum of the quotas.
+ *   Inside a segment the retained pairs keep their ascending original order.
+ * - Expert weights are stored [in x out], row-major: W2[e] is [F x D] (FC2, the
+ *   protected projection whose input is phi), W1[e] is [D x 2F] (FC1) whose columns
+ *   [0,F) are the gate and [F,2F) the up projection of a SwiGLU expert,
+ *   phi = silu(gate) * up.
+ * - "storage dtype" (problem.dtype) is the dtype of G, Phi, X, H, W1, W2 and of the
+ *   packed and gradient rows (Dlt, PhiC, XC, HC, dH, dIn). bf16 tensors hold raw
+ *   bf16 bit patterns. Weight gradients dW1/dW2, scores and scatter outputs are f32.
+ * - All pointers other than those documented "host" are device pointers. Row-major,
+ *   dense, 16-byte aligned; D and F must be multiples of 8.
+ * - Ownership: the caller owns every buffer. The library allocates nothing, frees
+ *   nothing and keeps no state between calls. Scratch memory comes through the
+ *   (ws, ws_bytes) arguments; lrmoe_workspace_size gives the size.
+ * - Streams: every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *   stream) and never synchronises it. Argument checks run on the host before any
+ *   launch; on error nothing is launched.
+ * - Quotas are fixed before the call (section 3.1: quotas remain fixed for the
+ *   invocation). A quota outside 0 <= q_e <= n_e is LRMOE_ERR_INFEASIBLE_QUOTA,
+ *   the analogue of Algorithm 1's "return Infeasible".
+ */
+#ifndef LRMOE_H
+#define LRMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same type as HIP's hipStream_t. */
+typedef struct ihipStream_t* lrmoe_stream_t;
+
+typedef enum lrmoe_status {
+  LRMOE_OK = 0,
+  LRMOE_ERR_INVALID_ARG = 1,       /* null pointer, bad size, non-monotone offsets ... */
+  LRMOE_ERR_INFEASIBLE_QUOTA = 2,  /* some q_e < 0 or q_e > n_e                         */
+  LRMOE_ERR_UNSUPPORTED = 3,       /* shape/dtype combination not implemented          */
+  LRMOE_ERR_WORKSPACE = 4,         /* ws is NULL or smaller than lrmoe_workspace_size  */
+  LRMOE_ERR_HIP = 5                /* a HIP launch failed                              */
+} lrmoe_status;
+
+typedef enum lrmoe_dtype { LRMOE_F32 = 0, LRMOE_BF16 = 1 } lrmoe_dtype;
+
+/* PHYSICAL: retained rows are copied into K_tot-row packed buffers (section 3.4).
+ * ZERO_MASKED: the same-shape baseline of section 3.4 - N-row buffers in which the
+ * dropped pairs' gradient rows are zero; the GEMMs then run over all N rows. */
+typedef enum lrmoe_compact_mode { LRMOE_COMPACT_PHYSICAL = 0, LRMOE_COMPACT_ZERO_MASKED = 1 } lrmoe_compact_mode;
+
+/* TOKEN: out[t] = sum of the rows of token t (back to token order).
+ * SLOT:  out[t*K + k] = the row of pair (t, k), every other row zero
+ *        ((token, routing-slot) positions in a zero-initialised buffer, section 3.1). */
+typedef enum lrmoe_scatter_mode { LRMOE_SCATTER_TOKEN = 0, LRMOE_SCATTER_SLOT = 1 } lrmoe_scatter_mode;
+
+typedef struct lrmoe_problem {
+  int32_t E;              /* local experts                                          */
+  int32_t T;              /* tokens                                                 */
+  int32_t K;              /* routing slots per token (top-K)                        */
+  int32_t D;              /* hidden size: width of g_t and x_t                      */
+  int32_t F;              /* expert intermediate size: width of phi_u               */
+  int32_t swiglu;         /* 1: SwiGLU experts (FC1 + FC2); 0: FC2 only             */
+  int32_t dtype;          /* lrmoe_dtype: storage dtype                             */
+  int32_t reserved;       /* must be 0                                              */
+  int64_t N;              /* routed pairs = seg_off[E]                              */
+  const int64_t* seg_off; /* host [E+1]: pair segment offsets, seg_off[0] = 0       */
+  const int32_t* quota;   /* host [E]: retention quotas q_e, fixed before the call  */
+} lrmoe_problem;
+
+const char* lrmoe_status_string(lrmoe_status s);
+const char* lrmoe_version(void);
+
+/* Host-only. Checks the problem (sizes, monotone offsets, N = seg_off[E], quotas
+ * 0 <= q_e <= n_e, supported dtype/shape) and returns K_tot = sum q_e and, if
+ * cseg_off is not NULL, the packed segment offsets (host [E+1]). Launches nothing. */
+lrmoe_status lrmoe_validate(const lrmoe_problem* p, int64_t* K_tot, int64_t* cseg_off);
+
+/* Host-only. Bytes of scratch that every entry point below needs for this problem
+ * and compact mode (one buffer serves all of them; calls on one stream may share it). */
+lrmoe_status lrmoe_workspace_size(const lrmoe_problem* p, lrmoe_compact_mode mode, size_t* bytes);
+
+/* Step 1 - LRM score (section 3.2, Proposition 3.1, Eq. 3; Algorithm 1's scoring step):
+ *   R[j] = alpha[j]^2 * ||G[tok[j]]||^2 * ||Phi[j]||^2   for every pair j < N.
+ * G [T x D] upstream gradient before the routing weight (appendix 7.1, Eq. 4-5),
+ * Phi [N x F] saved FC2 input per pair, alpha [N] f32, tok [N] int32 in [0,T).
+ * R [N] f32 out. Norms are accumulated in fp64; R is rounded once to f32. */
+lrmoe_status lrmoe_score(const lrmoe_problem* p, const void* G, const void* Phi, const float* alpha,
+                         const int32_t* tok, float* R, void* ws, size_t ws_bytes, lrmoe_stream_t stream);
+
+/* Step 2 - per-expert TopK under fixed quotas (section 3.3; appendix 7.2, Prop. 7.1):
+ * inside each segment keep the q_e largest R; among equal R the lower pair index wins.
+ * seg_off_d [E+1] int64, quota_d [E] int32, cseg_off_d [E+1] int64 are device copies of
+ * the problem's offsets, quotas and validated packed offsets.
+ * sel [K_tot] int32 out: retained pair indices, segment by segment, ascending.
+ * keep [N] uint8 out (may be NULL): 1 if retained, else 0. */
+lrmoe_status lrmoe_select(const lrmoe_problem* p, const float* R, const int64_t* seg_off_d,
+                          const int32_t* quota_d, const int64_t* cseg_off_d, int32_t* sel,
+                          uint8_t* keep, void* ws, size_t ws_bytes, lrmoe_stream_t stream);
+
+/* Step 3 - compaction (section 3.1 "compact runtime", section 3.4 / Figure 4).
+ * PHYSICAL, for packed row c < K_tot with j = sel[c], t = tok[j]:
+ *   Dlt[c]  = alpha[j] * G[t]   (weighted cotangent, Eq. 5; one rounding to the storage dtype,
+ *                                bf16 round-to-nearest-even of the exact product)
+ *   PhiC[c] = Phi[j];  XC[c] = X[t];  HC[c] = H[j];  ctok[c] = t;  cslot[c] = slot[j]
+ *   Dlt, XC [K_tot x D]; PhiC [K_tot x F]; HC [K_tot x 2F]; ctok, cslot [K_tot] int32.
+ *   X, H, XC, HC are used only when swiglu = 1 (else pass NULL). keep is ignored.
+ * ZERO_MASKED, for every pair j < N: Dlt[j] = keep[j] ? alpha[j] * G[tok[j]] : 0 and
+ *   XC[j] = X[tok[j]] (swiglu); sel is ignored; PhiC and HC must be NULL (the GEMMs read
+ *   Phi and H in place); ctok/cslot, if not NULL, receive copies of tok/slot. */
+lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, const int32_t* sel,
+                           const uint8_t* keep, const void* G, const void* Phi, const void* X,
+                           const void* H, const float* alpha, const int32_t* tok, const int32_t* slot,
+                           void* Dlt, void* PhiC, void* XC, void* HC, int32_t* ctok, int32_t* cslot,
+                           lrmoe_stream_t stream);
+
+/* Step 4 - packed expert backward, variable-size grouped GEMMs (section 3.4: the FC2
+ * and FC1 data- and weight-gradient GEMMs on the retained rows; section 3.1: the
+ * activation backward between them). Rows of expert e: [row_off[e], row_off[e+1]) with
+ * row_off = cseg_off (PHYSICAL) or seg_off (ZERO_MASKED); row_off_d is its device copy.
+ * In ZERO_MASKED mode pass Phi as PhiC and H as HC.
+ *   dW2[e] (+)= PhiC_e^T Dlt_e                        f32 [E x F x D]
+ *   dPhi      = Dlt_e W2[e]^T                         (internal)
+ *   dH        = [dPhi*up*silu'(gate), dPhi*silu(gate)] storage dtype [rows x 2F], out
+ *   dW1[e] (+)= XC_e^T dH_e                           f32 [E x D x 2F]
+ *   dIn       = dH_e W1[e]^T                          storage dtype [rows x D]
+ * with gate = HC[:, :F], up = HC[:, F:]. For swiglu = 0 only dW2 and dIn = dPhi
+ * [rows x F] are produced (dH, XC, HC, W1, dW1 must be NULL).
+ * accumulate = 0 overwrites dW1/dW2 (experts with no rows get 0); 1 adds to them.
+ * bf16: MFMA with fp32 accumulation. f32: fp32 FMA throughout. */
+lrmoe_status lrmoe_grouped_gemm_bwd(const lrmoe_problem* p, lrmoe_compact_mode mode,
+                                    const int64_t* row_off_d, const void* Dlt, const void* PhiC,
+                                    const void* XC, const void* HC, const void* W2, const void* W1,
+                                    float* dW2, float* dW1, void* dH, void* dIn, int32_t accumulate,
+                                    void* ws, size_t ws_bytes, lrmoe_stream_t stream);
+
+/* Step 5 - inverse mapping (section 3.1; Algorithm 1's ScatterWithZeros).
+ * rows [n_rows x width] of dtype rows_dtype; row c belongs to pair (ctok[c], cslot[c]),
+ * ctok in [0,T), cslot in [0,K), each (token, slot) at most once. Rows with an
+ * out-of-range index are ignored.
+ * TOKEN: out [T x width] f32 = per-token sums, added in slot order (deterministic).
+ * SLOT:  out [T*K x width] f32 = the row of each (t, k), zero where no row maps.
+ * out is overwritten. */
+lrmoe_status lrmoe_scatter(const lrmoe_problem* p, lrmoe_scatter_mode mode, int64_t n_rows, int32_t width,
+                           int32_t rows_dtype, const void* rows, const int32_t* ctok, const int32_t* cslot,
+                           float* out, void* ws, size_t ws_bytes, lrmoe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LRMOE_H */

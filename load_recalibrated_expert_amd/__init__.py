@@ -1,0 +1,203 @@
+"""Memory-aware MoE expert backward (LRMoE) on MI355X: Python binding of liblrmoe.
+
+The five steps of the LRMoE paper's backward-time calibration (Algorithm 1,
+section 3.3) are calls into ``liblrmoe.so`` (hand-written HIP for gfx950):
+
+    score -> select -> compact -> grouped_gemm_bwd -> scatter
+
+The functions here have the C entry points' names and only marshal arguments:
+torch tensors supply device memory and the current HIP stream. ``backward`` chains
+the five calls. Nothing falls back to another implementation; if the library is
+not built, the first call raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import (BF16, COMPACT_PHYSICAL, COMPACT_ZERO_MASKED, F32, SCATTER_SLOT, SCATTER_TOKEN,
+                   InfeasibleQuotaError, LrmoeError)
+
+__all__ = ["Problem", "score", "select", "compact", "grouped_gemm_bwd", "scatter", "backward",
+           "library", "BF16", "F32", "COMPACT_PHYSICAL", "COMPACT_ZERO_MASKED", "SCATTER_TOKEN",
+           "SCATTER_SLOT", "LrmoeError", "InfeasibleQuotaError"]
+
+
+def library() -> ctypes.CDLL:
+    return _lib.load()
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to liblrmoe must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+class Problem:
+    """Shapes, pair segments and quotas of one layer invocation (host + device copies).
+
+    seg_off: int64 [E+1] pair offsets per expert (pairs stored expert-major);
+    quota: int32 [E] retention quotas, fixed before the call."""
+
+    def __init__(self, *, E, T, K, D, F, swiglu, dtype, seg_off, quota, device="cuda"):
+        lib = library()
+        self.E, self.T, self.K, self.D, self.F = int(E), int(T), int(K), int(D), int(F)
+        self.swiglu, self.dtype = bool(swiglu), int(dtype)
+        self.c, self._keep = _lib.make_problem_struct(self.E, self.T, self.K, self.D, self.F, self.swiglu,
+                                                      self.dtype, seg_off, quota)
+        k_tot = ctypes.c_int64(0)
+        cseg = np.zeros(self.E + 1, dtype=np.int64)
+        _lib.check(lib.lrmoe_validate(ctypes.byref(self.c), ctypes.byref(k_tot),
+                                      cseg.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))), "lrmoe_validate")
+        self.N = int(self._keep[0][-1])
+        self.K_tot = int(k_tot.value)
+        self.seg_off = self._keep[0]
+        self.quota = self._keep[1]
+        self.cseg_off = cseg
+        self.device = torch.device(device)
+        self.seg_off_d = torch.from_numpy(self.seg_off).to(self.device)
+        self.quota_d = torch.from_numpy(self.quota).to(self.device)
+        self.cseg_off_d = torch.from_numpy(self.cseg_off).to(self.device)
+        self._ws = None
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == BF16 else torch.float32
+
+    def workspace_size(self, mode=COMPACT_PHYSICAL) -> int:
+        n = ctypes.c_size_t(0)
+        _lib.check(library().lrmoe_workspace_size(ctypes.byref(self.c), mode, ctypes.byref(n)),
+                   "lrmoe_workspace_size")
+        return int(n.value)
+
+    def workspace(self) -> torch.Tensor:
+        """One scratch buffer large enough for every call in either compact mode."""
+        if self._ws is None:
+            n = max(self.workspace_size(COMPACT_PHYSICAL), self.workspace_size(COMPACT_ZERO_MASKED))
+            self._ws = torch.empty(n, dtype=torch.uint8, device=self.device)
+        return self._ws
+
+    def rows(self, mode=COMPACT_PHYSICAL) -> int:
+        return self.K_tot if mode == COMPACT_PHYSICAL else self.N
+
+    def row_off_d(self, mode=COMPACT_PHYSICAL):
+        return self.cseg_off_d if mode == COMPACT_PHYSICAL else self.seg_off_d
+
+
+def score(p: Problem, G, Phi, alpha, tok, R=None, stream=None):
+    R = R if R is not None else torch.empty(p.N, dtype=torch.float32, device=p.device)
+    ws = p.workspace()
+    _lib.check(library().lrmoe_score(ctypes.byref(p.c), _ptr(G), _ptr(Phi), _ptr(alpha), _ptr(tok), _ptr(R),
+                                     _ptr(ws), ws.numel(), _stream(stream)), "lrmoe_score")
+    return R
+
+
+def select(p: Problem, R, sel=None, keep=None, want_keep=True, stream=None):
+    sel = sel if sel is not None else torch.empty(max(p.K_tot, 1), dtype=torch.int32, device=p.device)
+    if keep is None and want_keep:
+        keep = torch.empty(max(p.N, 1), dtype=torch.uint8, device=p.device)
+    ws = p.workspace()
+    _lib.check(library().lrmoe_select(ctypes.byref(p.c), _ptr(R), _ptr(p.seg_off_d), _ptr(p.quota_d),
+                                      _ptr(p.cseg_off_d), _ptr(sel), _ptr(keep), _ptr(ws), ws.numel(),
+                                      _stream(stream)), "lrmoe_select")
+    return sel[:p.K_tot], (keep[:p.N] if keep is not None else None)
+
+
+def compact(p: Problem, G, Phi, alpha, tok, slot, sel=None, keep=None, X=None, H=None,
+            mode=COMPACT_PHYSICAL, out=None, stream=None):
+    rows = p.rows(mode)
+    dt = p.torch_dtype
+    o = dict(out or {})
+    dev = p.device
+    o.setdefault("Dlt", torch.empty(max(rows, 1), p.D, dtype=dt, device=dev))
+    if mode == COMPACT_PHYSICAL:
+        o.setdefault("PhiC", torch.empty(max(rows, 1), p.F, dtype=dt, device=dev))
+        if p.swiglu:
+            o.setdefault("HC", torch.empty(max(rows, 1), 2 * p.F, dtype=dt, device=dev))
+    if p.swiglu:
+        o.setdefault("XC", torch.empty(max(rows, 1), p.D, dtype=dt, device=dev))
+    o.setdefault("ctok", torch.empty(max(rows, 1), dtype=torch.int32, device=dev))
+    o.setdefault("cslot", torch.empty(max(rows, 1), dtype=torch.int32, device=dev))
+    _lib.check(library().lrmoe_compact(
+        ctypes.byref(p.c), mode, _ptr(sel), _ptr(keep), _ptr(G), _ptr(Phi), _ptr(X), _ptr(H), _ptr(alpha),
+        _ptr(tok), _ptr(slot), _ptr(o["Dlt"]), _ptr(o.get("PhiC")), _ptr(o.get("XC")), _ptr(o.get("HC")),
+        _ptr(o["ctok"]), _ptr(o["cslot"]), _stream(stream)), "lrmoe_compact")
+    return {k: v[:rows] for k, v in o.items()}
+
+
+def grouped_gemm_bwd(p: Problem, Dlt, PhiC, W2, XC=None, HC=None, W1=None, mode=COMPACT_PHYSICAL,
+                     out=None, accumulate=False, stream=None):
+    rows = p.rows(mode)
+    dt = p.torch_dtype
+    dev = p.device
+    o = dict(out or {})
+    o.setdefault("dW2", torch.empty(p.E, p.F, p.D, dtype=torch.float32, device=dev))
+    if p.swiglu:
+        o.setdefault("dW1", torch.empty(p.E, p.D, 2 * p.F, dtype=torch.float32, device=dev))
+        o.setdefault("dH", torch.empty(max(rows, 1), 2 * p.F, dtype=dt, device=dev))
+        o.setdefault("dIn", torch.empty(max(rows, 1), p.D, dtype=dt, device=dev))
+    else:
+        o.setdefault("dIn", torch.empty(max(rows, 1), p.F, dtype=dt, device=dev))
+    ws = p.workspace()
+    _lib.check(library().lrmoe_grouped_gemm_bwd(
+        ctypes.byref(p.c), mode, _ptr(p.row_off_d(mode)), _ptr(Dlt), _ptr(PhiC), _ptr(XC), _ptr(HC), _ptr(W2),
+        _ptr(W1), _ptr(o["dW2"]), _ptr(o.get("dW1")), _ptr(o.get("dH")), _ptr(o["dIn"]), int(bool(accumulate)),
+        _ptr(ws), ws.numel(), _stream(stream)), "lrmoe_grouped_gemm_bwd")
+    res = dict(o)
+    res["dIn"] = o["dIn"][:rows]
+    if "dH" in o:
+        res["dH"] = o["dH"][:rows]
+    return res
+
+
+def scatter(p: Problem, rows_t, ctok, cslot, n_rows=None, mode=SCATTER_TOKEN, out=None, stream=None):
+    n_rows = rows_t.shape[0] if n_rows is None else n_rows
+    width = rows_t.shape[1]
+    rdt = BF16 if rows_t.dtype == torch.bfloat16 else F32
+    if out is None:
+        nout = p.T if mode == SCATTER_TOKEN else p.T * p.K
+        out = torch.empty(max(nout, 1), width, dtype=torch.float32, device=p.device)
+    ws = p.workspace()
+    _lib.check(library().lrmoe_scatter(ctypes.byref(p.c), mode, n_rows, width, rdt, _ptr(rows_t), _ptr(ctok),
+                                       _ptr(cslot), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
+               "lrmoe_scatter")
+    return out
+
+
+def backward(p: Problem, *, G, Phi, alpha, tok, slot, W2, X=None, H=None, W1=None, mode=COMPACT_PHYSICAL,
+             scatter_mode=SCATTER_TOKEN, bufs=None, stream=None):
+    """The whole path: score -> select -> compact -> grouped GEMMs -> scatter.
+
+    ``bufs`` (a dict, optional) carries preallocated outputs between calls; it is
+    filled on first use. Returns a dict of every intermediate and output."""
+    b = bufs if bufs is not None else {}
+    b["R"] = score(p, G, Phi, alpha, tok, R=b.get("R"), stream=stream)
+    sel, keep = select(p, b["R"], sel=b.get("sel_full"), keep=b.get("keep_full"), stream=stream)
+    b.setdefault("sel_full", sel)
+    b.setdefault("keep_full", keep)
+    c = compact(p, G, Phi, alpha, tok, slot, sel=sel, keep=keep, X=X, H=H, mode=mode, out=b.get("compact"),
+                stream=stream)
+    b.setdefault("compact", c)
+    PhiC = c["PhiC"] if mode == COMPACT_PHYSICAL else Phi
+    HC = c.get("HC") if mode == COMPACT_PHYSICAL else H
+    g = grouped_gemm_bwd(p, c["Dlt"], PhiC, W2, XC=c.get("XC"), HC=HC, W1=W1, mode=mode, out=b.get("gemm"),
+                         stream=stream)
+    b.setdefault("gemm", g)
+    if mode == COMPACT_PHYSICAL:
+        ctok, cslot = c["ctok"], c["cslot"]
+    else:
+        ctok, cslot = tok, slot
+    out = scatter(p, g["dIn"], ctok, cslot, n_rows=p.rows(mode), mode=scatter_mode, out=b.get("out"),
+                  stream=stream)
+    b.setdefault("out", out)
+    return {"R": b["R"], "sel": sel, "keep": keep, **c, **g, "out": out}

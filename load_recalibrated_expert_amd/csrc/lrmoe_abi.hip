@@ -1,0 +1,173 @@
+// C ABI of liblrmoe: host-side argument checks, workspace sizing and dispatch to the
+// kernels of each step. Every check runs before any launch; nothing here allocates,
+// synchronises or keeps state.
+#include <algorithm>
+#include <vector>
+
+#include "common.h"
+
+using namespace lrmoe;
+
+namespace {
+
+lrmoe_status check_problem(const lrmoe_problem* p, int64_t* K_tot, std::vector<int64_t>* cseg) {
+  if (!p || !p->seg_off || !p->quota) return LRMOE_ERR_INVALID_ARG;
+  if (p->reserved != 0) return LRMOE_ERR_INVALID_ARG;
+  if (p->E < 1 || p->E > 65535 || p->T < 0 || p->K < 1 || p->N < 0) return LRMOE_ERR_INVALID_ARG;
+  if (p->D < 8 || p->F < 8) return LRMOE_ERR_INVALID_ARG;
+  if (p->dtype != LRMOE_F32 && p->dtype != LRMOE_BF16) return LRMOE_ERR_UNSUPPORTED;
+  if (p->swiglu != 0 && p->swiglu != 1) return LRMOE_ERR_INVALID_ARG;
+  if (p->D % 8 != 0 || p->F % 8 != 0) return LRMOE_ERR_UNSUPPORTED;
+  if ((int64_t)p->T * p->K >= ((int64_t)1 << 31)) return LRMOE_ERR_UNSUPPORTED;
+  if (p->seg_off[0] != 0 || p->seg_off[p->E] != p->N) return LRMOE_ERR_INVALID_ARG;
+  if (p->N > (int64_t)p->T * p->K) return LRMOE_ERR_INVALID_ARG;  // each (token, slot) holds one pair
+  for (int e = 0; e < p->E; ++e)
+    if (p->seg_off[e + 1] < p->seg_off[e]) return LRMOE_ERR_INVALID_ARG;
+  int64_t k = 0;
+  if (cseg) cseg->assign(p->E + 1, 0);
+  for (int e = 0; e < p->E; ++e) {
+    const int64_t n = p->seg_off[e + 1] - p->seg_off[e];
+    const int64_t q = p->quota[e];
+    if (q < 0 || q > n) return LRMOE_ERR_INFEASIBLE_QUOTA;
+    k += q;
+    if (cseg) (*cseg)[e + 1] = k;
+  }
+  if (K_tot) *K_tot = k;
+  return LRMOE_OK;
+}
+
+size_t ws_need(const lrmoe_problem* p, lrmoe_compact_mode mode) {
+  std::vector<int64_t> cseg;
+  check_problem(p, nullptr, &cseg);
+  const int64_t* row_off = mode == LRMOE_COMPACT_ZERO_MASKED ? p->seg_off : cseg.data();
+  size_t b = align_up(sizeof(double) * (size_t)p->T, 256);  // score: token norms
+  b = std::max(b, select_ws_bytes(p));
+  b = std::max(b, gemm_ws_bytes(p, row_off));
+  b = std::max(b, scatter_ws_bytes(p));
+  return std::max<size_t>(b, 256);
+}
+
+#define LRMOE_TRY(x)                      \
+  do {                                    \
+    const lrmoe_status st_ = (x);         \
+    if (st_ != LRMOE_OK) return st_;      \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* lrmoe_status_string(lrmoe_status s) {
+  switch (s) {
+    case LRMOE_OK: return "ok";
+    case LRMOE_ERR_INVALID_ARG: return "invalid argument";
+    case LRMOE_ERR_INFEASIBLE_QUOTA: return "infeasible quota (need 0 <= q_e <= n_e)";
+    case LRMOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case LRMOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case LRMOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* lrmoe_version(void) { return "lrmoe 0.1 gfx950"; }
+
+lrmoe_status lrmoe_validate(const lrmoe_problem* p, int64_t* K_tot, int64_t* cseg_off) {
+  std::vector<int64_t> cseg;
+  int64_t k = 0;
+  LRMOE_TRY(check_problem(p, &k, &cseg));
+  if (K_tot) *K_tot = k;
+  if (cseg_off) std::copy(cseg.begin(), cseg.end(), cseg_off);
+  return LRMOE_OK;
+}
+
+lrmoe_status lrmoe_workspace_size(const lrmoe_problem* p, lrmoe_compact_mode mode, size_t* bytes) {
+  if (!bytes) return LRMOE_ERR_INVALID_ARG;
+  if (mode != LRMOE_COMPACT_PHYSICAL && mode != LRMOE_COMPACT_ZERO_MASKED) return LRMOE_ERR_INVALID_ARG;
+  LRMOE_TRY(check_problem(p, nullptr, nullptr));
+  *bytes = ws_need(p, mode);
+  return LRMOE_OK;
+}
+
+lrmoe_status lrmoe_score(const lrmoe_problem* p, const void* G, const void* Phi, const float* alpha,
+                         const int32_t* tok, float* R, void* ws, size_t ws_bytes, lrmoe_stream_t stream) {
+  LRMOE_TRY(check_problem(p, nullptr, nullptr));
+  if ((p->T > 0 && !G) || (p->N > 0 && (!Phi || !alpha || !tok || !R))) return LRMOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < align_up(sizeof(double) * (size_t)p->T, 256)) return LRMOE_ERR_WORKSPACE;
+  return launch_score(p, G, Phi, alpha, tok, R, (double*)ws, (hipStream_t)stream);
+}
+
+lrmoe_status lrmoe_select(const lrmoe_problem* p, const float* R, const int64_t* seg_off_d,
+                          const int32_t* quota_d, const int64_t* cseg_off_d, int32_t* sel, uint8_t* keep,
+                          void* ws, size_t ws_bytes, lrmoe_stream_t stream) {
+  int64_t K_tot = 0;
+  LRMOE_TRY(check_problem(p, &K_tot, nullptr));
+  if (!seg_off_d || !quota_d || !cseg_off_d) return LRMOE_ERR_INVALID_ARG;
+  if ((p->N > 0 && !R) || (K_tot > 0 && !sel)) return LRMOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < select_ws_bytes(p)) return LRMOE_ERR_WORKSPACE;
+  return launch_select(p, R, seg_off_d, quota_d, cseg_off_d, sel, keep, ws, (hipStream_t)stream);
+}
+
+lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, const int32_t* sel,
+                           const uint8_t* keep, const void* G, const void* Phi, const void* X, const void* H,
+                           const float* alpha, const int32_t* tok, const int32_t* slot, void* Dlt, void* PhiC,
+                           void* XC, void* HC, int32_t* ctok, int32_t* cslot, lrmoe_stream_t stream) {
+  int64_t K_tot = 0;
+  LRMOE_TRY(check_problem(p, &K_tot, nullptr));
+  const bool sw = p->swiglu != 0;
+  if (mode == LRMOE_COMPACT_PHYSICAL) {
+    if (K_tot == 0) return LRMOE_OK;
+    if (!sel || !G || !Phi || !alpha || !tok || !slot || !Dlt || !PhiC || !ctok || !cslot)
+      return LRMOE_ERR_INVALID_ARG;
+    if (sw && (!X || !H || !XC || !HC)) return LRMOE_ERR_INVALID_ARG;
+    if (!sw && (X || H || XC || HC)) return LRMOE_ERR_INVALID_ARG;
+    return launch_compact(p, K_tot, false, sel, nullptr, G, Phi, X, H, alpha, tok, slot, Dlt, PhiC, XC, HC,
+                          ctok, cslot, (hipStream_t)stream);
+  }
+  if (mode == LRMOE_COMPACT_ZERO_MASKED) {
+    if (p->N == 0) return LRMOE_OK;
+    if (!keep || !G || !alpha || !tok || !Dlt || PhiC || HC) return LRMOE_ERR_INVALID_ARG;
+    if ((ctok || cslot) && !slot) return LRMOE_ERR_INVALID_ARG;
+    if (sw && (!X || !XC)) return LRMOE_ERR_INVALID_ARG;
+    if (!sw && (X || XC)) return LRMOE_ERR_INVALID_ARG;
+    return launch_compact(p, p->N, true, nullptr, keep, G, Phi, X, H, alpha, tok, slot, Dlt, nullptr, XC,
+                          nullptr, ctok, cslot, (hipStream_t)stream);
+  }
+  return LRMOE_ERR_INVALID_ARG;
+}
+
+lrmoe_status lrmoe_grouped_gemm_bwd(const lrmoe_problem* p, lrmoe_compact_mode mode, const int64_t* row_off_d,
+                                    const void* Dlt, const void* PhiC, const void* XC, const void* HC,
+                                    const void* W2, const void* W1, float* dW2, float* dW1, void* dH, void* dIn,
+                                    int32_t accumulate, void* ws, size_t ws_bytes, lrmoe_stream_t stream) {
+  std::vector<int64_t> cseg;
+  LRMOE_TRY(check_problem(p, nullptr, &cseg));
+  if (mode != LRMOE_COMPACT_PHYSICAL && mode != LRMOE_COMPACT_ZERO_MASKED) return LRMOE_ERR_INVALID_ARG;
+  if (accumulate != 0 && accumulate != 1) return LRMOE_ERR_INVALID_ARG;
+  const int64_t* row_off_h = mode == LRMOE_COMPACT_ZERO_MASKED ? p->seg_off : cseg.data();
+  const int64_t rows = row_off_h[p->E];
+  if (!row_off_d || !W2 || !dW2) return LRMOE_ERR_INVALID_ARG;
+  if (rows > 0 && (!Dlt || !PhiC || !dIn)) return LRMOE_ERR_INVALID_ARG;
+  if (p->swiglu) {
+    if (!W1 || !dW1 || (rows > 0 && (!XC || !HC || !dH))) return LRMOE_ERR_INVALID_ARG;
+  } else if (W1 || dW1 || dH || XC || HC) {
+    return LRMOE_ERR_INVALID_ARG;
+  }
+  if (ws_bytes < gemm_ws_bytes(p, row_off_h) || (!ws && gemm_ws_bytes(p, row_off_h) > 0))
+    return LRMOE_ERR_WORKSPACE;
+  return launch_grouped_gemm_bwd(p, row_off_h, row_off_d, Dlt, PhiC, XC, HC, W2, W1, dW2, dW1, dH, dIn,
+                                 accumulate, ws, (hipStream_t)stream);
+}
+
+lrmoe_status lrmoe_scatter(const lrmoe_problem* p, lrmoe_scatter_mode mode, int64_t n_rows, int32_t width,
+                           int32_t rows_dtype, const void* rows, const int32_t* ctok, const int32_t* cslot,
+                           float* out, void* ws, size_t ws_bytes, lrmoe_stream_t stream) {
+  LRMOE_TRY(check_problem(p, nullptr, nullptr));
+  if (mode != LRMOE_SCATTER_TOKEN && mode != LRMOE_SCATTER_SLOT) return LRMOE_ERR_INVALID_ARG;
+  if (rows_dtype != LRMOE_F32 && rows_dtype != LRMOE_BF16) return LRMOE_ERR_UNSUPPORTED;
+  if (n_rows < 0 || n_rows > p->N || width < 8 || width % 8 != 0) return LRMOE_ERR_INVALID_ARG;
+  if (!out || (n_rows > 0 && (!rows || !ctok || !cslot))) return LRMOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < scatter_ws_bytes(p)) return LRMOE_ERR_WORKSPACE;
+  return launch_scatter(p, mode, n_rows, width, rows_dtype, rows, ctok, cslot, out, ws, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+// Step 5: inverse mapping (LRMoE paper, section 3.1: returned input-gradient contributions
+// are scatter-added at their original token and routing-slot positions in zero-initialised
+// dense buffers; Algorithm 1's ScatterWithZeros).
+//
+// Each packed row belongs to one (token, slot) position and each position holds at most one
+// pair, so a [T x K] map from position to packed row is built first (fill -1, then one
+// store per row: no conflicts). Token mode then sums, per token, the rows of its K slots in
+// slot order - a fixed order, so the result is deterministic without atomics. Slot mode
+// copies each position's row or writes zeros.
+#include "common.h"
+
+namespace lrmoe {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void map_fill_kernel(int64_t n, int32_t* __restrict__ map) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) map[i] = -1;
+}
+
+__global__ __launch_bounds__(kThreads) void map_scatter_kernel(int64_t rows, int T, int K,
+                                                               const int32_t* __restrict__ ctok,
+                                                               const int32_t* __restrict__ cslot,
+                                                               int32_t* __restrict__ map) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= rows) return;
+  const int t = ctok[c], k = cslot[c];
+  if (t >= 0 && t < T && k >= 0 && k < K) map[(int64_t)t * K + k] = (int32_t)c;
+}
+
+// 8 elements of a row -> f32, from 16 bytes (bf16) or 32 bytes (f32).
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* __restrict__ rows, int64_t row, int width, int c8, float v[8]) {
+  if (BF16) {
+    const uint4 x = ld_stream((const uint4*)((const uint16_t*)rows + row * width) + c8);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    const float4* p = (const float4*)((const float*)rows + row * width) + 2 * c8;
+    const uint4 a = ld_stream(p), b = ld_stream(p + 1);
+    v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y); v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+    v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y); v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+  }
+}
+
+__device__ __forceinline__ void store8(float* __restrict__ out, int64_t row, int width, int c8, const float v[8]) {
+  float4* p = (float4*)(out + row * width) + 2 * c8;
+  p[0] = make_float4(v[0], v[1], v[2], v[3]);
+  p[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
+// One wavefront per token: out[t] = sum over k of rows[map[t][k]], in slot order.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void token_reduce_kernel(int T, int K, int width,
+                                                                const int32_t* __restrict__ map,
+                                                                const void* __restrict__ rows,
+                                                                float* __restrict__ out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  if (t >= T) return;
+  const int n8 = width / 8;
+  for (int c8 = lane; c8 < n8; c8 += kWave) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int k = 0; k < K; ++k) {
+      const int32_t r = map[t * K + k];
+      if (r < 0) continue;
+      float v[8];
+      load8<BF16>(rows, r, width, c8, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
+    store8(out, t, width, c8, acc);
+  }
+}
+
+// One wavefront per (token, slot) position: copy its row or write zeros.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void slot_copy_kernel(int64_t positions, int width,
+                                                             const int32_t* __restrict__ map,
+                                                             const void* __restrict__ rows,
+                                                             float* __restrict__ out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t q = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  if (q >= positions) return;
+  const int32_t r = map[q];
+  const int n8 = width / 8;
+  for (int c8 = lane; c8 < n8; c8 += kWave) {
+    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (r >= 0) load8<BF16>(rows, r, width, c8, v);
+    store8(out, q, width, c8, v);
+  }
+}
+
+}  // namespace
+
+size_t scatter_ws_bytes(const lrmoe_problem* p) { return align_up(sizeof(int32_t) * (size_t)p->T * p->K, 256); }
+
+lrmoe_status launch_scatter(const lrmoe_problem* p, int mode, int64_t n_rows, int width, int rows_dtype,
+                            const void* rows, const int32_t* ctok, const int32_t* cslot, float* out,
+                            void* ws, hipStream_t s) {
+  const int64_t positions = (int64_t)p->T * p->K;
+  if (positions == 0) return LRMOE_OK;
+  int32_t* map = (int32_t*)ws;
+  map_fill_kernel<<<(unsigned)ceil_div(positions, kThreads), kThreads, 0, s>>>(positions, map);
+  if (n_rows > 0)
+    map_scatter_kernel<<<(unsigned)ceil_div(n_rows, kThreads), kThreads, 0, s>>>(n_rows, p->T, p->K, ctok,
+                                                                                 cslot, map);
+  const bool bf16 = rows_dtype == LRMOE_BF16;
+  constexpr int per_block = kThreads / kWave;
+  if (mode == LRMOE_SCATTER_TOKEN) {
+    const unsigned g = (unsigned)ceil_div(p->T, per_block);
+    if (bf16) token_reduce_kernel<true><<<g, kThreads, 0, s>>>(p->T, p->K, width, map, rows, out);
+    else token_reduce_kernel<false><<<g, kThreads, 0, s>>>(p->T, p->K, width, map, rows, out);
+  } else {
+    const unsigned g = (unsigned)ceil_div(positions, per_block);
+    if (bf16) slot_copy_kernel<true><<<g, kThreads, 0, s>>>(positions, width, map, rows, out);
+    else slot_copy_kernel<false><<<g, kThreads, 0, s>>>(positions, width, map, rows, out);
+  }
+  return launch_status();
+}
+
+}  // namespace lrmoe

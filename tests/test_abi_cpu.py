@@ -1,0 +1,123 @@
+"""C-ABI library checks that need no GPU: it loads, exports every symbol the header
+declares, and its host-side validation answers before any launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from load_recalibrated_expert_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "lrmoe.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\*|lrmoe_status)\s+(lrmoe_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_five_steps():
+    d = _declared()
+    for name in ("lrmoe_score", "lrmoe_select", "lrmoe_compact", "lrmoe_grouped_gemm_bwd", "lrmoe_scatter",
+                 "lrmoe_validate", "lrmoe_workspace_size", "lrmoe_status_string", "lrmoe_version"):
+        assert name in d
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\sT\s+(lrmoe_\w+)", out))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+    assert set(_lib.EXPORTS) <= exported
+
+
+def _problem(E=3, T=10, K=2, D=64, F=32, swiglu=1, dtype=_lib.BF16, counts=(5, 0, 7), quota=(3, 0, 7)):
+    seg = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    return _lib.make_problem_struct(E, T, K, D, F, swiglu, dtype, seg, np.array(quota, dtype=np.int32))
+
+
+def _validate(p):
+    k = ctypes.c_int64(-1)
+    cseg = np.full(p.E + 1, -7, dtype=np.int64)
+    st = _lib.load().lrmoe_validate(ctypes.byref(p), ctypes.byref(k), cseg.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)))
+    return st, k.value, cseg
+
+
+def test_validate_accepts_and_returns_packed_offsets():
+    p, keep = _problem()
+    st, k, cseg = _validate(p)
+    assert st == _lib.OK and k == 10 and cseg.tolist() == [0, 3, 3, 10]
+
+
+def test_validate_worked_example_offsets():
+    # loads [4,2,3] retained [3,1,2] (LRMoE Figure 4) -> packed offsets [0,3,4,6]
+    p, keep = _problem(counts=(4, 2, 3), quota=(3, 1, 2), T=5)
+    st, k, cseg = _validate(p)
+    assert st == _lib.OK and k == 6 and cseg.tolist() == [0, 3, 4, 6]
+
+
+@pytest.mark.parametrize("quota", [(6, 0, 7), (3, -1, 7), (3, 1, 7)])
+def test_validate_rejects_infeasible_quota(quota):
+    p, keep = _problem(quota=quota)
+    assert _validate(p)[0] == _lib.ERR_INFEASIBLE_QUOTA
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(D=60), _lib.ERR_UNSUPPORTED),
+    (dict(F=12), _lib.ERR_UNSUPPORTED),
+    (dict(dtype=7), _lib.ERR_UNSUPPORTED),
+    (dict(T=5), _lib.ERR_INVALID_ARG),          # N = 12 pairs > T*K = 10 positions
+    (dict(K=0), _lib.ERR_INVALID_ARG),
+])
+def test_validate_rejects_bad_shapes(kw, expect):
+    p, keep = _problem(**kw)
+    assert _validate(p)[0] == expect
+
+
+def test_validate_rejects_bad_flags():
+    p, keep = _problem()
+    p.swiglu = 2
+    assert _validate(p)[0] == _lib.ERR_INVALID_ARG
+    p.swiglu = 1
+    p.reserved = 1
+    assert _validate(p)[0] == _lib.ERR_INVALID_ARG
+
+
+def test_validate_rejects_non_monotone_offsets():
+    p, keep = _problem()
+    keep[0][1] = 9  # seg_off = [0, 9, 5, 12]
+    assert _validate(p)[0] == _lib.ERR_INVALID_ARG
+
+
+def test_workspace_size_and_host_side_rejections():
+    lib = _lib.load()
+    p, keep = _problem()
+    n = ctypes.c_size_t(0)
+    assert lib.lrmoe_workspace_size(ctypes.byref(p), _lib.COMPACT_PHYSICAL, ctypes.byref(n)) == _lib.OK
+    assert n.value >= 256
+    # null device pointers and missing workspaces are refused on the host, before any launch
+    assert lib.lrmoe_score(ctypes.byref(p), None, None, None, None, None, None, 0, None) == _lib.ERR_INVALID_ARG
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.lrmoe_score(ctypes.byref(p), fake, fake, fake, fake, fake, None, 0, None) == _lib.ERR_WORKSPACE
+    assert lib.lrmoe_select(ctypes.byref(p), fake, fake, fake, fake, fake, None, None, 0, None) == _lib.ERR_WORKSPACE
+    assert lib.lrmoe_scatter(ctypes.byref(p), 0, 3, 12, _lib.BF16, fake, fake, fake, fake, fake, 1 << 20,
+                             None) == _lib.ERR_INVALID_ARG  # width not a multiple of 8
+    assert lib.lrmoe_compact(ctypes.byref(p), 5, *([None] * 15), None) == _lib.ERR_INVALID_ARG
+    q, keep2 = _problem(quota=(6, 0, 7))
+    assert lib.lrmoe_grouped_gemm_bwd(ctypes.byref(q), 0, *([fake] * 11), 0, fake, 1 << 30,
+                                      None) == _lib.ERR_INFEASIBLE_QUOTA
+    assert _lib.status_string(_lib.ERR_INFEASIBLE_QUOTA).startswith("infeasible")
+
+
+def test_product_path_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "load_recalibrated_expert_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f
+                assert "synth" not in re.findall(r"^\s*(?:import|from)\s+(\w+)", text, re.M), f

@@ -33,7 +33,7 @@ def parse():
     ap.add_argument("--rho", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-masked", action="store_true")
-    ap.add_argument("--cpu-sample-frac", type=float, default=0.4,
+    ap.add_argument("--cpu-sample-frac", type=float, default=1.0,
                     help="fraction of the pairs (smallest experts first) the oracle runs on")
     return ap.parse_args()
 

@@ -6,10 +6,12 @@ Tolerances (derived in the design notes from the arithmetic each step does):
 * score: |R - R_oracle| <= 1e-6 R_oracle.
 * select / compaction indices: bit-exact (selection taken on f32 scores on both sides).
 * compaction rows: bit-exact copies; Dlt = bf16 nearest of the exact alpha*g.
-* FC2 weight gradient: inputs are exact bf16, fp32 accumulation -> rel. Frobenius <= 1e-4.
-* dH: bf16 output rounding -> per element |err| <= 2^-8 |ref| + 1e-5 rms(ref).
-* FC1 weight gradient and input gradients consume bf16 dH -> rel. Frobenius <= 5e-3
-  per expert (spec bar 2e-2), per packed row <= 2e-2.
+* GEMM outputs against the exact oracle: the packed gradient rows Dlt and dH are stored
+  in bf16 (relative rounding error <= 2^-9, rms ~1.1e-3), so weight gradients, dH and
+  input gradients get rel. Frobenius <= 5e-3 per expert (spec bar 2e-2), and every
+  packed input-gradient row <= 2e-2.
+* GEMM outputs against the oracle fed the bf16-stored Dlt: FC2 weight gradient rel.
+  Frobenius <= 1e-5 (fp32 accumulation only); dH per element <= 2^-8 |ref| + 2e-5 rms(row).
 * f32 path: rel. Frobenius <= 1e-5.
 """
 import numpy as np
@@ -104,27 +106,47 @@ def test_grouped_gemm(case):
     E = pr.cfg.E
     cseg = ref["cseg_off"]
     f32 = pr.cfg.dtype == "f32"
+    bar = 1e-5 if f32 else 2e-2      # spec bar
+    derived = 1e-5 if f32 else 5e-3  # bf16 storage of Dlt and dH: ~1.1e-3 rms each
     dW2 = as_f64(res["dW2"])
     for e in range(E):
-        assert rel_fro(dW2[e], ref["dW2"][e]) <= (1e-5 if f32 else 1e-4), f"{name}: dW2 expert {e}"
+        assert rel_fro(dW2[e], ref["dW2"][e]) <= derived, f"{name}: dW2 expert {e}"
     dIn = as_f64(res["dIn"])
     key = "dXC" if pr.cfg.swiglu else "dPhi"
-    assert rel_fro(dIn, ref[key]) <= (1e-5 if f32 else 5e-3)
-    for c in range(dIn.shape[0]):
-        if np.linalg.norm(ref[key][c]) > 0:
-            assert rel_fro(dIn[c], ref[key][c]) <= (1e-5 if f32 else 2e-2), f"{name}: row {c}"
+    assert rel_fro(dIn, ref[key]) <= derived
+    num = np.linalg.norm(dIn - ref[key], axis=1)
+    den = np.linalg.norm(ref[key], axis=1)
+    assert np.all(num <= bar * np.maximum(den, 1e-30)), f"{name}: worst row {np.max(num / np.maximum(den, 1e-30))}"
     if pr.cfg.swiglu:
         dW1 = as_f64(res["dW1"])
         for e in range(E):
-            assert rel_fro(dW1[e], ref["dW1"][e]) <= (1e-5 if f32 else 5e-3), f"{name}: dW1 expert {e}"
+            assert rel_fro(dW1[e], ref["dW1"][e]) <= derived, f"{name}: dW1 expert {e}"
             if cseg[e] == cseg[e + 1]:
                 assert np.all(dW1[e] == 0) and np.all(dW2[e] == 0)
-        dH = as_f64(res["dH"])
-        if f32:
-            assert rel_fro(dH, ref["dH"]) <= 1e-5
-        else:
-            rms = np.sqrt(np.mean(ref["dH"] ** 2))
-            assert np.all(np.abs(dH - ref["dH"]) <= 2 ** -8 * np.abs(ref["dH"]) + 1e-5 * rms), name
+        assert rel_fro(as_f64(res["dH"]), ref["dH"]) <= derived
+
+
+def test_grouped_gemm_at_storage_precision(case):
+    """Same GEMMs against the oracle fed the packed gradient rows at their stored bf16
+    precision (the pages' BF16 storage): FC2 weight gradient and dH then differ only by
+    fp32 accumulation and the final bf16 rounding of dH."""
+    name, pr, s, res, ref = case
+    if pr.cfg.dtype != "bf16" or not np.array_equal(res["sel"].cpu().numpy(), ref["sel"]):
+        pytest.skip("bf16 problems with identical selections only")
+    dlt = oracle.widen(oracle.round_bf16(ref["Dlt"]), "bf16")
+    cseg = ref["cseg_off"]
+    if pr.cfg.swiglu:
+        dW1, dW2, dH, dXC = oracle.swiglu_expert_backward(cseg, dlt, ref["PhiC"], ref["XC"], ref["HC"],
+                                                          oracle.widen(pr.W1, "bf16"), oracle.widen(pr.W2, "bf16"))
+        got = as_f64(res["dH"])
+        rms = np.sqrt(np.mean(dH ** 2, axis=1, keepdims=True))
+        assert np.all(np.abs(got - dH) <= 2 ** -8 * np.abs(dH) + 2e-5 * rms), name
+    else:
+        dW2, dPhi = oracle.linear_expert_backward(cseg, dlt, ref["PhiC"], oracle.widen(pr.W2, "bf16"))
+        assert rel_fro(as_f64(res["dIn"]), dPhi) <= 4e-3  # one bf16 rounding of the output
+    got2 = as_f64(res["dW2"])
+    for e in range(pr.cfg.E):
+        assert rel_fro(got2[e], dW2[e]) <= 1e-5, f"{name}: dW2 expert {e}"
 
 
 def test_scatter_token_order(case):
@@ -159,7 +181,7 @@ def test_zero_masked_equals_compact(case):
     torch.cuda.synchronize()
     f32 = pr.cfg.dtype == "f32"
     tol = 1e-5 if f32 else 5e-3
-    assert rel_fro(as_f64(m["dW2"]), ref["dW2"]) <= (1e-5 if f32 else 1e-4)
+    assert rel_fro(as_f64(m["dW2"]), ref["dW2"]) <= tol
     assert rel_fro(as_f64(m["out"]), ref["out"]) <= tol
     if pr.cfg.swiglu:
         assert rel_fro(as_f64(m["dW1"]), ref["dW1"]) <= tol

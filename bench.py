@@ -33,6 +33,9 @@ def parse():
     ap.add_argument("--rho", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-masked", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="before timing, run 3 device-to-device copies of this many MiB (a plain copy kernel "
+                         "of known size, used to scale hardware byte counters)")
     ap.add_argument("--cpu-sample-frac", type=float, default=1.0,
                     help="fraction of the pairs (smallest experts first) the oracle runs on")
     return ap.parse_args()
@@ -130,6 +133,15 @@ def main():
                slot=torch.from_numpy(r.slot).to(dev))
     print(f"# workload {cfg.name} rho={rho} N={P.N} K_tot={P.K_tot} generated in {gen_s:.1f}s", file=sys.stderr,
           flush=True)
+
+    if args.copy_calib_mib > 0:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def run(mode, bufs, timing=None):
         """One step; with `timing`, HIP events bracket each step's call on the launch stream."""

@@ -31,12 +31,13 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-constexpr int BM = 256, BN = 256, BK = 64, NTHR = 256;
-constexpr int kTileChunks = BM * BK / 8;  // uint4 per operand tile per stage
-constexpr int64_t kKcMax = 16384;        // max packed rows per weight-gradient chunk
-
-__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+constexpr int BM = 256, BN = 256, BK = 32, NTHR = 256, STAGES = 4;
+constexpr int kTileU4 = BM * BK * 2 / 16;  // uint4 per operand tile per stage (16 KB)
+constexpr int64_t kKcMax = 16384;          // max packed rows per weight-gradient chunk
+constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past num_records: the load returns 0
 
 __device__ __forceinline__ int xcd_remap(int b, int n) {
   const int x = b & 7, i = b >> 3;
@@ -44,100 +45,146 @@ __device__ __forceinline__ int xcd_remap(int b, int n) {
   return x * q + min(x, r) + i;
 }
 
-// ---------------------------------------------------------------- global -> LDS staging
-
-// Operand stored [rows x K] with K contiguous: tile rows [0, rows_valid), k in [k0, k0+64).
-__device__ __forceinline__ void load_kc(const uint16_t* __restrict__ base, int64_t ld, int rows_valid, int k0,
-                                        int kend, uint4 (&v)[8]) {
-  const int ch = threadIdx.x & 7, r0 = threadIdx.x >> 3;
-  const int k = k0 + ch * 8;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = r0 + 32 * i;
-    v[i] = (r < rows_valid && k < kend) ? *(const uint4*)(base + (int64_t)r * ld + k) : make_uint4(0, 0, 0, 0);
-  }
-}
-__device__ __forceinline__ void store_kc(uint4* __restrict__ lds, const uint4 (&v)[8]) {
-  const int ch = threadIdx.x & 7, r0 = threadIdx.x >> 3;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = r0 + 32 * i;
-    lds[r * 8 + (ch ^ swz(r))] = v[i];
-  }
+// Raw buffer resource over [p, p + 2 GiB): loads at offsets >= 2^31 return zeros without
+// touching memory, which is how tile edges are masked without branches.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7FFFFFFF, 0x00020000);
 }
 
-// Operand stored [K x cols] with cols contiguous (row index = reduction index): tile
-// columns [0, 256) of which [0, mn_valid) exist, reduction rows [k0, k0+64) below kend.
-__device__ __forceinline__ void load_mn(const uint16_t* __restrict__ base, int64_t ld, int mn_valid, int k0,
-                                        int kend, uint4 (&v)[8]) {
-  const int mc = threadIdx.x & 31, kg = threadIdx.x >> 5;
-  const bool col_ok = mc * 8 < mn_valid;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int k = k0 + kg * 8 + i;
-    v[i] = (col_ok && k < kend) ? *(const uint4*)(base + (int64_t)k * ld + mc * 8) : make_uint4(0, 0, 0, 0);
-  }
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land at
+// lds_wave_base + 16 l (lds_wave_base is wave-uniform). Out-of-range offsets write zeros.
+__device__ __forceinline__ void dma16(rsrc_t r, const uint4* lds_wave_base, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds_wave_base), 16, off, 0, 0, 0);
 }
-// 8x8 transpose of 16-bit values: v[k] holds columns m0..m7 of reduction row k; out row m
-// holds reduction rows k0..k7 of column m, which is what an MFMA fragment wants.
-__device__ __forceinline__ void store_mn(uint4* __restrict__ lds, const uint4 (&v)[8]) {
-  const int mc = threadIdx.x & 31, kg = threadIdx.x >> 5;
-  uint32_t w[8][4];
+
+// ---------------------------------------------------------------- LDS layouts
+//
+// K-contiguous operand (data-gradient GEMMs): a stage holds 256 rows x 32 K values, 64 bytes
+// per row as four 16-byte chunks; chunk c of row r sits in slot c ^ ((r >> 2) & 3), so the
+// 16-byte fragment reads of 16 consecutive rows cover all 64 banks.
+//
+// Row-major-in-K operand (weight-gradient GEMMs): a stage holds 32 K rows x 256 columns,
+// 512 bytes per row as eight 64-byte segments; segment s of row k sits in slot s ^ (k & 3),
+// so the 4-row transpose reads of one half-wavefront cover all 64 banks.
+
+__device__ __forceinline__ int swz_k(int row) { return (row >> 2) & 3; }
+
+// Direct-to-LDS loader of a K-contiguous operand. Wave w fills tile rows [64 w, 64 w + 64)
+// with 4 instructions of 16 rows each; lane l loads row 16 j + l/4 (+64 w) at the chunk that
+// belongs in slot l % 4.
+struct DmaK {
+  rsrc_t r;
+  uint32_t off[4];
+  int col;    // first K element of this lane's chunk within the stage
+  int wbase;  // uint4 offset of this wave's 4 KB region in a stage
+  __device__ __forceinline__ void init(const uint16_t* p, int64_t ld, int rows_valid) {
+    r = make_rsrc(p);
+    const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    col = ((l & 3) ^ ((l >> 4) & 3)) * 8;
+    wbase = w * 256;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    w[k][0] = v[k].x;
-    w[k][1] = v[k].y;
-    w[k][2] = v[k].z;
-    w[k][3] = v[k].w;
+    for (int j = 0; j < 4; ++j) {
+      const int row = w * 64 + j * 16 + (l >> 2);
+      off[j] = row < rows_valid ? (uint32_t)((row * ld + col) * 2) : kOOB;
+    }
   }
+  __device__ __forceinline__ void issue(const uint4* stage, int k0, int kend) const {
+    const bool kok = k0 + col < kend;
 #pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int p = m >> 1;
-    const uint32_t sel = (m & 1) ? 0x07060302u : 0x05040100u;
-    uint4 o;
-    o.x = __builtin_amdgcn_perm(w[1][p], w[0][p], sel);
-    o.y = __builtin_amdgcn_perm(w[3][p], w[2][p], sel);
-    o.z = __builtin_amdgcn_perm(w[5][p], w[4][p], sel);
-    o.w = __builtin_amdgcn_perm(w[7][p], w[6][p], sel);
-    const int r = mc * 8 + m;
-    lds[r * 8 + (kg ^ swz(r))] = o;
+    for (int j = 0; j < 4; ++j)
+      dma16(r, stage + wbase + j * 64, (kok && off[j] != kOOB) ? off[j] + (uint32_t)k0 * 2u : kOOB);
   }
+};
+
+// Direct-to-LDS loader of a row-major-in-K operand. Wave w fills K rows [8 w, 8 w + 8) with
+// 4 instructions of 2 rows each; lane l loads row 2 j + l/32 (+8 w) at the chunk that belongs
+// in 16-byte slot l % 32.
+struct DmaT {
+  rsrc_t r;
+  uint32_t off[4];
+  int row[4];
+  int wbase;
+  __device__ __forceinline__ void init(const uint16_t* p, int64_t ld, int mn_valid) {
+    r = make_rsrc(p);
+    const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    wbase = w * 256;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k = w * 8 + j * 2 + (l >> 5);
+      const int pc = l & 31;
+      const int c = (((pc >> 2) ^ (k & 3)) << 2) | (pc & 3);  // logical 16-byte chunk
+      row[j] = k;
+      off[j] = c * 8 < mn_valid ? (uint32_t)((k * ld + c * 8) * 2) : kOOB;
+    }
+  }
+  __device__ __forceinline__ void issue(const uint4* stage, int k0, int kend, uint32_t kstep) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dma16(r, stage + wbase + j * 64,
+            (off[j] != kOOB && k0 + row[j] < kend) ? off[j] + (uint32_t)k0 * kstep : kOOB);
+  }
+};
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+
+// MFMA fragment (32 columns from `col0`, 16 reduction rows from `k0`) out of a row-major-in-K
+// stage with the gfx950 LDS transpose read. Within each 16-lane group the read hands lane
+// i the (i%4)-th 16-bit element of the 8-byte segments addressed by lanes i/4, i/4+4,
+// i/4+8, i/4+12 of the group. So lane s of group g addresses reduction row
+// k0 + 8*(g/2) + s/4 at columns col0 + 16*(g%2) + 4*(s%4): lane i then holds column
+// col0 + 16*(g%2) + i at 4 consecutive reduction rows, and two reads (rows +0..3, +4..7)
+// give the 8 consecutive K values of the MFMA operand layout.
+__device__ __forceinline__ bf16x8_t frag_tr(const uint4* stage, int col0, int k0, int lane) {
+  const int g = lane >> 4, sl = lane & 15;
+  const int k = k0 + 8 * (g >> 1) + (sl >> 2);
+  const int col = col0 + 16 * (g & 1) + 4 * (sl & 3);
+  const int pcol = ((((col >> 5) ^ (k & 3))) << 5) | (col & 31);  // rows k and k+4 share k & 3
+  const __attribute__((address_space(3))) short* base =
+      (const __attribute__((address_space(3))) short*)(const lds_void_t*)stage;
+  const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base + k * BM + pcol));
+  const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base + (k + 4) * BM + pcol));
+  typedef short v8s_t __attribute__((ext_vector_type(8)));
+  const v8s_t both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, both);
 }
 
 // ---------------------------------------------------------------- MFMA on one LDS stage
 
-__device__ __forceinline__ void mma_stage(const uint4* __restrict__ la, const uint4* __restrict__ lb,
-                                          f32x16_t (&acc)[4][4], int wm, int wn, int lane) {
-  const int lr = lane & 31, lk = lane >> 5;
+// la holds the 256 output rows' operand (m), lb the 256 output columns' operand (n).
+// The MFMA takes the n fragment first, so each lane's accumulator holds 4 consecutive
+// output columns of one output row: acc[nb][mb][v] is output row
+// wm*128 + mb*32 + lane%32, column wn*128 + nb*32 + 8*(v/4) + 4*(lane/32) + v%4.
+template <bool TN>
+__device__ __forceinline__ void load_frags(const uint4* __restrict__ la, const uint4* __restrict__ lb, int kk,
+                                           int wm, int wn, int lane, bf16x8_t (&fa)[4], bf16x8_t (&fb)[4]) {
+  if (TN) {
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int ch = kk * 2 + lk;
-    bf16x8_t a[4], b[4];
+    for (int i = 0; i < 4; ++i) {
+      fa[i] = frag_tr(la, wm * 128 + i * 32, kk * 16, lane);
+      fb[i] = frag_tr(lb, wn * 128 + i * 32, kk * 16, lane);
+    }
+  } else {
+    const int lr = lane & 31, ch = kk * 2 + (lane >> 5);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ra = wm * 128 + i * 32 + lr;
       const int rb = wn * 128 + i * 32 + lr;
-      a[i] = __builtin_bit_cast(bf16x8_t, la[ra * 8 + (ch ^ swz(ra))]);
-      b[i] = __builtin_bit_cast(bf16x8_t, lb[rb * 8 + (ch ^ swz(rb))]);
+      fa[i] = __builtin_bit_cast(bf16x8_t, la[ra * 4 + (ch ^ swz_k(ra))]);
+      fb[i] = __builtin_bit_cast(bf16x8_t, lb[rb * 4 + (ch ^ swz_k(rb))]);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
   }
 }
 
-// acc[i][j][v] sits at tile row wm*128 + i*32 + 8*(v/4) + 4*(lane/32) + v%4,
-// tile column wn*128 + j*32 + lane%32.
-#define LRMOE_FOR_ACC(BODY)                                                               \
-  _Pragma("unroll") for (int i = 0; i < 4; ++i) _Pragma("unroll") for (int j = 0; j < 4; ++j) \
-      _Pragma("unroll") for (int v = 0; v < 16; ++v) {                                    \
-    const int tr = wm * 128 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);          \
-    const int tc = wn * 128 + j * 32 + (lane & 31);                                       \
-    const float val = acc[i][j][v];                                                       \
-    BODY                                                                                  \
-  }
+__device__ __forceinline__ void mma16(const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[4], f32x16_t (&acc)[4][4]) {
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+      acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb], acc[nb][mb], 0, 0, 0);
+}
 
 __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
 #pragma unroll
@@ -147,6 +194,73 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 }
+
+struct StageBufs {
+  uint4 a[STAGES][kTileU4];
+  uint4 b[STAGES][kTileU4];
+};
+
+// The K loop shared by every bf16 GEMM. Four LDS stages of 32 K values per operand are
+// filled by direct loads issued three stages ahead. At the top of stage kt each wave waits
+// for its own loads of stage kt+1, and one barrier then makes stage kt+1 visible and frees
+// stage kt-1's buffer, into which stage kt+3 is loaded. The first fragments of every stage
+// are read during the previous stage, so MFMAs start right after the barrier.
+template <bool TN, class LA, class LB>
+__device__ __forceinline__ void gemm_mainloop(StageBufs& sm, const LA& la, const LB& lb, int kend, uint32_t kstep_a,
+                                              uint32_t kstep_b, f32x16_t (&acc)[4][4], int wm, int wn, int lane) {
+  const int nk = (kend + BK - 1) / BK;
+  if (nk <= 0) return;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) {
+    if constexpr (TN) {
+      la.issue(sm.a[s], s * BK, kend, kstep_a);
+      lb.issue(sm.b[s], s * BK, kend, kstep_b);
+    } else {
+      la.issue(sm.a[s], s * BK, kend);
+      lb.issue(sm.b[s], s * BK, kend);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (16 & 0xF) | ((16 >> 4) << 14));  // vmcnt(16): stage 0 landed
+  __syncthreads();
+  bf16x8_t fa[2][4], fb[2][4];
+  load_frags<TN>(sm.a[0], sm.b[0], 0, wm, wn, lane, fa[0], fb[0]);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & (STAGES - 1), nxt = (kt + 1) & (STAGES - 1), ld = (kt + 3) & (STAGES - 1);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (8 & 0xF) | ((8 >> 4) << 14));  // vmcnt(8): stage kt+1 landed
+    __syncthreads();
+    if constexpr (TN) {
+      la.issue(sm.a[ld], (kt + 3) * BK, kend, kstep_a);
+      lb.issue(sm.b[ld], (kt + 3) * BK, kend, kstep_b);
+    } else {
+      la.issue(sm.a[ld], (kt + 3) * BK, kend);
+      lb.issue(sm.b[ld], (kt + 3) * BK, kend);
+    }
+    // Each phase issues the fragment reads of the next K16 step, then runs the 16 MFMAs of
+    // the current one; the fences keep the compiler from sinking the reads behind the MFMAs.
+    load_frags<TN>(sm.a[cur], sm.b[cur], 1, wm, wn, lane, fa[1], fb[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    mma16(fa[0], fb[0], acc);
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags<TN>(sm.a[nxt], sm.b[nxt], 0, wm, wn, lane, fa[0], fb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    mma16(fa[1], fb[1], acc);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the loop
+}
+
+// Visits the accumulator as runs of 4 consecutive output columns:
+// BODY sees tile row `tm`, first tile column `tn` and the 4 values v0..v3.
+#define LRMOE_FOR_RUNS(BODY)                                                       \
+  _Pragma("unroll") for (int nb = 0; nb < 4; ++nb)                                 \
+  _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                 \
+  _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                  \
+    const int tm = wm * 128 + mb * 32 + (lane & 31);                               \
+    const int tn = wn * 128 + nb * 32 + 8 * q + 4 * (lane >> 5);                   \
+    const float v0 = acc[nb][mb][4 * q], v1 = acc[nb][mb][4 * q + 1];              \
+    const float v2 = acc[nb][mb][4 * q + 2], v3 = acc[nb][mb][4 * q + 3];          \
+    BODY                                                                           \
+  }
 
 // ---------------------------------------------------------------- data-gradient kernel
 
@@ -168,11 +282,12 @@ struct DgradArgs {
   int F;
 };
 
+__device__ __forceinline__ float silu_fwd(float g, float s) { return g * s; }
+
 template <int EPI>
 __global__ __launch_bounds__(NTHR) void dgrad_kernel(DgradArgs g) {
-  __shared__ uint4 lds[2][2][kTileChunks];
+  __shared__ StageBufs lds;
   const int b = xcd_remap(blockIdx.x, gridDim.x);
-  // locate the tile: experts in order, ceil(m_e/BM) x ntn tiles each
   int e = 0, local = b;
   int64_t r0 = 0, m = 0;
   for (; e < g.E; ++e) {
@@ -188,52 +303,60 @@ __global__ __launch_bounds__(NTHR) void dgrad_kernel(DgradArgs g) {
   const int rows_valid = (int)min<int64_t>(BM, m - (int64_t)mt * BM);
   const int n0 = nt * BN;
   const int n_valid = min(BN, g.N - n0);
-  const uint16_t* Ab = g.A + row0 * g.lda;
-  const uint16_t* Bb = g.W + (int64_t)e * g.w_estride + (int64_t)n0 * g.ldw;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   f32x16_t acc[4][4];
   zero_acc(acc);
-  uint4 ra[8], rb[8];
-  const int nk = (g.K + BK - 1) / BK;
-  load_kc(Ab, g.lda, rows_valid, 0, g.K, ra);
-  load_kc(Bb, g.ldw, n_valid, 0, g.K, rb);
-  store_kc(lds[0][0], ra);
-  store_kc(lds[0][1], rb);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      load_kc(Ab, g.lda, rows_valid, (kt + 1) * BK, g.K, ra);
-      load_kc(Bb, g.ldw, n_valid, (kt + 1) * BK, g.K, rb);
-    }
-    mma_stage(lds[cur][0], lds[cur][1], acc, wm, wn, lane);
-    if (more) {
-      store_kc(lds[cur ^ 1][0], ra);
-      store_kc(lds[cur ^ 1][1], rb);
-    }
-    __syncthreads();
-  }
+  DmaK la, lb;
+  la.init(g.A + row0 * g.lda, g.lda, rows_valid);
+  lb.init(g.W + (int64_t)e * g.w_estride + (int64_t)n0 * g.ldw, g.ldw, n_valid);
+  gemm_mainloop<false>(lds, la, lb, g.K, 0, 0, acc, wm, wn, lane);
 
   if (EPI == EPI_SWIGLU) {
     const int64_t ld = 2 * (int64_t)g.F;
-    LRMOE_FOR_ACC({
-      if (tr < rows_valid && tc < n_valid) {
-        const int64_t row = row0 + tr;
-        const int f = n0 + tc;
-        const float gate = bf16_to_f32(g.HC[row * ld + f]);
-        const float up = bf16_to_f32(g.HC[row * ld + g.F + f]);
-        const float s = 1.0f / (1.0f + expf(-gate));
-        const float silu = gate * s;
-        const float dsilu = s * (1.0f + gate * (1.0f - s));
-        g.out[row * ld + f] = (uint16_t)f32_to_bf16(val * up * dsilu);
-        g.out[row * ld + g.F + f] = (uint16_t)f32_to_bf16(val * silu);
+    const uint16_t* __restrict__ hc = g.HC;
+    uint16_t* __restrict__ dh = g.out;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int tm = wm * 128 + mb * 32 + (lane & 31);
+        const bool row_ok = tm < rows_valid;
+        const int64_t rowb = (row0 + tm) * ld;
+        uint2 gv[4], uv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int tn = wn * 128 + nb * 32 + 8 * q + 4 * (lane >> 5);
+          if (row_ok && tn < n_valid) {
+            gv[q] = *(const uint2*)(hc + rowb + n0 + tn);
+            uv[q] = *(const uint2*)(hc + rowb + g.F + n0 + tn);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int tn = wn * 128 + nb * 32 + 8 * q + 4 * (lane >> 5);
+          if (row_ok && tn < n_valid) {
+            const float gate[4] = {bf16_lo(gv[q].x), bf16_hi(gv[q].x), bf16_lo(gv[q].y), bf16_hi(gv[q].y)};
+            const float up[4] = {bf16_lo(uv[q].x), bf16_hi(uv[q].x), bf16_lo(uv[q].y), bf16_hi(uv[q].y)};
+            float dg[4], du[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float dphi = acc[nb][mb][4 * q + c];
+              const float s = 1.0f / (1.0f + expf(-gate[c]));
+              dg[c] = dphi * up[c] * (s * (1.0f + gate[c] * (1.0f - s)));
+              du[c] = dphi * silu_fwd(gate[c], s);
+            }
+            *(uint2*)(dh + rowb + n0 + tn) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+            *(uint2*)(dh + rowb + g.F + n0 + tn) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+          }
+        }
       }
-    })
+    }
   } else {
-    LRMOE_FOR_ACC({
-      if (tr < rows_valid && tc < n_valid) g.out[(row0 + tr) * g.ldo + n0 + tc] = (uint16_t)f32_to_bf16(val);
+    uint16_t* __restrict__ out = g.out;
+    LRMOE_FOR_RUNS({
+      if (tm < rows_valid && tn < n_valid)
+        *(uint2*)(out + (row0 + tm) * g.ldo + n0 + tn) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
     })
   }
 }
@@ -314,10 +437,9 @@ __global__ __launch_bounds__(NTHR) void wgrad_plan_kernel(WgradArgs g) {
 }
 
 __global__ __launch_bounds__(NTHR) void wgrad_kernel(WgradArgs g) {
-  __shared__ uint4 lds[2][2][kTileChunks];
+  __shared__ StageBufs lds;
   const int b = xcd_remap(blockIdx.x, gridDim.x);
-  // binary search over the planned experts
-  int lo = 0, hi = g.E;  // find r with prefix[r] <= b < prefix[r+1]
+  int lo = 0, hi = g.E;  // planned expert r with prefix[r] <= b < prefix[r+1]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (g.plan_prefix[mid] <= b) lo = mid;
@@ -337,45 +459,33 @@ __global__ __launch_bounds__(NTHR) void wgrad_kernel(WgradArgs g) {
   const int klen = (int)max<int64_t>(0, min<int64_t>(kc, m - k_begin));
   const int m0 = mt * BM, n0 = nt * BN;
   const int m_valid = min(BM, T.M - m0), n_valid = min(BN, T.N - n0);
-  const uint16_t* Ab = T.A + (r0 + k_begin) * T.lda + m0;
-  const uint16_t* Bb = T.B + (r0 + k_begin) * T.ldb + n0;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
   f32x16_t acc[4][4];
   zero_acc(acc);
-  const int nk = (klen + BK - 1) / BK;
-  if (nk > 0) {
-    uint4 ra[8], rb[8];
-    load_mn(Ab, T.lda, m_valid, 0, klen, ra);
-    load_mn(Bb, T.ldb, n_valid, 0, klen, rb);
-    store_mn(lds[0][0], ra);
-    store_mn(lds[0][1], rb);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        load_mn(Ab, T.lda, m_valid, (kt + 1) * BK, klen, ra);
-        load_mn(Bb, T.ldb, n_valid, (kt + 1) * BK, klen, rb);
-      }
-      mma_stage(lds[cur][0], lds[cur][1], acc, wm, wn, lane);
-      if (more) {
-        store_mn(lds[cur ^ 1][0], ra);
-        store_mn(lds[cur ^ 1][1], rb);
-      }
-      __syncthreads();
-    }
-  }
+  DmaT la, lb;
+  la.init(T.A + (r0 + k_begin) * T.lda + m0, T.lda, m_valid);
+  lb.init(T.B + (r0 + k_begin) * T.ldb + n0, T.ldb, n_valid);
+  gemm_mainloop<true>(lds, la, lb, klen, (uint32_t)(T.lda * 2), (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
+
   if (s > 1) {
-    float* p = g.partials + (g.plan_pbase[e] + (int64_t)chunk * tiles + rem) * (int64_t)(BM * BN);
-    LRMOE_FOR_ACC({ p[tr * BN + tc] = val; })
+    float* __restrict__ p = g.partials + (g.plan_pbase[e] + (int64_t)chunk * tiles + rem) * (int64_t)(BM * BN);
+    LRMOE_FOR_RUNS({ *(float4*)(p + tm * BN + tn) = make_float4(v0, v1, v2, v3); })
   } else {
-    float* o = T.out + (int64_t)e * T.M * T.N;
+    float* __restrict__ o = T.out + (int64_t)e * T.M * T.N;
     const bool accum = g.accumulate != 0;
-    LRMOE_FOR_ACC({
-      if (tr < m_valid && tc < n_valid) {
-        float* q = o + (int64_t)(m0 + tr) * T.N + n0 + tc;
-        *q = accum ? *q + val : val;
+    LRMOE_FOR_RUNS({
+      if (tm < m_valid && tn < n_valid) {
+        float4* q4 = (float4*)(o + (int64_t)(m0 + tm) * T.N + n0 + tn);
+        float4 val = make_float4(v0, v1, v2, v3);
+        if (accum) {
+          const float4 old = *q4;
+          val.x += old.x;
+          val.y += old.y;
+          val.z += old.z;
+          val.w += old.w;
+        }
+        *q4 = val;
       }
     })
   }

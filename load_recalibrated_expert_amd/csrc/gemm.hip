@@ -34,7 +34,14 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-constexpr int BM = 256, BN = 256, BK = 32, NTHR = 256, STAGES = 4;
+constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4;
+// 8 wavefronts (two per SIMD) per 256x256 tile: a 2 x 4 grid of 128 x 64 wave tiles, so each
+// wavefront holds 2 x 4 MFMA accumulators (128 registers) and the SIMD can issue one
+// wavefront's MFMAs while the other waits on memory.
+constexpr int NWAVE = 8, NTHR = NWAVE * 64;
+constexpr int WN = 4, WM = NWAVE / WN;          // wave grid over the tile (N x M)
+constexpr int NB = BN / WN / 32, MB = BM / WM / 32;  // 32-wide MFMA blocks per wave (2 x 4)
+constexpr int DMA_PER_WAVE = BM * BK * 2 / 1024 / NWAVE;  // 1 KB direct loads per operand per stage
 constexpr int kTileU4 = BM * BK * 2 / 16;  // uint4 per operand tile per stage (16 KB)
 constexpr int64_t kKcMax = 16384;          // max packed rows per weight-gradient chunk
 constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past num_records: the load returns 0
@@ -71,59 +78,54 @@ __device__ __forceinline__ void dma16(rsrc_t r, const uint4* lds_wave_base, uint
 
 __device__ __forceinline__ int swz_k(int row) { return (row >> 2) & 3; }
 
-// Direct-to-LDS loader of a K-contiguous operand. Wave w fills tile rows [64 w, 64 w + 64)
-// with 4 instructions of 16 rows each; lane l loads row 16 j + l/4 (+64 w) at the chunk that
-// belongs in slot l % 4.
+// Direct-to-LDS loader of a K-contiguous operand. A 1 KB direct load fills 16 tile rows;
+// wave w issues loads j = 0..DMA_PER_WAVE-1 covering rows 16 (w*DMA_PER_WAVE + j) + l/4, and
+// lane l fetches the chunk that belongs in slot l % 4 of its row.
 struct DmaK {
   rsrc_t r;
-  uint32_t off[4];
+  uint32_t off[DMA_PER_WAVE];
   int col;    // first K element of this lane's chunk within the stage
-  int wbase;  // uint4 offset of this wave's 4 KB region in a stage
+  int wbase;  // uint4 offset of this wave's region in a stage
   __device__ __forceinline__ void init(const uint16_t* p, int64_t ld, int rows_valid) {
     r = make_rsrc(p);
     const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     col = ((l & 3) ^ ((l >> 4) & 3)) * 8;
-    wbase = w * 256;
+    wbase = w * DMA_PER_WAVE * 64;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = w * 64 + j * 16 + (l >> 2);
+    for (int j = 0; j < DMA_PER_WAVE; ++j) {
+      const int row = (w * DMA_PER_WAVE + j) * 16 + (l >> 2);
       off[j] = row < rows_valid ? (uint32_t)((row * ld + col) * 2) : kOOB;
     }
   }
-  __device__ __forceinline__ void issue(const uint4* stage, int k0, int kend) const {
+  __device__ __forceinline__ void issue_one(int j, const uint4* stage, int k0, int kend, uint32_t) const {
     const bool kok = k0 + col < kend;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dma16(r, stage + wbase + j * 64, (kok && off[j] != kOOB) ? off[j] + (uint32_t)k0 * 2u : kOOB);
+    dma16(r, stage + wbase + j * 64, (kok && off[j] != kOOB) ? off[j] + (uint32_t)k0 * 2u : kOOB);
   }
 };
 
-// Direct-to-LDS loader of a row-major-in-K operand. Wave w fills K rows [8 w, 8 w + 8) with
-// 4 instructions of 2 rows each; lane l loads row 2 j + l/32 (+8 w) at the chunk that belongs
-// in 16-byte slot l % 32.
+// Direct-to-LDS loader of a row-major-in-K operand. A 1 KB direct load fills 2 K rows;
+// wave w issues loads j covering rows 2 (w*DMA_PER_WAVE + j) + l/32, and lane l fetches the
+// chunk that belongs in 16-byte slot l % 32 of its row.
 struct DmaT {
   rsrc_t r;
-  uint32_t off[4];
-  int row[4];
+  uint32_t off[DMA_PER_WAVE];
+  int row[DMA_PER_WAVE];
   int wbase;
   __device__ __forceinline__ void init(const uint16_t* p, int64_t ld, int mn_valid) {
     r = make_rsrc(p);
     const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    wbase = w * 256;
+    wbase = w * DMA_PER_WAVE * 64;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = w * 8 + j * 2 + (l >> 5);
+    for (int j = 0; j < DMA_PER_WAVE; ++j) {
+      const int k = (w * DMA_PER_WAVE + j) * 2 + (l >> 5);
       const int pc = l & 31;
       const int c = (((pc >> 2) ^ (k & 3)) << 2) | (pc & 3);  // logical 16-byte chunk
       row[j] = k;
       off[j] = c * 8 < mn_valid ? (uint32_t)((k * ld + c * 8) * 2) : kOOB;
     }
   }
-  __device__ __forceinline__ void issue(const uint4* stage, int k0, int kend, uint32_t kstep) const {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dma16(r, stage + wbase + j * 64,
-            (off[j] != kOOB && k0 + row[j] < kend) ? off[j] + (uint32_t)k0 * kstep : kOOB);
+  __device__ __forceinline__ void issue_one(int j, const uint4* stage, int k0, int kend, uint32_t kstep) const {
+    dma16(r, stage + wbase + j * 64, (off[j] != kOOB && k0 + row[j] < kend) ? off[j] + (uint32_t)k0 * kstep : kOOB);
   }
 };
 
@@ -156,41 +158,23 @@ __device__ __forceinline__ bf16x8_t frag_tr(const uint4* stage, int col0, int k0
 // la holds the 256 output rows' operand (m), lb the 256 output columns' operand (n).
 // The MFMA takes the n fragment first, so each lane's accumulator holds 4 consecutive
 // output columns of one output row: acc[nb][mb][v] is output row
-// wm*128 + mb*32 + lane%32, column wn*128 + nb*32 + 8*(v/4) + 4*(lane/32) + v%4.
+// wm*(32 MB) + mb*32 + lane%32, column wn*(32 NB) + nb*32 + 8*(v/4) + 4*(lane/32) + v%4.
+// One MFMA fragment: rows row0..row0+31 of an operand stage, K16 step kk.
 template <bool TN>
-__device__ __forceinline__ void load_frags(const uint4* __restrict__ la, const uint4* __restrict__ lb, int kk,
-                                           int wm, int wn, int lane, bf16x8_t (&fa)[4], bf16x8_t (&fb)[4]) {
-  if (TN) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      fa[i] = frag_tr(la, wm * 128 + i * 32, kk * 16, lane);
-      fb[i] = frag_tr(lb, wn * 128 + i * 32, kk * 16, lane);
-    }
+__device__ __forceinline__ bf16x8_t load_frag(const uint4* __restrict__ stage, int row0, int kk, int lane) {
+  if constexpr (TN) {
+    return frag_tr(stage, row0, kk * 16, lane);
   } else {
-    const int lr = lane & 31, ch = kk * 2 + (lane >> 5);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ra = wm * 128 + i * 32 + lr;
-      const int rb = wn * 128 + i * 32 + lr;
-      fa[i] = __builtin_bit_cast(bf16x8_t, la[ra * 4 + (ch ^ swz_k(ra))]);
-      fb[i] = __builtin_bit_cast(bf16x8_t, lb[rb * 4 + (ch ^ swz_k(rb))]);
-    }
+    const int r = row0 + (lane & 31), ch = kk * 2 + (lane >> 5);
+    return __builtin_bit_cast(bf16x8_t, stage[r * 4 + (ch ^ swz_k(r))]);
   }
 }
 
-__device__ __forceinline__ void mma16(const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[4], f32x16_t (&acc)[4][4]) {
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[NB][MB]) {
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int i = 0; i < NB; ++i)
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-      acc[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb], fa[mb], acc[nb][mb], 0, 0, 0);
-}
-
-__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[4][4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < MB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 }
@@ -200,51 +184,63 @@ struct StageBufs {
   uint4 b[STAGES][kTileU4];
 };
 
+__device__ __forceinline__ void mfma(f32x16_t& acc, const bf16x8_t& n_frag, const bf16x8_t& m_frag) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(n_frag, m_frag, acc, 0, 0, 0);
+}
+
 // The K loop shared by every bf16 GEMM. Four LDS stages of 32 K values per operand are
 // filled by direct loads issued three stages ahead. At the top of stage kt each wave waits
 // for its own loads of stage kt+1, and one barrier then makes stage kt+1 visible and frees
-// stage kt-1's buffer, into which stage kt+3 is loaded. The first fragments of every stage
-// are read during the previous stage, so MFMAs start right after the barrier.
+// stage kt-1's buffer, into which stage kt+3 is loaded. A stage is two K16 steps of
+// NB x MB MFMAs. The wavefront issues in order, so every memory instruction sits right
+// behind an MFMA (hard scheduling fences keep that order): during the first step the
+// direct loads of stage kt+3 and the fragments of the second step; during the second step
+// the fragments of stage kt+1's first step, so MFMAs start right after the next barrier.
 template <bool TN, class LA, class LB>
 __device__ __forceinline__ void gemm_mainloop(StageBufs& sm, const LA& la, const LB& lb, int kend, uint32_t kstep_a,
-                                              uint32_t kstep_b, f32x16_t (&acc)[4][4], int wm, int wn, int lane) {
+                                              uint32_t kstep_b, f32x16_t (&acc)[NB][MB], int wm, int wn, int lane) {
+  constexpr int NM = NB * MB;
   const int nk = (kend + BK - 1) / BK;
   if (nk <= 0) return;
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) {
-    if constexpr (TN) {
-      la.issue(sm.a[s], s * BK, kend, kstep_a);
-      lb.issue(sm.b[s], s * BK, kend, kstep_b);
-    } else {
-      la.issue(sm.a[s], s * BK, kend);
-      lb.issue(sm.b[s], s * BK, kend);
+  for (int s = 0; s < STAGES - 1; ++s)
+#pragma unroll
+    for (int j = 0; j < DMA_PER_WAVE; ++j) {
+      la.issue_one(j, sm.a[s], s * BK, kend, kstep_a);
+      lb.issue_one(j, sm.b[s], s * BK, kend, kstep_b);
     }
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70 | (16 & 0xF) | ((16 >> 4) << 14));  // vmcnt(16): stage 0 landed
+  // vmcnt(2 stages): stage 0 landed
+  __builtin_amdgcn_s_waitcnt(0x0F70 | ((4 * DMA_PER_WAVE) & 0xF) | (((4 * DMA_PER_WAVE) >> 4) << 14));
   __syncthreads();
-  bf16x8_t fa[2][4], fb[2][4];
-  load_frags<TN>(sm.a[0], sm.b[0], 0, wm, wn, lane, fa[0], fb[0]);
+  bf16x8_t fa[2][MB], fb[2][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) fa[0][i] = load_frag<TN>(sm.a[0], wm * 32 * MB + i * 32, 0, lane);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) fb[0][i] = load_frag<TN>(sm.b[0], wn * 32 * NB + i * 32, 0, lane);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & (STAGES - 1), nxt = (kt + 1) & (STAGES - 1), ld = (kt + 3) & (STAGES - 1);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (8 & 0xF) | ((8 >> 4) << 14));  // vmcnt(8): stage kt+1 landed
+    const int cur = kt & (STAGES - 1), nxt = (kt + 1) & (STAGES - 1), ldst = (kt + 3) & (STAGES - 1);
+    const int k_ld = (kt + 3) * BK;
+    // vmcnt(1 stage): stage kt+1 landed
+    __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * DMA_PER_WAVE) & 0xF) | (((2 * DMA_PER_WAVE) >> 4) << 14));
     __syncthreads();
-    if constexpr (TN) {
-      la.issue(sm.a[ld], (kt + 3) * BK, kend, kstep_a);
-      lb.issue(sm.b[ld], (kt + 3) * BK, kend, kstep_b);
-    } else {
-      la.issue(sm.a[ld], (kt + 3) * BK, kend);
-      lb.issue(sm.b[ld], (kt + 3) * BK, kend);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      mfma(acc[i / MB][i % MB], fb[0][i / MB], fa[0][i % MB]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < DMA_PER_WAVE) la.issue_one(i, sm.a[ldst], k_ld, kend, kstep_a);
+      else if (i < 2 * DMA_PER_WAVE) lb.issue_one(i - DMA_PER_WAVE, sm.b[ldst], k_ld, kend, kstep_b);
+      if (i < MB) fa[1][i] = load_frag<TN>(sm.a[cur], wm * 32 * MB + i * 32, 1, lane);
+      else if (i < MB + NB) fb[1][i - MB] = load_frag<TN>(sm.b[cur], wn * 32 * NB + (i - MB) * 32, 1, lane);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // Each phase issues the fragment reads of the next K16 step, then runs the 16 MFMAs of
-    // the current one; the fences keep the compiler from sinking the reads behind the MFMAs.
-    load_frags<TN>(sm.a[cur], sm.b[cur], 1, wm, wn, lane, fa[1], fb[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    mma16(fa[0], fb[0], acc);
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags<TN>(sm.a[nxt], sm.b[nxt], 0, wm, wn, lane, fa[0], fb[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    mma16(fa[1], fb[1], acc);
-    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      mfma(acc[i / MB][i % MB], fb[1][i / MB], fa[1][i % MB]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < MB) fa[0][i] = load_frag<TN>(sm.a[nxt], wm * 32 * MB + i * 32, 0, lane);
+      else if (i < MB + NB) fb[0][i - MB] = load_frag<TN>(sm.b[nxt], wn * 32 * NB + (i - MB) * 32, 0, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the loop
 }
@@ -252,11 +248,11 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs& sm, const LA& la, const
 // Visits the accumulator as runs of 4 consecutive output columns:
 // BODY sees tile row `tm`, first tile column `tn` and the 4 values v0..v3.
 #define LRMOE_FOR_RUNS(BODY)                                                       \
-  _Pragma("unroll") for (int nb = 0; nb < 4; ++nb)                                 \
-  _Pragma("unroll") for (int mb = 0; mb < 4; ++mb)                                 \
+  _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                \
+  _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                \
   _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                  \
-    const int tm = wm * 128 + mb * 32 + (lane & 31);                               \
-    const int tn = wn * 128 + nb * 32 + 8 * q + 4 * (lane >> 5);                   \
+    const int tm = wm * 32 * MB + mb * 32 + (lane & 31);                           \
+    const int tn = wn * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5);               \
     const float v0 = acc[nb][mb][4 * q], v1 = acc[nb][mb][4 * q + 1];              \
     const float v2 = acc[nb][mb][4 * q + 2], v3 = acc[nb][mb][4 * q + 3];          \
     BODY                                                                           \
@@ -304,8 +300,8 @@ __global__ __launch_bounds__(NTHR) void dgrad_kernel(DgradArgs g) {
   const int n0 = nt * BN;
   const int n_valid = min(BN, g.N - n0);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
-  f32x16_t acc[4][4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN;
+  f32x16_t acc[NB][MB];
   zero_acc(acc);
   DmaK la, lb;
   la.init(g.A + row0 * g.lda, g.lda, rows_valid);
@@ -317,16 +313,16 @@ __global__ __launch_bounds__(NTHR) void dgrad_kernel(DgradArgs g) {
     const uint16_t* __restrict__ hc = g.HC;
     uint16_t* __restrict__ dh = g.out;
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int tm = wm * 128 + mb * 32 + (lane & 31);
+      for (int mb = 0; mb < MB; ++mb) {
+        const int tm = wm * 32 * MB + mb * 32 + (lane & 31);
         const bool row_ok = tm < rows_valid;
         const int64_t rowb = (row0 + tm) * ld;
         uint2 gv[4], uv[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int tn = wn * 128 + nb * 32 + 8 * q + 4 * (lane >> 5);
+          const int tn = wn * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5);
           if (row_ok && tn < n_valid) {
             gv[q] = *(const uint2*)(hc + rowb + n0 + tn);
             uv[q] = *(const uint2*)(hc + rowb + g.F + n0 + tn);
@@ -334,7 +330,7 @@ __global__ __launch_bounds__(NTHR) void dgrad_kernel(DgradArgs g) {
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int tn = wn * 128 + nb * 32 + 8 * q + 4 * (lane >> 5);
+          const int tn = wn * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5);
           if (row_ok && tn < n_valid) {
             const float gate[4] = {bf16_lo(gv[q].x), bf16_hi(gv[q].x), bf16_lo(gv[q].y), bf16_hi(gv[q].y)};
             const float up[4] = {bf16_lo(uv[q].x), bf16_hi(uv[q].x), bf16_lo(uv[q].y), bf16_hi(uv[q].y)};
@@ -460,8 +456,8 @@ __global__ __launch_bounds__(NTHR) void wgrad_kernel(WgradArgs g) {
   const int m0 = mt * BM, n0 = nt * BN;
   const int m_valid = min(BM, T.M - m0), n_valid = min(BN, T.N - n0);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
-  f32x16_t acc[4][4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN;
+  f32x16_t acc[NB][MB];
   zero_acc(acc);
   DmaT la, lb;
   la.init(T.A + (r0 + k_begin) * T.lda + m0, T.lda, m_valid);

@@ -9,8 +9,10 @@ intermediate 768, retention 0.6, bf16 with fp32 accumulation), seeded synthetic 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -60,6 +62,23 @@ def algorithmic_bytes(cfg, N, K_tot):
     width = D if cfg.swiglu else F
     scatter = K_tot * width * e + T * width * 4
     return {"score": score, "compact": compact, "scatter": scatter}
+
+
+def recorded_traffic(workload):
+    """HBM bytes per grouped-GEMM call recorded from rocprofv3 byte counters in profiles/,
+    valid only while the GEMM source is the one the counters were taken on."""
+    path = os.path.join(ROOT, "profiles", f"grouped_gemm_bwd_{workload}.md")
+    src = os.path.join(ROOT, "load_recalibrated_expert_amd", "csrc", "gemm.hip")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"gemm_source_sha256:\s*([0-9a-f]{64})", text)
+    m_tr = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not (m_sha and m_tr):
+        return None
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    return int(m_tr.group(1)) if sha == m_sha.group(1) else None
 
 
 def gemm_flops(cfg, rows):
@@ -217,7 +236,7 @@ def main():
                    "F": cfg.F, "swiglu": cfg.swiglu, "rho": rho, "pairs": P.N, "retained_pairs": P.K_tot,
                    "mode": "physical compaction"},
         "roofline": {"bound": "mfma", "achieved": gemm_tf, "peak": peak, "unit": "TFLOP/s",
-                     "frac": gemm_tf / peak, "traffic": None,
+                     "frac": gemm_tf / peak, "traffic": recorded_traffic(cfg.name),
                      "kernel": "lrmoe_grouped_gemm_bwd (FC2 dgrad+SwiGLU, FC1 dgrad, FC1+FC2 wgrad launches)",
                      "flops_per_launch": fl},
         "kernels": kernels,

@@ -245,18 +245,50 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs& sm, const LA& la, const
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the loop
 }
 
-// Visits the accumulator as runs of 4 consecutive output columns:
-// BODY sees tile row `tm`, first tile column `tn` and the 4 values v0..v3.
-#define LRMOE_FOR_RUNS(BODY)                                                       \
-  _Pragma("unroll") for (int nb = 0; nb < NB; ++nb)                                \
-  _Pragma("unroll") for (int mb = 0; mb < MB; ++mb)                                \
-  _Pragma("unroll") for (int q = 0; q < 4; ++q) {                                  \
-    const int tm = wm * 32 * MB + mb * 32 + (lane & 31);                           \
-    const int tn = wn * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5);               \
-    const float v0 = acc[nb][mb][4 * q], v1 = acc[nb][mb][4 * q + 1];              \
-    const float v2 = acc[nb][mb][4 * q + 2], v3 = acc[nb][mb][4 * q + 3];          \
-    BODY                                                                           \
+// ---------------------------------------------------------------- epilogue through LDS
+
+// Writes the accumulators out through LDS so that every output row is handled by
+// consecutive threads with 16-byte accesses. The 256x256 fp32 tile is staged in two halves
+// of 128 rows (the wavefronts with wm = 0, then wm = 1), each filling the 128 KB of stage
+// buffers. A staged row holds 64 chunks of 4 floats; chunk c of row r sits in slot
+// c ^ (r & 15), so the accumulator writes (32 rows per instruction) and the row reads both
+// spread over the banks. BODY(row, col, v[8]) receives 8 consecutive columns of one tile row.
+template <class Body>
+__device__ __forceinline__ void epilogue_staged(StageBufs& sm, const f32x16_t (&acc)[NB][MB], int wm, int wn,
+                                                int lane, Body body) {
+  float4* st = reinterpret_cast<float4*>(&sm);
+#pragma unroll
+  for (int half = 0; half < WM; ++half) {
+    __syncthreads();
+    if (wm == half) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = mb * 32 + (lane & 31);
+            const int c = (wn * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5)) >> 2;
+            st[r * 64 + (c ^ (r & 15))] =
+                make_float4(acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
+          }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < (BM / WM) * (BN / 8) / NTHR; ++i) {
+      const int id = threadIdx.x + NTHR * i;
+      const int r = id / (BN / 8), c8 = id % (BN / 8);
+      const float4 lo = st[r * 64 + ((2 * c8) ^ (r & 15))];
+      const float4 hi = st[r * 64 + ((2 * c8 + 1) ^ (r & 15))];
+      const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      body(half * (BM / WM) + r, c8 * 8, v);
+    }
   }
+}
+
+__device__ __forceinline__ uint4 pack_bf16x8(const float (&v)[8]) {
+  return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+}
 
 // ---------------------------------------------------------------- data-gradient kernel
 
@@ -277,8 +309,6 @@ struct DgradArgs {
   int64_t ldo;
   int F;
 };
-
-__device__ __forceinline__ float silu_fwd(float g, float s) { return g * s; }
 
 template <int EPI>
 __global__ __launch_bounds__(NTHR) void dgrad_kernel(DgradArgs g) {
@@ -312,48 +342,31 @@ __global__ __launch_bounds__(NTHR) void dgrad_kernel(DgradArgs g) {
     const int64_t ld = 2 * (int64_t)g.F;
     const uint16_t* __restrict__ hc = g.HC;
     uint16_t* __restrict__ dh = g.out;
+    const int F = g.F;
+    epilogue_staged(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&dphi)[8]) {
+      if (tr < rows_valid && tc < n_valid) {
+        const int64_t rowb = (row0 + tr) * ld + n0 + tc;
+        const uint4 gw = *(const uint4*)(hc + rowb);
+        const uint4 uw = *(const uint4*)(hc + rowb + F);
+        const uint32_t gg[4] = {gw.x, gw.y, gw.z, gw.w}, uu[4] = {uw.x, uw.y, uw.z, uw.w};
+        float dg[8], du[8];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int tm = wm * 32 * MB + mb * 32 + (lane & 31);
-        const bool row_ok = tm < rows_valid;
-        const int64_t rowb = (row0 + tm) * ld;
-        uint2 gv[4], uv[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int tn = wn * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5);
-          if (row_ok && tn < n_valid) {
-            gv[q] = *(const uint2*)(hc + rowb + n0 + tn);
-            uv[q] = *(const uint2*)(hc + rowb + g.F + n0 + tn);
-          }
+        for (int c = 0; c < 8; ++c) {
+          const float gate = (c & 1) ? bf16_hi(gg[c >> 1]) : bf16_lo(gg[c >> 1]);
+          const float up = (c & 1) ? bf16_hi(uu[c >> 1]) : bf16_lo(uu[c >> 1]);
+          const float s = 1.0f / (1.0f + expf(-gate));
+          dg[c] = dphi[c] * up * (s * (1.0f + gate * (1.0f - s)));
+          du[c] = dphi[c] * (gate * s);
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int tn = wn * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5);
-          if (row_ok && tn < n_valid) {
-            const float gate[4] = {bf16_lo(gv[q].x), bf16_hi(gv[q].x), bf16_lo(gv[q].y), bf16_hi(gv[q].y)};
-            const float up[4] = {bf16_lo(uv[q].x), bf16_hi(uv[q].x), bf16_lo(uv[q].y), bf16_hi(uv[q].y)};
-            float dg[4], du[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const float dphi = acc[nb][mb][4 * q + c];
-              const float s = 1.0f / (1.0f + expf(-gate[c]));
-              dg[c] = dphi * up[c] * (s * (1.0f + gate[c] * (1.0f - s)));
-              du[c] = dphi * silu_fwd(gate[c], s);
-            }
-            *(uint2*)(dh + rowb + n0 + tn) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
-            *(uint2*)(dh + rowb + g.F + n0 + tn) = make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
-          }
-        }
+        *(uint4*)(dh + rowb) = pack_bf16x8(dg);
+        *(uint4*)(dh + rowb + F) = pack_bf16x8(du);
       }
-    }
+    });
   } else {
     uint16_t* __restrict__ out = g.out;
-    LRMOE_FOR_RUNS({
-      if (tm < rows_valid && tn < n_valid)
-        *(uint2*)(out + (row0 + tm) * g.ldo + n0 + tn) = make_uint2(pack_bf16x2(v0, v1), pack_bf16x2(v2, v3));
-    })
+    epilogue_staged(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
+      if (tr < rows_valid && tc < n_valid) *(uint4*)(out + (row0 + tr) * g.ldo + n0 + tc) = pack_bf16x8(v);
+    });
   }
 }
 
@@ -466,24 +479,27 @@ __global__ __launch_bounds__(NTHR) void wgrad_kernel(WgradArgs g) {
 
   if (s > 1) {
     float* __restrict__ p = g.partials + (g.plan_pbase[e] + (int64_t)chunk * tiles + rem) * (int64_t)(BM * BN);
-    LRMOE_FOR_RUNS({ *(float4*)(p + tm * BN + tn) = make_float4(v0, v1, v2, v3); })
+    epilogue_staged(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
+      float4* q4 = (float4*)(p + tr * BN + tc);
+      q4[0] = make_float4(v[0], v[1], v[2], v[3]);
+      q4[1] = make_float4(v[4], v[5], v[6], v[7]);
+    });
   } else {
     float* __restrict__ o = T.out + (int64_t)e * T.M * T.N;
     const bool accum = g.accumulate != 0;
-    LRMOE_FOR_RUNS({
-      if (tm < m_valid && tn < n_valid) {
-        float4* q4 = (float4*)(o + (int64_t)(m0 + tm) * T.N + n0 + tn);
-        float4 val = make_float4(v0, v1, v2, v3);
+    epilogue_staged(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
+      if (tr < m_valid && tc < n_valid) {
+        float4* q4 = (float4*)(o + (int64_t)(m0 + tr) * T.N + n0 + tc);
+        float4 a = make_float4(v[0], v[1], v[2], v[3]), b = make_float4(v[4], v[5], v[6], v[7]);
         if (accum) {
-          const float4 old = *q4;
-          val.x += old.x;
-          val.y += old.y;
-          val.z += old.z;
-          val.w += old.w;
+          const float4 oa = q4[0], ob = q4[1];
+          a.x += oa.x; a.y += oa.y; a.z += oa.z; a.w += oa.w;
+          b.x += ob.x; b.y += ob.y; b.z += ob.z; b.w += ob.w;
         }
-        *q4 = val;
+        q4[0] = a;
+        q4[1] = b;
       }
-    })
+    });
   }
 }
 

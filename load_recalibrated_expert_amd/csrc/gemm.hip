@@ -24,6 +24,10 @@
 // tiles that share operands in its L2.
 //
 // f32 path (small problems): plain fp32 FMA kernels, no bf16 anywhere.
+#include <algorithm>
+#include <functional>
+#include <vector>
+
 #include "common.h"
 
 namespace lrmoe {
@@ -43,7 +47,7 @@ constexpr int WN = 4, WM = NWAVE / WN;          // wave grid over the tile (N x 
 constexpr int NB = BN / WN / 32, MB = BM / WM / 32;  // 32-wide MFMA blocks per wave (2 x 4)
 constexpr int DMA_PER_WAVE = BM * BK * 2 / 1024 / NWAVE;  // 1 KB direct loads per operand per stage
 constexpr int kTileU4 = BM * BK * 2 / 16;  // uint4 per operand tile per stage (16 KB)
-constexpr int64_t kKcMax = 16384;          // max packed rows per weight-gradient chunk
+constexpr int64_t kKcMax = 12288;          // max packed rows per weight-gradient chunk
 constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past num_records: the load returns 0
 
 __device__ __forceinline__ int xcd_remap(int b, int n) {
@@ -68,19 +72,23 @@ __device__ __forceinline__ void dma16(rsrc_t r, const uint4* lds_wave_base, uint
 
 // ---------------------------------------------------------------- LDS layouts
 //
-// K-contiguous operand (data-gradient GEMMs): a stage holds 256 rows x 32 K values, 64 bytes
-// per row as four 16-byte chunks; chunk c of row r sits in slot c ^ ((r >> 2) & 3), so the
-// 16-byte fragment reads of 16 consecutive rows cover all 64 banks.
+// K-contiguous operand (data-gradient GEMMs): a stage holds 256 rows x 32 K values (64 bytes
+// per row, four 16-byte chunks). Rows r and r + 128 share one 128-byte LDS line: line
+// L = r % 128 holds eight 16-byte slots, and chunk c of row r sits in slot
+// (4 (r / 128) + c) ^ (L % 8). MFMA fragment reads (one 16-byte chunk of each of 32
+// consecutive rows) then run at the full LDS rate; with a 64-byte line pitch they ran at half.
 //
 // Row-major-in-K operand (weight-gradient GEMMs): a stage holds 32 K rows x 256 columns,
 // 512 bytes per row as eight 64-byte segments; segment s of row k sits in slot s ^ (k & 3),
 // so the 4-row transpose reads of one half-wavefront cover all 64 banks.
 
-__device__ __forceinline__ int swz_k(int row) { return (row >> 2) & 3; }
+// uint4 index of chunk c of row r in a K-contiguous stage
+__device__ __forceinline__ int nt_slot(int r, int c) { return (r & 127) * 8 + ((((r >> 7) << 2) | c) ^ (r & 7)); }
 
-// Direct-to-LDS loader of a K-contiguous operand. A 1 KB direct load fills 16 tile rows;
-// wave w issues loads j = 0..DMA_PER_WAVE-1 covering rows 16 (w*DMA_PER_WAVE + j) + l/4, and
-// lane l fetches the chunk that belongs in slot l % 4 of its row.
+// Direct-to-LDS loader of a K-contiguous operand. A 1 KB direct load fills 8 LDS lines
+// (16 tile rows); wave w issues loads j = 0..DMA_PER_WAVE-1 covering lines
+// 8 (w*DMA_PER_WAVE + j) + l/8, and lane l fetches the chunk that belongs in slot l % 8 of
+// its line: slot s holds chunk (s ^ line%8) % 4 of row 128 ((s ^ line%8) / 4) + line.
 struct DmaK {
   rsrc_t r;
   uint32_t off[DMA_PER_WAVE];
@@ -89,11 +97,12 @@ struct DmaK {
   __device__ __forceinline__ void init(const uint16_t* p, int64_t ld, int rows_valid) {
     r = make_rsrc(p);
     const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    col = ((l & 3) ^ ((l >> 4) & 3)) * 8;
+    const int logical = (l & 7) ^ ((l >> 3) & 7);  // line % 8 == (l / 8) % 8
+    col = (logical & 3) * 8;
     wbase = w * DMA_PER_WAVE * 64;
 #pragma unroll
     for (int j = 0; j < DMA_PER_WAVE; ++j) {
-      const int row = (w * DMA_PER_WAVE + j) * 16 + (l >> 2);
+      const int row = (logical >> 2) * 128 + (w * DMA_PER_WAVE + j) * 8 + (l >> 3);
       off[j] = row < rows_valid ? (uint32_t)((row * ld + col) * 2) : kOOB;
     }
   }
@@ -165,8 +174,7 @@ __device__ __forceinline__ bf16x8_t load_frag(const uint4* __restrict__ stage, i
   if constexpr (TN) {
     return frag_tr(stage, row0, kk * 16, lane);
   } else {
-    const int r = row0 + (lane & 31), ch = kk * 2 + (lane >> 5);
-    return __builtin_bit_cast(bf16x8_t, stage[r * 4 + (ch ^ swz_k(r))]);
+    return __builtin_bit_cast(bf16x8_t, stage[nt_slot(row0 + (lane & 31), kk * 2 + (lane >> 5))]);
   }
 }
 
@@ -209,8 +217,10 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs& sm, const LA& la, const
       la.issue_one(j, sm.a[s], s * BK, kend, kstep_a);
       lb.issue_one(j, sm.b[s], s * BK, kend, kstep_b);
     }
-  // vmcnt(2 stages): stage 0 landed
-  __builtin_amdgcn_s_waitcnt(0x0F70 | ((4 * DMA_PER_WAVE) & 0xF) | (((4 * DMA_PER_WAVE) >> 4) << 14));
+  // stage 0 landed: the loads of stages 1..STAGES-2 may still be in flight
+  constexpr int kPro = (STAGES - 2) * 2 * DMA_PER_WAVE, kLoop = (STAGES - 3) * 2 * DMA_PER_WAVE;
+  static_assert(kPro < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (kPro & 0xF) | ((kPro >> 4) << 14));
   __syncthreads();
   bf16x8_t fa[2][MB], fb[2][NB];
 #pragma unroll
@@ -218,10 +228,10 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs& sm, const LA& la, const
 #pragma unroll
   for (int i = 0; i < NB; ++i) fb[0][i] = load_frag<TN>(sm.b[0], wn * 32 * NB + i * 32, 0, lane);
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & (STAGES - 1), nxt = (kt + 1) & (STAGES - 1), ldst = (kt + 3) & (STAGES - 1);
-    const int k_ld = (kt + 3) * BK;
-    // vmcnt(1 stage): stage kt+1 landed
-    __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * DMA_PER_WAVE) & 0xF) | (((2 * DMA_PER_WAVE) >> 4) << 14));
+    const int cur = kt % STAGES, nxt = (kt + 1) % STAGES, ldst = (kt + STAGES - 1) % STAGES;
+    const int k_ld = (kt + STAGES - 1) * BK;
+    // stage kt+1 landed: the loads of stages kt+2..kt+STAGES-2 may still be in flight
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (kLoop & 0xF) | ((kLoop >> 4) << 14));
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
@@ -394,9 +404,14 @@ struct WgradArgs {
   int64_t* plan_pbase;  // [E] first partial tile of expert e (split experts only)
   float* partials;      // [npartials x BM x BN]
   int accumulate;
+  // Items (planned order) of XCD x: [xlo[x], xlo[x+1]). The ranges are contiguous, so the
+  // tiles sharing operand panels stay in one L2, and cut so every XCD gets the same number
+  // of K steps: items are sorted by decreasing length, so equal item counts would hand the
+  // first XCD several times the work of the last.
+  int xlo[9];
 };
 
-__device__ __forceinline__ void expert_split(int64_t m, int& s, int& kc) {
+__host__ __device__ inline void expert_split(int64_t m, int& s, int& kc) {
   if (m <= 0) {
     s = 1;
     kc = 0;
@@ -447,7 +462,10 @@ __global__ __launch_bounds__(NTHR) void wgrad_plan_kernel(WgradArgs g) {
 
 __global__ __launch_bounds__(NTHR) void wgrad_kernel(WgradArgs g) {
   __shared__ StageBufs lds;
-  const int b = xcd_remap(blockIdx.x, gridDim.x);
+  // hardware sends block i to XCD i % 8; the grid holds 8 x (largest range) blocks
+  const int x = blockIdx.x & 7;
+  const int b = g.xlo[x] + (int)(blockIdx.x >> 3);
+  if (b >= g.xlo[x + 1]) return;  // uniform per block
   int lo = 0, hi = g.E;  // planned expert r with prefix[r] <= b < prefix[r+1]
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -625,6 +643,66 @@ WgradLayout wgrad_layout(const lrmoe_problem* p, const int64_t* row_off_h) {
   return L;
 }
 
+// Splits the weight-gradient items, in the order the plan kernel gives them (experts by
+// decreasing chunk length, ties by id; chunk-major within an expert), into 8 contiguous
+// ranges, one per XCD. An item costs its K steps plus 8 for its prologue and epilogue. The
+// split minimises the largest range's finishing time when its 32 CUs take items in order
+// as they free up: a bisection on that time, each probe filling the ranges greedily.
+// Returns the largest range's item count. Any monotone split covers every item exactly
+// once, so the split only affects balance, never results.
+int64_t wgrad_xcd_ranges(const lrmoe_problem* p, const int64_t* row_off_h, int (&xlo)[9]) {
+  constexpr int kXcd = 8, kCuPerXcd = 32;
+  const int E = p->E;
+  const int tiles = wgrad_tiles(p->F, p->D) + (p->swiglu ? wgrad_tiles(p->D, 2 * p->F) : 0);
+  std::vector<int> order(E), S(E), KC(E);
+  for (int e = 0; e < E; ++e) {
+    order[e] = e;
+    expert_split(row_off_h[e + 1] - row_off_h[e], S[e], KC[e]);
+  }
+  std::sort(order.begin(), order.end(), [&](int a, int b) { return KC[a] != KC[b] ? KC[a] > KC[b] : a < b; });
+  std::vector<int64_t> cost;  // per item, planned order
+  for (int e : order) {
+    const int64_t m = row_off_h[e + 1] - row_off_h[e];
+    for (int c = 0; c < S[e]; ++c) {
+      const int64_t klen = std::max<int64_t>(0, std::min<int64_t>(KC[e], m - (int64_t)c * KC[e]));
+      cost.insert(cost.end(), tiles, ceil_div(klen, BK) + 8);
+    }
+  }
+  const int64_t n = (int64_t)cost.size();
+  int64_t total = 0, longest = 0;
+  for (int64_t c : cost) {
+    total += c;
+    longest = std::max(longest, c);
+  }
+  // fills the ranges so that no CU finishes after T; false if items are left over
+  auto fill = [&](int64_t T, int (&lo)[9]) {
+    int64_t i = 0;
+    lo[0] = 0;
+    for (int x = 0; x < kXcd; ++x) {
+      std::vector<int64_t> cu(kCuPerXcd, 0);  // min-heap of CU finishing times
+      std::make_heap(cu.begin(), cu.end(), std::greater<int64_t>());
+      while (i < n && cu.front() + cost[i] <= T) {
+        std::pop_heap(cu.begin(), cu.end(), std::greater<int64_t>());
+        cu.back() += cost[i++];
+        std::push_heap(cu.begin(), cu.end(), std::greater<int64_t>());
+      }
+      lo[x + 1] = (int)i;
+    }
+    return i == n;
+  };
+  int64_t lo_t = std::max(longest, ceil_div(total, (int64_t)kXcd * kCuPerXcd)), hi_t = total;
+  while (lo_t < hi_t) {
+    const int64_t mid = lo_t + (hi_t - lo_t) / 2;
+    int tmp[9];
+    if (fill(mid, tmp)) hi_t = mid;
+    else lo_t = mid + 1;
+  }
+  fill(lo_t, xlo);
+  int64_t mx = 0;
+  for (int x = 0; x < kXcd; ++x) mx = std::max<int64_t>(mx, xlo[x + 1] - xlo[x]);
+  return mx;
+}
+
 }  // namespace
 
 size_t gemm_ws_bytes(const lrmoe_problem* p, const int64_t* row_off_h) {
@@ -727,8 +805,9 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
   w.partials = (float*)(b + L.plan_bytes);
   w.accumulate = accumulate;
   if (E > 0) {
+    const int64_t per_xcd = wgrad_xcd_ranges(p, row_off_h, w.xlo);
     wgrad_plan_kernel<<<1, NTHR, 0, s>>>(w);
-    wgrad_kernel<<<(unsigned)L.nitems, NTHR, 0, s>>>(w);
+    if (per_xcd > 0) wgrad_kernel<<<(unsigned)(8 * per_xcd), NTHR, 0, s>>>(w);
     if (L.nreduce > 0) wgrad_reduce_kernel<<<(unsigned)L.nreduce, NTHR, 0, s>>>(w);
   }
   return launch_status();

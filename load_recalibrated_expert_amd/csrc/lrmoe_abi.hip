@@ -103,7 +103,7 @@ lrmoe_status lrmoe_select(const lrmoe_problem* p, const float* R, const int64_t*
   LRMOE_TRY(check_problem(p, &K_tot, nullptr));
   if (!seg_off_d || !quota_d || !cseg_off_d) return LRMOE_ERR_INVALID_ARG;
   if ((p->N > 0 && !R) || (K_tot > 0 && !sel)) return LRMOE_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < select_ws_bytes(p)) return LRMOE_ERR_WORKSPACE;
+  if (select_ws_bytes(p) > 0 && (!ws || ws_bytes < select_ws_bytes(p))) return LRMOE_ERR_WORKSPACE;
   return launch_select(p, R, seg_off_d, quota_d, cseg_off_d, sel, keep, ws, (hipStream_t)stream);
 }
 

@@ -6,13 +6,14 @@
 //
 // Scores are non-negative f32, so their bit patterns order like unsigned integers. The
 // q_e-th largest key of every segment is found by a three-pass most-significant-digit
-// radix select (11, 11 and 10 bits). Every pass is one launch over (chunk, expert)
-// blocks: blocks build LDS histograms of the digit among keys that still match the
-// prefix, add them to a global per-expert histogram, and the last block to finish (an
-// atomic ticket) walks each histogram from the top to fix the next digit. Two more
-// launches count, per chunk, keys above and equal to the threshold, then write the
-// retained indices at positions given by block-level ballot scans. Nothing spins: each
-// block either does its share and leaves or, being last, finishes the pass.
+// radix select (11, 11 and 10 bits). A pass is two launches: chunk blocks (4096 keys of one
+// segment each) build LDS histograms of the digit among keys that still match the fixed
+// prefix and add them to the segment's global histogram; then one block per segment scans
+// its histogram from the highest bin and fixes the digit. The write side is three more
+// launches: chunk blocks count keys above and equal to the threshold, one block per segment
+// turns the counts into chunk offsets, and chunk blocks write the retained indices at
+// positions given by block-level ballot scans. Kernel boundaries order every step, so no
+// block waits on another and no block needs a device-wide fence.
 #include "common.h"
 
 namespace lrmoe {
@@ -20,7 +21,7 @@ namespace {
 
 constexpr int kSelThreads = 256;
 constexpr int kSelPer = 16;
-constexpr int kChunk = kSelThreads * kSelPer;  // keys per block
+constexpr int kChunk = kSelThreads * kSelPer;  // keys per chunk block
 constexpr int kBins = 2048;
 
 enum : uint32_t { kKeepNone = 0, kKeepAll = 1, kKeepThreshold = 2 };
@@ -29,9 +30,7 @@ struct SegState {
   uint32_t prefix;  // digits fixed so far (after the last pass: the threshold key)
   uint32_t mask;    // bits of prefix that are fixed
   uint32_t need;    // rank still to find among keys matching prefix (ties kept at the end)
-  uint32_t cnt_gt;  // keys strictly above the prefix range
   uint32_t mode;
-  uint32_t pad[3];
 };
 
 struct SelWs {
@@ -39,7 +38,6 @@ struct SelWs {
   SegState* state;   // [E]
   uint32_t* counts;  // [E][maxch][2]  keys above / equal to the threshold, per chunk
   uint32_t* offs;    // [E][maxch][2]  exclusive prefix of counts within the segment
-  uint32_t* ticket;  // [1]
 };
 
 int max_chunks(const lrmoe_problem* p) {
@@ -59,8 +57,6 @@ SelWs carve(void* ws, int E, int maxch) {
   w.counts = (uint32_t*)(b + o);
   o = align_up(o + sizeof(uint32_t) * 2 * (size_t)E * maxch, 256);
   w.offs = (uint32_t*)(b + o);
-  o = align_up(o + sizeof(uint32_t) * 2 * (size_t)E * maxch, 256);
-  w.ticket = (uint32_t*)(b + o);
   return w;
 }
 
@@ -70,26 +66,21 @@ size_t carve_bytes(int E, int maxch) {
   o = align_up(o + sizeof(SegState) * (size_t)E, 256);
   o = align_up(o + sizeof(uint32_t) * 2 * (size_t)E * maxch, 256);
   o = align_up(o + sizeof(uint32_t) * 2 * (size_t)E * maxch, 256);
-  return o + 256;
+  return o;
 }
 
-__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Returns true in every thread of the block that finished last among all blocks of the grid.
-__device__ __forceinline__ bool last_block_done(uint32_t* ticket) {
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t total = gridDim.x * gridDim.y;
-    const uint32_t t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (t == total - 1);
+// Keys of the chunk block at [lo, hi): thread t holds keys lo + r*256 + t, r < kSelPer,
+// all loaded before any is used. Bit r of the result marks keys inside the chunk.
+__device__ __forceinline__ uint32_t load_chunk(const float* __restrict__ R, int64_t lo, int64_t hi,
+                                               uint32_t (&k)[kSelPer]) {
+  uint32_t ok = 0;
+#pragma unroll
+  for (int r = 0; r < kSelPer; ++r) {
+    const int64_t i = lo + (int64_t)r * kSelThreads + threadIdx.x;
+    k[r] = i < hi ? __float_as_uint(R[i]) : 0u;
+    ok |= (i < hi ? 1u : 0u) << r;
   }
-  __syncthreads();
-  if (s_last) __threadfence();
-  return s_last != 0;
+  return ok;
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_init_kernel(int E, const int64_t* __restrict__ seg_off,
@@ -104,90 +95,112 @@ __global__ __launch_bounds__(kSelThreads) void select_init_kernel(int E, const i
     s.prefix = 0;
     s.mask = 0;
     s.need = (uint32_t)q;
-    s.cnt_gt = 0;
     s.mode = q <= 0 ? kKeepNone : (q >= n ? kKeepAll : kKeepThreshold);
-    s.pad[0] = s.pad[1] = s.pad[2] = 0;
     w.state[gid] = s;
   }
-  if (gid == 0) *w.ticket = 0;
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_hist_kernel(int shift, int nbits, const float* __restrict__ R,
-                                                                  const int64_t* __restrict__ seg_off,
-                                                                  SelWs w, int E) {
+                                                                  const int64_t* __restrict__ seg_off, SelWs w) {
   __shared__ uint32_t h[kBins];
   const int e = blockIdx.y, tid = threadIdx.x;
   const SegState st = w.state[e];
   const int64_t lo = seg_off[e] + (int64_t)blockIdx.x * kChunk;
   const int64_t hi = min(seg_off[e + 1], lo + kChunk);
+  if (st.mode != kKeepThreshold || lo >= hi) return;  // uniform across the block
   const uint32_t nb = 1u << nbits;
-  if (st.mode == kKeepThreshold && lo < hi) {  // uniform across the block
-    for (uint32_t b = tid; b < nb; b += kSelThreads) h[b] = 0;
-    __syncthreads();
-    for (int64_t i = lo + tid; i < hi; i += kSelThreads) {
-      const uint32_t key = __float_as_uint(R[i]);
-      if ((key & st.mask) == st.prefix) atomicAdd(&h[(key >> shift) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    for (uint32_t b = tid; b < nb; b += kSelThreads) {
-      const uint32_t c = h[b];
-      if (c) atomicAdd(&w.hist[(size_t)e * kBins + b], c);
-    }
-  }
-  if (!last_block_done(w.ticket)) return;
-
-  // Last block: fix this pass's digit of every thresholded segment, one wavefront each.
-  const int wave = tid / kWave, lane = tid % kWave;
-  const uint32_t per = nb / kWave;  // bins per lane; lane 0 owns the highest bins
-  for (int e2 = wave; e2 < E; e2 += kSelThreads / kWave) {
-    SegState s2 = w.state[e2];
-    if (s2.mode != kKeepThreshold) continue;
-    uint32_t* hg = w.hist + (size_t)e2 * kBins;
-    const int top = (int)(nb - lane * per);
-    uint32_t c = 0;
-    for (int b = top - (int)per; b < top; ++b) c += load_agent(&hg[b]);
-    uint32_t inc = c;
+  uint32_t k[kSelPer];
+  const uint32_t ok = load_chunk(R, lo, hi, k);
+  for (uint32_t b = tid; b < nb; b += kSelThreads) h[b] = 0;
+  __syncthreads();
 #pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-      const uint32_t v = __shfl_up(inc, o, kWave);
-      if (lane >= o) inc += v;
-    }
-    const uint32_t exc = inc - c;
-    const bool mine = exc < s2.need && inc >= s2.need;
-    if (mine) {
-      uint32_t above = exc;
-      int b = top - 1;
-      for (; b > top - (int)per; --b) {
-        const uint32_t cb = load_agent(&hg[b]);
-        if (above + cb >= s2.need) break;
-        above += cb;
-      }
-      s2.need -= above;
-      s2.cnt_gt += above;
-      s2.prefix |= (uint32_t)b << shift;
-      s2.mask |= (nb - 1) << shift;
-      w.state[e2] = s2;
-    }
-    for (uint32_t b = lane; b < nb; b += kWave) hg[b] = 0;  // ready for the next pass
+  for (int r = 0; r < kSelPer; ++r)
+    if ((ok >> r & 1) && (k[r] & st.mask) == st.prefix) atomicAdd(&h[(k[r] >> shift) & (nb - 1)], 1u);
+  __syncthreads();
+  for (uint32_t b = tid; b < nb; b += kSelThreads) {
+    const uint32_t c = h[b];
+    if (c) atomicAdd(&w.hist[(size_t)e * kBins + b], c);
+  }
+}
+
+// Block-wide inclusive prefix in thread order (256 threads); total in tot. Every thread of
+// the block must call it.
+__device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t& tot, uint32_t* sh) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  uint32_t inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const uint32_t u = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += u;
+  }
+  if (lane == kWave - 1) sh[wave] = inc;
+  __syncthreads();
+  uint32_t pre = 0;
+  tot = 0;
+#pragma unroll
+  for (int v2 = 0; v2 < kSelThreads / kWave; ++v2) {
+    if (v2 < wave) pre += sh[v2];
+    tot += sh[v2];
   }
   __syncthreads();
-  if (tid == 0) *w.ticket = 0;
+  return pre + inc;
+}
+
+// One block per segment: fix this pass's digit from the segment's histogram (thread t owns
+// the `per` bins just below nb - per*t, thread 0 the highest) and clear it for the next pass.
+__global__ __launch_bounds__(kSelThreads) void select_digit_kernel(int shift, int nbits, SelWs w) {
+  __shared__ uint32_t sh[kSelThreads / kWave];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  SegState st = w.state[e];
+  if (st.mode != kKeepThreshold) return;  // uniform across the block
+  const uint32_t nb = 1u << nbits, per = nb / kSelThreads;  // 8 or 4
+  uint32_t* hg = w.hist + (size_t)e * kBins;
+  const int top = (int)(nb - tid * per);
+  uint32_t c[8];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    c[j] = j < (int)per ? hg[top - 1 - j] : 0u;  // c[0] is the thread's highest bin
+    sum += c[j];
+  }
+  uint32_t tot;
+  const uint32_t inc = block_incl_scan(sum, tot, sh);
+  const uint32_t exc = inc - sum;
+  if (exc < st.need && inc >= st.need) {  // exactly one thread
+    uint32_t above = exc;
+    int j = 0;
+    for (; j < (int)per - 1; ++j) {
+      if (above + c[j] >= st.need) break;
+      above += c[j];
+    }
+    st.need -= above;
+    st.prefix |= (uint32_t)(top - 1 - j) << shift;
+    st.mask |= (nb - 1) << shift;
+    w.state[e] = st;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < (int)per) hg[top - 1 - j] = 0;
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_count_kernel(const float* __restrict__ R,
                                                                    const int64_t* __restrict__ seg_off,
-                                                                   SelWs w, int E, int maxch) {
+                                                                   SelWs w, int maxch) {
   __shared__ uint32_t red[2][kSelThreads / kWave];
   const int e = blockIdx.y, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const SegState st = w.state[e];
   const int64_t lo = seg_off[e] + (int64_t)blockIdx.x * kChunk;
   const int64_t hi = min(seg_off[e + 1], lo + kChunk);
+  if (lo >= hi) return;  // uniform across the block
   uint32_t gt = 0, eq = 0;
   if (st.mode != kKeepNone) {
-    for (int64_t i = lo + tid; i < hi; i += kSelThreads) {
-      const uint32_t key = __float_as_uint(R[i]);
-      gt += (st.mode == kKeepAll || key > st.prefix) ? 1u : 0u;
-      eq += (st.mode == kKeepThreshold && key == st.prefix) ? 1u : 0u;
+    uint32_t k[kSelPer];
+    const uint32_t ok = load_chunk(R, lo, hi, k);
+#pragma unroll
+    for (int r = 0; r < kSelPer; ++r) {
+      const bool v = ok >> r & 1;
+      gt += (v && (st.mode == kKeepAll || k[r] > st.prefix)) ? 1u : 0u;
+      eq += (v && st.mode == kKeepThreshold && k[r] == st.prefix) ? 1u : 0u;
     }
   }
 #pragma unroll
@@ -210,21 +223,30 @@ __global__ __launch_bounds__(kSelThreads) void select_count_kernel(const float* 
     w.counts[slot] = a;
     w.counts[slot + 1] = b;
   }
-  if (!last_block_done(w.ticket)) return;
-  for (int e2 = tid; e2 < E; e2 += kSelThreads) {
-    const int64_t n = seg_off[e2 + 1] - seg_off[e2];
-    const int nch = (int)((n + kChunk - 1) / kChunk);
-    uint32_t rg = 0, re = 0;
-    for (int c = 0; c < nch && c < maxch; ++c) {
-      const size_t slot = ((size_t)e2 * maxch + c) * 2;
-      w.offs[slot] = rg;
-      w.offs[slot + 1] = re;
-      rg += load_agent(&w.counts[slot]);
-      re += load_agent(&w.counts[slot + 1]);
+}
+
+// One block per segment: exclusive prefix of its per-chunk counts, 256 chunks at a time.
+__global__ __launch_bounds__(kSelThreads) void select_offs_kernel(const int64_t* __restrict__ seg_off, SelWs w,
+                                                                  int maxch) {
+  __shared__ uint32_t sh[2][kSelThreads / kWave];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const int64_t n = seg_off[e + 1] - seg_off[e];
+  const int nch = (int)min<int64_t>((n + kChunk - 1) / kChunk, maxch);
+  uint32_t rg = 0, re = 0;
+  for (int c0 = 0; c0 < nch; c0 += kSelThreads) {  // uniform trip count
+    const int c = c0 + tid;
+    const size_t slot = ((size_t)e * maxch + c) * 2;
+    const uint32_t g = c < nch ? w.counts[slot] : 0u, q = c < nch ? w.counts[slot + 1] : 0u;
+    uint32_t tg, tq;
+    const uint32_t ig = block_incl_scan(g, tg, sh[0]);
+    const uint32_t iq = block_incl_scan(q, tq, sh[1]);
+    if (c < nch) {
+      w.offs[slot] = rg + ig - g;
+      w.offs[slot + 1] = re + iq - q;
     }
+    rg += tg;
+    re += tq;
   }
-  __syncthreads();
-  if (tid == 0) *w.ticket = 0;
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_write_kernel(const float* __restrict__ R,
@@ -233,7 +255,7 @@ __global__ __launch_bounds__(kSelThreads) void select_write_kernel(const float* 
                                                                    SelWs w, int maxch, int64_t K_tot,
                                                                    int32_t* __restrict__ sel,
                                                                    uint8_t* __restrict__ keep) {
-  __shared__ uint32_t wtot[2][2][kSelThreads / kWave];
+  __shared__ uint32_t wtot[kSelPer][2][kSelThreads / kWave];
   const int e = blockIdx.y, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const SegState st = w.state[e];
   const int64_t lo = seg_off[e] + (int64_t)blockIdx.x * kChunk;
@@ -244,24 +266,30 @@ __global__ __launch_bounds__(kSelThreads) void select_write_kernel(const float* 
   const uint32_t need = st.mode == kKeepThreshold ? st.need : 0u;
   const int64_t cbase = cseg_off[e], cend = min(cseg_off[e + 1], K_tot);
   const uint64_t lt_mask = (1ull << lane) - 1ull;
-  uint32_t run_gt = 0, run_eq = 0;
+  uint32_t k[kSelPer];
+  const uint32_t ok = load_chunk(R, lo, hi, k);
+  uint64_t bg[kSelPer], be[kSelPer];
+#pragma unroll
   for (int r = 0; r < kSelPer; ++r) {
-    const int64_t i = lo + (int64_t)r * kSelThreads + tid;
-    const bool valid = i < hi;
-    const uint32_t key = valid ? __float_as_uint(R[i]) : 0u;
-    const bool gt = valid && (st.mode == kKeepAll || (st.mode == kKeepThreshold && key > st.prefix));
-    const bool eq = valid && st.mode == kKeepThreshold && key == st.prefix;
-    const uint64_t bg = __ballot(gt), be = __ballot(eq);
-    const int buf = r & 1;
+    const bool v = ok >> r & 1;
+    const bool gt = v && (st.mode == kKeepAll || (st.mode == kKeepThreshold && k[r] > st.prefix));
+    const bool eq = v && st.mode == kKeepThreshold && k[r] == st.prefix;
+    bg[r] = __ballot(gt);
+    be[r] = __ballot(eq);
     if (lane == 0) {
-      wtot[buf][0][wave] = (uint32_t)__popcll(bg);
-      wtot[buf][1][wave] = (uint32_t)__popcll(be);
+      wtot[r][0][wave] = (uint32_t)__popcll(bg[r]);
+      wtot[r][1][wave] = (uint32_t)__popcll(be[r]);
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  // keys before (r, wave, lane) in index order: rows r' < r, then earlier waves of row r
+  uint32_t run_gt = 0, run_eq = 0;
+#pragma unroll
+  for (int r = 0; r < kSelPer; ++r) {
     uint32_t og = 0, oe = 0, tg = 0, te = 0;
 #pragma unroll
     for (int v = 0; v < kSelThreads / kWave; ++v) {
-      const uint32_t a = wtot[buf][0][v], b = wtot[buf][1][v];
+      const uint32_t a = wtot[r][0][v], b = wtot[r][1][v];
       if (v < wave) {
         og += a;
         oe += b;
@@ -269,14 +297,16 @@ __global__ __launch_bounds__(kSelThreads) void select_write_kernel(const float* 
       tg += a;
       te += b;
     }
-    const uint32_t gt_before = base_gt + run_gt + og + (uint32_t)__popcll(bg & lt_mask);
-    const uint32_t eq_before = base_eq + run_eq + oe + (uint32_t)__popcll(be & lt_mask);
-    const bool k = gt || (eq && eq_before < need);
-    if (k) {
+    const int64_t i = lo + (int64_t)r * kSelThreads + tid;
+    const bool gt = bg[r] >> lane & 1, eq = be[r] >> lane & 1;
+    const uint32_t gt_before = base_gt + run_gt + og + (uint32_t)__popcll(bg[r] & lt_mask);
+    const uint32_t eq_before = base_eq + run_eq + oe + (uint32_t)__popcll(be[r] & lt_mask);
+    const bool kp = gt || (eq && eq_before < need);
+    if (kp) {
       const int64_t pos = cbase + gt_before + min(eq_before, need);
       if (pos < cend) sel[pos] = (int32_t)i;
     }
-    if (keep != nullptr && valid) keep[i] = k ? 1 : 0;
+    if (keep != nullptr && (ok >> r & 1)) keep[i] = kp ? 1 : 0;
     run_gt += tg;
     run_eq += te;
   }
@@ -290,16 +320,20 @@ lrmoe_status launch_select(const lrmoe_problem* p, const float* R, const int64_t
                            const int32_t* quota_d, const int64_t* cseg_off_d, int32_t* sel,
                            uint8_t* keep, void* ws, hipStream_t s) {
   const int E = p->E, maxch = max_chunks(p);
+  if (E <= 0) return LRMOE_OK;
   int64_t K_tot = 0;
   for (int e = 0; e < E; ++e) K_tot += p->quota[e];
   SelWs w = carve(ws, E, maxch);
-  const int64_t init_threads = std::max<int64_t>((int64_t)E * kBins, 1);
-  select_init_kernel<<<(unsigned)ceil_div(init_threads, kSelThreads), kSelThreads, 0, s>>>(E, seg_off_d, quota_d, w);
-  dim3 grid(maxch, E);
-  select_hist_kernel<<<grid, kSelThreads, 0, s>>>(21, 11, R, seg_off_d, w, E);
-  select_hist_kernel<<<grid, kSelThreads, 0, s>>>(10, 11, R, seg_off_d, w, E);
-  select_hist_kernel<<<grid, kSelThreads, 0, s>>>(0, 10, R, seg_off_d, w, E);
-  select_count_kernel<<<grid, kSelThreads, 0, s>>>(R, seg_off_d, w, E, maxch);
+  select_init_kernel<<<(unsigned)ceil_div((int64_t)E * kBins, kSelThreads), kSelThreads, 0, s>>>(E, seg_off_d,
+                                                                                                   quota_d, w);
+  const dim3 grid(maxch, E);
+  const int shifts[3] = {21, 10, 0}, bits[3] = {11, 11, 10};
+  for (int pass = 0; pass < 3; ++pass) {
+    select_hist_kernel<<<grid, kSelThreads, 0, s>>>(shifts[pass], bits[pass], R, seg_off_d, w);
+    select_digit_kernel<<<E, kSelThreads, 0, s>>>(shifts[pass], bits[pass], w);
+  }
+  select_count_kernel<<<grid, kSelThreads, 0, s>>>(R, seg_off_d, w, maxch);
+  select_offs_kernel<<<E, kSelThreads, 0, s>>>(seg_off_d, w, maxch);
   select_write_kernel<<<grid, kSelThreads, 0, s>>>(R, seg_off_d, cseg_off_d, w, maxch, K_tot, sel, keep);
   return launch_status();
 }

@@ -54,16 +54,68 @@ __device__ __forceinline__ void store8(float* __restrict__ out, int64_t row, int
   p[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// One wavefront per token: out[t] = sum over k of rows[map[t][k]], in slot order.
+// One wavefront per token: out[t] = sum over k of rows[map[t][k]], in slot order. The
+// token's K map entries are read once (wave-uniform), and for K <= kMaxK every row chunk
+// of two column blocks is loaded before the first add, so a lane keeps up to 2K loads in
+// flight; the adds still run in slot order.
+constexpr int kMaxK = 8;
+
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void token_reduce_kernel(int T, int K, int width,
                                                                 const int32_t* __restrict__ map,
                                                                 const void* __restrict__ rows,
                                                                 float* __restrict__ out) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + threadIdx.x / kWave;
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (t >= T) return;
   const int n8 = width / 8;
+  if (K <= kMaxK) {
+    int32_t m[kMaxK];
+#pragma unroll
+    for (int k = 0; k < kMaxK; ++k) m[k] = k < K ? __builtin_amdgcn_readfirstlane(map[t * K + k]) : -1;
+    constexpr int W = BF16 ? 1 : 2;  // 16-byte words per 8 elements
+    for (int c0 = lane; c0 < n8; c0 += 2 * kWave) {
+      uint4 raw[2][kMaxK][W];
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k) {
+          const int c8 = c0 + u * kWave;
+          const bool ok = m[k] >= 0 && c8 < n8;
+#pragma unroll
+          for (int q = 0; q < W; ++q)
+            raw[u][k][q] = ok ? ld_stream((const uint4*)rows + ((int64_t)m[k] * width / 8 + c8) * W + q)
+                              : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int c8 = c0 + u * kWave;
+        if (c8 >= n8) break;
+        float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < kMaxK; ++k) {
+          float v[8];
+          if (BF16) {
+            const uint32_t w[4] = {raw[u][k][0].x, raw[u][k][0].y, raw[u][k][0].z, raw[u][k][0].w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v[2 * i] = bf16_lo(w[i]);
+              v[2 * i + 1] = bf16_hi(w[i]);
+            }
+          } else {
+            const uint32_t w[8] = {raw[u][k][0].x, raw[u][k][0].y, raw[u][k][0].z, raw[u][k][0].w,
+                                   raw[u][k][W - 1].x, raw[u][k][W - 1].y, raw[u][k][W - 1].z, raw[u][k][W - 1].w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(w[i]);
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += v[i];
+        }
+        store8(out, t, width, c8, acc);
+      }
+    }
+    return;
+  }
   for (int c8 = lane; c8 < n8; c8 += kWave) {
     float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     for (int k = 0; k < K; ++k) {

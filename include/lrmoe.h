@@ -124,14 +124,19 @@ lrmoe_status lrmoe_select(const lrmoe_problem* p, const float* R, const int64_t*
  *   PhiC[c] = Phi[j];  XC[c] = X[t];  HC[c] = H[j];  ctok[c] = t;  cslot[c] = slot[j]
  *   Dlt, XC [K_tot x D]; PhiC [K_tot x F]; HC [K_tot x 2F]; ctok, cslot [K_tot] int32.
  *   X, H, XC, HC are used only when swiglu = 1 (else pass NULL). keep is ignored.
+ *   Each (token, slot) position holds at most one pair (a token routes to an expert through
+ *   one slot); the gather runs token by token through a [T x K] position map kept in ws, so
+ *   a token's G and X rows are read from HBM once for all of its retained pairs. A packed
+ *   row whose pair has tok outside [0,T) or slot outside [0,K) is left untouched.
  * ZERO_MASKED, for every pair j < N: Dlt[j] = keep[j] ? alpha[j] * G[tok[j]] : 0 and
  *   XC[j] = X[tok[j]] (swiglu); sel is ignored; PhiC and HC must be NULL (the GEMMs read
- *   Phi and H in place); ctok/cslot, if not NULL, receive copies of tok/slot. */
+ *   Phi and H in place); ctok/cslot, if not NULL, receive copies of tok/slot. ws may be NULL.
+ * ws: scratch of at least lrmoe_workspace_size bytes (PHYSICAL), else LRMOE_ERR_WORKSPACE. */
 lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, const int32_t* sel,
                            const uint8_t* keep, const void* G, const void* Phi, const void* X,
                            const void* H, const float* alpha, const int32_t* tok, const int32_t* slot,
                            void* Dlt, void* PhiC, void* XC, void* HC, int32_t* ctok, int32_t* cslot,
-                           lrmoe_stream_t stream);
+                           void* ws, size_t ws_bytes, lrmoe_stream_t stream);
 
 /* Step 4 - packed expert backward, variable-size grouped GEMMs (section 3.4: the FC2
  * and FC1 data- and weight-gradient GEMMs on the retained rows; section 3.1: the

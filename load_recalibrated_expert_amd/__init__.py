@@ -128,10 +128,11 @@ def compact(p: Problem, G, Phi, alpha, tok, slot, sel=None, keep=None, X=None, H
         o.setdefault("XC", torch.empty(max(rows, 1), p.D, dtype=dt, device=dev))
     o.setdefault("ctok", torch.empty(max(rows, 1), dtype=torch.int32, device=dev))
     o.setdefault("cslot", torch.empty(max(rows, 1), dtype=torch.int32, device=dev))
+    ws = p.workspace()
     _lib.check(library().lrmoe_compact(
         ctypes.byref(p.c), mode, _ptr(sel), _ptr(keep), _ptr(G), _ptr(Phi), _ptr(X), _ptr(H), _ptr(alpha),
         _ptr(tok), _ptr(slot), _ptr(o["Dlt"]), _ptr(o.get("PhiC")), _ptr(o.get("XC")), _ptr(o.get("HC")),
-        _ptr(o["ctok"]), _ptr(o["cslot"]), _stream(stream)), "lrmoe_compact")
+        _ptr(o["ctok"]), _ptr(o["cslot"]), _ptr(ws), ws.numel(), _stream(stream)), "lrmoe_compact")
     return {k: v[:rows] for k, v in o.items()}
 
 

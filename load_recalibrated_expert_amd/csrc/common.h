@@ -96,7 +96,8 @@ lrmoe_status launch_compact(const lrmoe_problem* p, int64_t rows, bool masked, c
                             const uint8_t* keep, const void* G, const void* Phi, const void* X,
                             const void* H, const float* alpha, const int32_t* tok, const int32_t* slot,
                             void* Dlt, void* PhiC, void* XC, void* HC, int32_t* ctok, int32_t* cslot,
-                            hipStream_t s);
+                            void* ws, hipStream_t s);
+size_t compact_ws_bytes(const lrmoe_problem* p);
 
 size_t gemm_ws_bytes(const lrmoe_problem* p, const int64_t* row_off_h);
 lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_off_h,

@@ -7,8 +7,13 @@
 // The zero-masked baseline of section 3.4 keeps all N rows and zeroes the dropped pairs'
 // gradient rows instead.
 //
-// HBM-bound gather/copy: one wavefront per packed row, 16-byte vector accesses, several
-// loads in flight per lane before the matching stores.
+// HBM-bound gather/copy with 16-byte vector accesses, several loads in flight per lane
+// before the matching stores. Physical compaction runs token-major: a [T x K] map from
+// (token, slot) to packed row is built first (each position holds at most one pair), then
+// one wavefront per token writes all of its retained rows. Every pair of a token gathers
+// the same G and X rows, so they come from HBM once and from L2 for the other pairs; in
+// packed-row order the pairs of a token lie in different expert segments and each would
+// fetch the rows again. The zero-masked baseline keeps pair order, one wavefront per row.
 #include "common.h"
 
 namespace lrmoe {
@@ -36,14 +41,16 @@ __device__ __forceinline__ uint4 scale_f32x4(float a, uint4 g) {
   return o;
 }
 
-// dst[0..n) = src[0..n), 16-byte chunks strided over the wavefront.
+// dst[0..n) = src[0..n), 16-byte chunks strided over the wavefront. STREAM marks rows read
+// once (Phi, H); token rows (X) stay cacheable for the token's other pairs.
+template <bool STREAM>
 __device__ __forceinline__ void copy_row(uint4* __restrict__ dst, const uint4* __restrict__ src, int n, int lane) {
   for (int c0 = lane; c0 < n; c0 += kWave * kU) {
     uint4 v[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int c = c0 + u * kWave;
-      if (c < n) v[u] = ld_stream(src + c);
+      if (c < n) v[u] = STREAM ? ld_stream(src + c) : src[c];
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -53,24 +60,15 @@ __device__ __forceinline__ void copy_row(uint4* __restrict__ dst, const uint4* _
   }
 }
 
+// Writes packed row c of pair j (token t): Dlt, and unless MASKED PhiC/HC; XC when gated.
 template <bool BF16, bool SWIGLU, bool MASKED>
-__global__ __launch_bounds__(kThreads) void compact_kernel(
-    int64_t rows, int64_t N, int T, int dch, int fch, const int32_t* __restrict__ sel, const uint8_t* __restrict__ keep,
-    const uint4* __restrict__ G, const uint4* __restrict__ Phi, const uint4* __restrict__ X,
-    const uint4* __restrict__ H, const float* __restrict__ alpha, const int32_t* __restrict__ tok,
-    const int32_t* __restrict__ slot, uint4* __restrict__ Dlt, uint4* __restrict__ PhiC, uint4* __restrict__ XC,
-    uint4* __restrict__ HC, int32_t* __restrict__ ctok, int32_t* __restrict__ cslot) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t c = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
-  if (c >= rows) return;  // whole wavefront
-  const int64_t j = MASKED ? c : (int64_t)sel[c];
-  if (j < 0 || j >= N) return;  // not a pair index: nothing to gather
-  const int t = tok[j];
-  const bool tok_ok = t >= 0 && t < T;
-  const bool kept = MASKED ? (keep[j] != 0) : true;
-  const float a = alpha[j];
-  // weighted gradient row
-  {
+__device__ __forceinline__ void gather_row(int64_t c, int64_t j, int t, bool tok_ok, bool kept, float a, int dch,
+                                           int fch, int lane, const uint4* __restrict__ G,
+                                           const uint4* __restrict__ Phi, const uint4* __restrict__ X,
+                                           const uint4* __restrict__ H, uint4* __restrict__ Dlt,
+                                           uint4* __restrict__ PhiC, uint4* __restrict__ XC,
+                                           uint4* __restrict__ HC) {
+  {  // weighted gradient row
     const uint4* src = G + (int64_t)t * dch;
     uint4* dst = Dlt + c * dch;
     for (int c0 = lane; c0 < dch; c0 += kWave * kU) {
@@ -78,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int cc = c0 + u * kWave;
-        v[u] = (cc < dch && kept && tok_ok) ? ld_stream(src + cc) : make_uint4(0, 0, 0, 0);
+        v[u] = (cc < dch && kept && tok_ok) ? src[cc] : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
@@ -88,50 +86,119 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(
     }
   }
   if (!MASKED) {
-    copy_row(PhiC + c * fch, Phi + j * fch, fch, lane);
-    if (SWIGLU) copy_row(HC + c * 2 * fch, H + j * 2 * fch, 2 * fch, lane);
+    copy_row<true>(PhiC + c * fch, Phi + j * fch, fch, lane);
+    if (SWIGLU) copy_row<true>(HC + c * 2 * fch, H + j * 2 * fch, 2 * fch, lane);
   }
   if (SWIGLU) {
-    if (tok_ok) copy_row(XC + c * dch, X + (int64_t)t * dch, dch, lane);
-  }
-  if (lane == 0) {
-    if (ctok) ctok[c] = t;
-    if (cslot) cslot[c] = slot[j];
+    if (tok_ok) copy_row<false>(XC + c * dch, X + (int64_t)t * dch, dch, lane);
   }
 }
 
-template <bool BF16, bool SWIGLU, bool MASKED>
-void launch(int64_t rows, const lrmoe_problem* p, const int32_t* sel, const uint8_t* keep, const void* G,
-            const void* Phi, const void* X, const void* H, const float* alpha, const int32_t* tok,
+// Zero-masked baseline: one wavefront per pair row, in pair order.
+template <bool BF16, bool SWIGLU>
+__global__ __launch_bounds__(kThreads) void compact_masked_kernel(
+    int64_t rows, int T, int dch, int fch, const uint8_t* __restrict__ keep, const uint4* __restrict__ G,
+    const uint4* __restrict__ X, const float* __restrict__ alpha, const int32_t* __restrict__ tok,
+    const int32_t* __restrict__ slot, uint4* __restrict__ Dlt, uint4* __restrict__ XC,
+    int32_t* __restrict__ ctok, int32_t* __restrict__ cslot) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t c = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kWave;
+  if (c >= rows) return;  // whole wavefront
+  const int t = tok[c];
+  const bool tok_ok = t >= 0 && t < T;
+  gather_row<BF16, SWIGLU, true>(c, c, t, tok_ok, keep[c] != 0, alpha[c], dch, fch, lane, G, nullptr, X, nullptr,
+                                 Dlt, nullptr, XC, nullptr);
+  if (lane == 0) {
+    if (ctok) ctok[c] = t;
+    if (cslot) cslot[c] = slot[c];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void position_fill_kernel(int64_t n, int32_t* __restrict__ map) {
+  const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (i < n) map[i] = -1;
+}
+
+// map[t*K + k] = packed row of the retained pair at token t, slot k (pairs whose token or
+// slot is out of range are skipped, and their rows are left untouched).
+__global__ __launch_bounds__(kThreads) void position_map_kernel(int64_t rows, int64_t N, int T, int K,
+                                                                const int32_t* __restrict__ sel,
+                                                                const int32_t* __restrict__ tok,
+                                                                const int32_t* __restrict__ slot,
+                                                                int32_t* __restrict__ map) {
+  const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (c >= rows) return;
+  const int64_t j = sel[c];
+  if (j < 0 || j >= N) return;
+  const int t = tok[j], k = slot[j];
+  if (t >= 0 && t < T && k >= 0 && k < K) map[(int64_t)t * K + k] = (int32_t)c;
+}
+
+// Physical compaction, one wavefront per token: every retained row of the token in slot order.
+template <bool BF16, bool SWIGLU>
+__global__ __launch_bounds__(kThreads) void compact_token_kernel(
+    int T, int K, int dch, int fch, const int32_t* __restrict__ map, const int32_t* __restrict__ sel,
+    const uint4* __restrict__ G, const uint4* __restrict__ Phi, const uint4* __restrict__ X,
+    const uint4* __restrict__ H, const float* __restrict__ alpha, const int32_t* __restrict__ slot,
+    uint4* __restrict__ Dlt, uint4* __restrict__ PhiC, uint4* __restrict__ XC, uint4* __restrict__ HC,
+    int32_t* __restrict__ ctok, int32_t* __restrict__ cslot) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (t >= T) return;  // whole wavefront
+  for (int k = 0; k < K; ++k) {
+    const int32_t c = __builtin_amdgcn_readfirstlane(map[(int64_t)t * K + k]);
+    if (c < 0) continue;
+    const int64_t j = __builtin_amdgcn_readfirstlane(sel[c]);
+    gather_row<BF16, SWIGLU, false>(c, j, t, true, true, alpha[j], dch, fch, lane, G, Phi, X, H, Dlt, PhiC, XC,
+                                    HC);
+    if (lane == 0) {
+      ctok[c] = t;
+      cslot[c] = slot[j];
+    }
+  }
+}
+
+template <bool BF16, bool SWIGLU>
+void launch(int64_t rows, bool masked, const lrmoe_problem* p, const int32_t* sel, const uint8_t* keep,
+            const void* G, const void* Phi, const void* X, const void* H, const float* alpha, const int32_t* tok,
             const int32_t* slot, void* Dlt, void* PhiC, void* XC, void* HC, int32_t* ctok, int32_t* cslot,
-            hipStream_t s) {
+            int32_t* map, hipStream_t s) {
   const int esz = BF16 ? 2 : 4;
   const int dch = p->D * esz / 16, fch = p->F * esz / 16;
-  compact_kernel<BF16, SWIGLU, MASKED><<<(unsigned)ceil_div(rows, kRowsPerBlock), kThreads, 0, s>>>(
-      rows, p->N, p->T, dch, fch, sel, keep, (const uint4*)G, (const uint4*)Phi, (const uint4*)X, (const uint4*)H,
-      alpha, tok, slot, (uint4*)Dlt, (uint4*)PhiC, (uint4*)XC, (uint4*)HC, ctok, cslot);
+  if (masked) {
+    compact_masked_kernel<BF16, SWIGLU><<<(unsigned)ceil_div(rows, kRowsPerBlock), kThreads, 0, s>>>(
+        rows, p->T, dch, fch, keep, (const uint4*)G, (const uint4*)X, alpha, tok, slot, (uint4*)Dlt, (uint4*)XC, ctok,
+        cslot);
+    return;
+  }
+  const int64_t positions = (int64_t)p->T * p->K;
+  position_fill_kernel<<<(unsigned)ceil_div(positions, kThreads), kThreads, 0, s>>>(positions, map);
+  position_map_kernel<<<(unsigned)ceil_div(rows, kThreads), kThreads, 0, s>>>(rows, p->N, p->T, p->K, sel, tok, slot,
+                                                                              map);
+  compact_token_kernel<BF16, SWIGLU><<<(unsigned)ceil_div(p->T, kRowsPerBlock), kThreads, 0, s>>>(
+      p->T, p->K, dch, fch, map, sel, (const uint4*)G, (const uint4*)Phi, (const uint4*)X, (const uint4*)H, alpha,
+      slot, (uint4*)Dlt, (uint4*)PhiC, (uint4*)XC, (uint4*)HC, ctok, cslot);
 }
 
 }  // namespace
+
+size_t compact_ws_bytes(const lrmoe_problem* p) { return align_up(sizeof(int32_t) * (size_t)p->T * p->K, 256); }
 
 lrmoe_status launch_compact(const lrmoe_problem* p, int64_t rows, bool masked, const int32_t* sel,
                             const uint8_t* keep, const void* G, const void* Phi, const void* X,
                             const void* H, const float* alpha, const int32_t* tok, const int32_t* slot,
                             void* Dlt, void* PhiC, void* XC, void* HC, int32_t* ctok, int32_t* cslot,
-                            hipStream_t s) {
+                            void* ws, hipStream_t s) {
   if (rows <= 0) return LRMOE_OK;
   const bool bf16 = p->dtype == LRMOE_BF16, sw = p->swiglu != 0;
-#define LRMOE_COMPACT_CASE(B, S, M)                                                                      \
-  if (bf16 == B && sw == S && masked == M)                                                               \
-    launch<B, S, M>(rows, p, sel, keep, G, Phi, X, H, alpha, tok, slot, Dlt, PhiC, XC, HC, ctok, cslot, s);
-  LRMOE_COMPACT_CASE(true, true, false)
-  LRMOE_COMPACT_CASE(true, true, true)
-  LRMOE_COMPACT_CASE(true, false, false)
-  LRMOE_COMPACT_CASE(true, false, true)
-  LRMOE_COMPACT_CASE(false, true, false)
-  LRMOE_COMPACT_CASE(false, true, true)
-  LRMOE_COMPACT_CASE(false, false, false)
-  LRMOE_COMPACT_CASE(false, false, true)
+  int32_t* map = (int32_t*)ws;
+#define LRMOE_COMPACT_CASE(B, S)                                                                               \
+  if (bf16 == B && sw == S)                                                                                    \
+    launch<B, S>(rows, masked, p, sel, keep, G, Phi, X, H, alpha, tok, slot, Dlt, PhiC, XC, HC, ctok, cslot, map, s);
+  LRMOE_COMPACT_CASE(true, true)
+  LRMOE_COMPACT_CASE(true, false)
+  LRMOE_COMPACT_CASE(false, true)
+  LRMOE_COMPACT_CASE(false, false)
 #undef LRMOE_COMPACT_CASE
   return launch_status();
 }

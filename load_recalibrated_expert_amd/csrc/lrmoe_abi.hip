@@ -42,6 +42,7 @@ size_t ws_need(const lrmoe_problem* p, lrmoe_compact_mode mode) {
   const int64_t* row_off = mode == LRMOE_COMPACT_ZERO_MASKED ? p->seg_off : cseg.data();
   size_t b = align_up(sizeof(double) * (size_t)p->T, 256);  // score: token norms
   b = std::max(b, select_ws_bytes(p));
+  b = std::max(b, compact_ws_bytes(p));
   b = std::max(b, gemm_ws_bytes(p, row_off));
   b = std::max(b, scatter_ws_bytes(p));
   return std::max<size_t>(b, 256);
@@ -110,7 +111,8 @@ lrmoe_status lrmoe_select(const lrmoe_problem* p, const float* R, const int64_t*
 lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, const int32_t* sel,
                            const uint8_t* keep, const void* G, const void* Phi, const void* X, const void* H,
                            const float* alpha, const int32_t* tok, const int32_t* slot, void* Dlt, void* PhiC,
-                           void* XC, void* HC, int32_t* ctok, int32_t* cslot, lrmoe_stream_t stream) {
+                           void* XC, void* HC, int32_t* ctok, int32_t* cslot, void* ws, size_t ws_bytes,
+                           lrmoe_stream_t stream) {
   int64_t K_tot = 0;
   LRMOE_TRY(check_problem(p, &K_tot, nullptr));
   const bool sw = p->swiglu != 0;
@@ -120,8 +122,9 @@ lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, cons
       return LRMOE_ERR_INVALID_ARG;
     if (sw && (!X || !H || !XC || !HC)) return LRMOE_ERR_INVALID_ARG;
     if (!sw && (X || H || XC || HC)) return LRMOE_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < compact_ws_bytes(p)) return LRMOE_ERR_WORKSPACE;
     return launch_compact(p, K_tot, false, sel, nullptr, G, Phi, X, H, alpha, tok, slot, Dlt, PhiC, XC, HC,
-                          ctok, cslot, (hipStream_t)stream);
+                          ctok, cslot, ws, (hipStream_t)stream);
   }
   if (mode == LRMOE_COMPACT_ZERO_MASKED) {
     if (p->N == 0) return LRMOE_OK;
@@ -130,7 +133,7 @@ lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, cons
     if (sw && (!X || !XC)) return LRMOE_ERR_INVALID_ARG;
     if (!sw && (X || XC)) return LRMOE_ERR_INVALID_ARG;
     return launch_compact(p, p->N, true, nullptr, keep, G, Phi, X, H, alpha, tok, slot, Dlt, nullptr, XC,
-                          nullptr, ctok, cslot, (hipStream_t)stream);
+                          nullptr, ctok, cslot, nullptr, (hipStream_t)stream);
   }
   return LRMOE_ERR_INVALID_ARG;
 }

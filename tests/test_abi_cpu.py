@@ -106,7 +106,10 @@ def test_workspace_size_and_host_side_rejections():
     assert lib.lrmoe_select(ctypes.byref(p), fake, fake, fake, fake, fake, None, None, 0, None) == _lib.ERR_WORKSPACE
     assert lib.lrmoe_scatter(ctypes.byref(p), 0, 3, 12, _lib.BF16, fake, fake, fake, fake, fake, 1 << 20,
                              None) == _lib.ERR_INVALID_ARG  # width not a multiple of 8
-    assert lib.lrmoe_compact(ctypes.byref(p), 5, *([None] * 15), None) == _lib.ERR_INVALID_ARG
+    assert lib.lrmoe_compact(ctypes.byref(p), 5, *([None] * 15), None, 0, None) == _lib.ERR_INVALID_ARG
+    sw = [fake] * 15 if p.swiglu else [fake, None, fake, fake, None, None, fake, fake, fake, fake, fake, None,
+                                         None, fake, fake]
+    assert lib.lrmoe_compact(ctypes.byref(p), _lib.COMPACT_PHYSICAL, *sw, None, 0, None) == _lib.ERR_WORKSPACE
     q, keep2 = _problem(quota=(6, 0, 7))
     assert lib.lrmoe_grouped_gemm_bwd(ctypes.byref(q), 0, *([fake] * 11), 0, fake, 1 << 30,
                                       None) == _lib.ERR_INFEASIBLE_QUOTA

@@ -135,6 +135,7 @@ __global__ __launch_bounds__(kThreads) void position_map_kernel(int64_t rows, in
 }
 
 // Physical compaction, one wavefront per token: every retained row of the token in slot order.
+// Generic shapes: each row is gathered section by section.
 template <bool BF16, bool SWIGLU>
 __global__ __launch_bounds__(kThreads) void compact_token_kernel(
     int T, int K, int dch, int fch, const int32_t* __restrict__ map, const int32_t* __restrict__ sel,
@@ -158,6 +159,111 @@ __global__ __launch_bounds__(kThreads) void compact_token_kernel(
   }
 }
 
+// Same rows for shapes whose rows fit the registers (dch <= 64 DL, fch <= 64 FL chunks): the
+// token's G and X rows are loaded once and kept in registers, and the next pair's Phi and
+// H rows are loaded before the current pair's rows are stored, so loads never queue behind
+// the stores of the same pair (vector memory operations complete in issue order).
+template <bool BF16, bool SWIGLU, int DL, int FL>
+__global__ __launch_bounds__(kThreads) void compact_token_reg_kernel(
+    int T, int K, int dch, int fch, const int32_t* __restrict__ map, const int32_t* __restrict__ sel,
+    const uint4* __restrict__ G, const uint4* __restrict__ Phi, const uint4* __restrict__ X,
+    const uint4* __restrict__ H, const float* __restrict__ alpha, const int32_t* __restrict__ slot,
+    uint4* __restrict__ Dlt, uint4* __restrict__ PhiC, uint4* __restrict__ XC, uint4* __restrict__ HC,
+    int32_t* __restrict__ ctok, int32_t* __restrict__ cslot) {
+  constexpr int HL = SWIGLU ? 2 * FL : 1;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (t >= T) return;  // whole wavefront
+  const int hch = 2 * fch;
+  // next retained slot at or after k (K when none)
+  auto next_slot = [&](int k) {
+    for (; k < K; ++k)
+      if (__builtin_amdgcn_readfirstlane(map[(int64_t)t * K + k]) >= 0) return k;
+    return K;
+  };
+  int k = next_slot(0);
+  if (k >= K) return;
+  uint4 g[DL], x[SWIGLU ? DL : 1];
+#pragma unroll
+  for (int u = 0; u < DL; ++u) {
+    const int cc = lane + u * kWave;
+    g[u] = cc < dch ? G[(int64_t)t * dch + cc] : make_uint4(0, 0, 0, 0);
+    if (SWIGLU) x[u] = cc < dch ? X[(int64_t)t * dch + cc] : make_uint4(0, 0, 0, 0);
+  }
+  int32_t c = __builtin_amdgcn_readfirstlane(map[(int64_t)t * K + k]);
+  int64_t j = __builtin_amdgcn_readfirstlane(sel[c]);
+  uint4 ph[FL], hh[HL];
+#pragma unroll
+  for (int u = 0; u < FL; ++u) {
+    const int cc = lane + u * kWave;
+    ph[u] = cc < fch ? ld_stream(Phi + j * fch + cc) : make_uint4(0, 0, 0, 0);
+  }
+  if (SWIGLU) {
+#pragma unroll
+    for (int u = 0; u < HL; ++u) {
+      const int cc = lane + u * kWave;
+      hh[u] = cc < hch ? ld_stream(H + j * hch + cc) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  while (true) {
+    const float a = alpha[j];
+    const int kn = next_slot(k + 1);
+    int32_t cn = -1;
+    int64_t jn = 0;
+    uint4 phn[FL], hhn[HL];
+    if (kn < K) {  // uniform
+      cn = __builtin_amdgcn_readfirstlane(map[(int64_t)t * K + kn]);
+      jn = __builtin_amdgcn_readfirstlane(sel[cn]);
+#pragma unroll
+      for (int u = 0; u < FL; ++u) {
+        const int cc = lane + u * kWave;
+        phn[u] = cc < fch ? ld_stream(Phi + jn * fch + cc) : make_uint4(0, 0, 0, 0);
+      }
+      if (SWIGLU) {
+#pragma unroll
+        for (int u = 0; u < HL; ++u) {
+          const int cc = lane + u * kWave;
+          hhn[u] = cc < hch ? ld_stream(H + jn * hch + cc) : make_uint4(0, 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < DL; ++u) {
+      const int cc = lane + u * kWave;
+      if (cc < dch) {
+        Dlt[(int64_t)c * dch + cc] = BF16 ? scale_bf16x8(a, g[u]) : scale_f32x4(a, g[u]);
+        if (SWIGLU) XC[(int64_t)c * dch + cc] = x[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < FL; ++u) {
+      const int cc = lane + u * kWave;
+      if (cc < fch) PhiC[(int64_t)c * fch + cc] = ph[u];
+    }
+    if (SWIGLU) {
+#pragma unroll
+      for (int u = 0; u < HL; ++u) {
+        const int cc = lane + u * kWave;
+        if (cc < hch) HC[(int64_t)c * hch + cc] = hh[u];
+      }
+    }
+    if (lane == 0) {
+      ctok[c] = t;
+      cslot[c] = slot[j];
+    }
+    if (kn >= K) break;
+    k = kn;
+    c = cn;
+    j = jn;
+#pragma unroll
+    for (int u = 0; u < FL; ++u) ph[u] = phn[u];
+    if (SWIGLU) {
+#pragma unroll
+      for (int u = 0; u < HL; ++u) hh[u] = hhn[u];
+    }
+  }
+}
+
 template <bool BF16, bool SWIGLU>
 void launch(int64_t rows, bool masked, const lrmoe_problem* p, const int32_t* sel, const uint8_t* keep,
             const void* G, const void* Phi, const void* X, const void* H, const float* alpha, const int32_t* tok,
@@ -175,9 +281,15 @@ void launch(int64_t rows, bool masked, const lrmoe_problem* p, const int32_t* se
   position_fill_kernel<<<(unsigned)ceil_div(positions, kThreads), kThreads, 0, s>>>(positions, map);
   position_map_kernel<<<(unsigned)ceil_div(rows, kThreads), kThreads, 0, s>>>(rows, p->N, p->T, p->K, sel, tok, slot,
                                                                               map);
-  compact_token_kernel<BF16, SWIGLU><<<(unsigned)ceil_div(p->T, kRowsPerBlock), kThreads, 0, s>>>(
-      p->T, p->K, dch, fch, map, sel, (const uint4*)G, (const uint4*)Phi, (const uint4*)X, (const uint4*)H, alpha,
-      slot, (uint4*)Dlt, (uint4*)PhiC, (uint4*)XC, (uint4*)HC, ctok, cslot);
+  const unsigned grid = (unsigned)ceil_div(p->T, kRowsPerBlock);
+  if (dch <= 4 * kWave && fch <= 2 * kWave)
+    compact_token_reg_kernel<BF16, SWIGLU, 4, 2><<<grid, kThreads, 0, s>>>(
+        p->T, p->K, dch, fch, map, sel, (const uint4*)G, (const uint4*)Phi, (const uint4*)X, (const uint4*)H, alpha,
+        slot, (uint4*)Dlt, (uint4*)PhiC, (uint4*)XC, (uint4*)HC, ctok, cslot);
+  else
+    compact_token_kernel<BF16, SWIGLU><<<grid, kThreads, 0, s>>>(
+        p->T, p->K, dch, fch, map, sel, (const uint4*)G, (const uint4*)Phi, (const uint4*)X, (const uint4*)H, alpha,
+        slot, (uint4*)Dlt, (uint4*)PhiC, (uint4*)XC, (uint4*)HC, ctok, cslot);
 }
 
 }  // namespace

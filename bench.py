@@ -55,10 +55,12 @@ def algorithmic_bytes(cfg, N, K_tot):
     e = 2 if cfg.dtype == "bf16" else 4
     T, D, F = cfg.T, cfg.D, cfg.F
     score = (T * D + N * F) * e + N * (4 + 4 + 4)            # G, Phi, alpha, tok -> R
+    # compact reads each token's G (and X) row once and each retained pair's Phi (and H)
+    # row once, and writes every packed row once
     if cfg.swiglu:
-        compact = K_tot * (2 * D + 3 * F) * e * 2             # read + write Dlt, X, Phi, H rows
+        compact = (2 * T * D + 3 * K_tot * F) * e + K_tot * (2 * D + 3 * F) * e
     else:
-        compact = K_tot * (D + F) * e * 2
+        compact = (T * D + K_tot * F) * e + K_tot * (D + F) * e
     width = D if cfg.swiglu else F
     scatter = K_tot * width * e + T * width * 4
     return {"score": score, "compact": compact, "scatter": scatter}

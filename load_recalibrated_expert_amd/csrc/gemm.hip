@@ -521,10 +521,17 @@ __global__ __launch_bounds__(NTHR) void wgrad_kernel(WgradArgs g) {
   }
 }
 
-// Sums the chunk partials of every split tile in chunk order into the output.
+// Sums the chunk partials of every split tile in chunk order into the output. Each tile is
+// shared by kRedParts blocks of BM / kRedParts rows, so enough blocks are in flight to
+// cover the partials' read latency; a thread keeps its four float4 loads of a chunk in
+// flight together.
+constexpr int kRedParts = 8;
+constexpr int kRedPer = BM / kRedParts * (BN / 4) / NTHR;  // float4 per thread (4)
+
 __global__ __launch_bounds__(NTHR) void wgrad_reduce_kernel(WgradArgs g) {
   const int tiles = g.t[0].tiles + (g.ntypes > 1 ? g.t[1].tiles : 0);
-  int b = blockIdx.x, e = 0;
+  const int part = blockIdx.x % kRedParts;
+  int b = blockIdx.x / kRedParts, e = 0;
   for (; e < g.E; ++e) {
     if (g.plan_s[e] > 1) {
       if (b < tiles) break;
@@ -542,26 +549,43 @@ __global__ __launch_bounds__(NTHR) void wgrad_reduce_kernel(WgradArgs g) {
   const float* p0 = g.partials + (g.plan_pbase[e] + rem) * (int64_t)(BM * BN);
   const int64_t pstride = (int64_t)tiles * BM * BN;
   float* o = T.out + (int64_t)e * T.M * T.N;
-  for (int idx = threadIdx.x; idx < BM * BN / 4; idx += NTHR) {
-    const int r = idx / (BN / 4), c = (idx % (BN / 4)) * 4;
-    if (r >= m_valid || c >= n_valid) continue;
-    float4 sum = *(const float4*)(p0 + r * BN + c);
-    for (int ch = 1; ch < s; ++ch) {
-      const float4 v = *(const float4*)(p0 + ch * pstride + r * BN + c);
-      sum.x += v.x;
-      sum.y += v.y;
-      sum.z += v.z;
-      sum.w += v.w;
+  int r[kRedPer], c[kRedPer];
+  bool ok[kRedPer];
+  float4 sum[kRedPer];
+#pragma unroll
+  for (int u = 0; u < kRedPer; ++u) {
+    const int idx = part * (BM / kRedParts) * (BN / 4) + threadIdx.x + u * NTHR;
+    r[u] = idx / (BN / 4);
+    c[u] = (idx % (BN / 4)) * 4;
+    ok[u] = r[u] < m_valid && c[u] < n_valid;
+    sum[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int ch = 0; ch < s; ++ch) {
+    float4 v[kRedPer];
+#pragma unroll
+    for (int u = 0; u < kRedPer; ++u)
+      v[u] = ok[u] ? *(const float4*)(p0 + ch * pstride + r[u] * BN + c[u]) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < kRedPer; ++u) {
+      sum[u].x += v[u].x;
+      sum[u].y += v[u].y;
+      sum[u].z += v[u].z;
+      sum[u].w += v[u].w;
     }
-    float4* q = (float4*)(o + (int64_t)(m0 + r) * T.N + n0 + c);
+  }
+#pragma unroll
+  for (int u = 0; u < kRedPer; ++u) {
+    if (!ok[u]) continue;
+    float4* q = (float4*)(o + (int64_t)(m0 + r[u]) * T.N + n0 + c[u]);
+    float4 t = sum[u];
     if (g.accumulate) {
       const float4 old = *q;
-      sum.x += old.x;
-      sum.y += old.y;
-      sum.z += old.z;
-      sum.w += old.w;
+      t.x += old.x;
+      t.y += old.y;
+      t.z += old.z;
+      t.w += old.w;
     }
-    *q = sum;
+    *q = t;
   }
 }
 
@@ -808,7 +832,7 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
     const int64_t per_xcd = wgrad_xcd_ranges(p, row_off_h, w.xlo);
     wgrad_plan_kernel<<<1, NTHR, 0, s>>>(w);
     if (per_xcd > 0) wgrad_kernel<<<(unsigned)(8 * per_xcd), NTHR, 0, s>>>(w);
-    if (L.nreduce > 0) wgrad_reduce_kernel<<<(unsigned)L.nreduce, NTHR, 0, s>>>(w);
+    if (L.nreduce > 0) wgrad_reduce_kernel<<<(unsigned)(L.nreduce * kRedParts), NTHR, 0, s>>>(w);
   }
   return launch_status();
 }

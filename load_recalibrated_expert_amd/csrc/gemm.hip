@@ -11,17 +11,16 @@
 //   FC2 wgrad  dW2  = PhiC^T Dlt    reduction over the packed rows: operands are row-major
 //   FC1 wgrad  dW1  = XC^T dH       in the output dims, transposed on the way into LDS
 //
-// bf16 path: MFMA v_mfma_f32_32x32x16_bf16 with fp32 accumulation. A block of 256 threads
-// (four 64-wide wavefronts, 2x2) owns a 256x256 output tile; each wavefront a 128x128
-// sub-tile held as 4x4 MFMA accumulators. K advances 64 per stage through two LDS stages
-// (2 x 64 KB): the next stage's global loads are issued before the current stage's MFMAs
-// and written to the other LDS stage after them, one barrier per stage. LDS rows are
-// 128 bytes (64 bf16 along K) with the 16-byte chunk index XOR-swizzled by the row so
-// 16-byte fragment reads spread over the banks. Weight-gradient tiles split the packed rows
+// bf16 path: MFMA v_mfma_f32_32x32x16_bf16 with fp32 accumulation. A block of 512 threads
+// (eight 64-wide wavefronts, two per SIMD) owns a 256x256 output tile; each wavefront a
+// 128x64 sub-tile held as 2x4 MFMA accumulators. K advances 32 per stage through four LDS
+// stages (4 x 32 KB) filled by direct global-to-LDS loads issued three stages ahead, one
+// barrier per stage. Finished tiles leave through LDS so every output row is written by
+// consecutive threads with 16-byte accesses. Weight-gradient tiles split the packed rows
 // of large experts into K chunks; chunk partials go to the workspace and a second kernel
-// sums them in chunk order, so results do not depend on scheduling. Blocks are renumbered
-// so each XCD (hardware round-robins blocks over its 8 XCDs) walks a contiguous run of
-// tiles that share operands in its L2.
+// sums them in chunk order, so results do not depend on scheduling. Tiles are handed to
+// the 8 XCDs (hardware round-robins blocks over them) in contiguous runs, so tiles that
+// share operand panels meet in one L2; weight-gradient runs are cut by work, not count.
 //
 // f32 path (small problems): plain fp32 FMA kernels, no bf16 anywhere.
 #include <algorithm>

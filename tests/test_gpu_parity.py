@@ -43,6 +43,14 @@ SMALL = {
     "tiny": dict(cfg=synth.CONFIGS["tiny"], rho="0.75"),
     "quota_edges": dict(cfg=synth.custom("quota_edges", T=200, K=4, E=5, D=256, F=128,
                                          counts=(300, 200, 0, 100, 90), seed=16), quota=(0, 200, 0, 1, 89)),
+    # top-10 routing (scatter beyond 8 slots) over 40 experts, a third of them empty, so the
+    # weight-gradient items outnumber the XCDs and some XCD ranges may be empty
+    "many_experts_top10": dict(cfg=synth.custom("many_experts_top10", T=300, K=10, E=40, D=256, F=128,
+                                                counts=tuple((0 if e % 3 == 1 else 3 * e + 5) for e in range(40)),
+                                                seed=18), rho="0.5"),
+    # rows wider than the token compaction keeps in registers (D = 2304 bf16 elements)
+    "wide_rows": dict(cfg=synth.custom("wide_rows", T=150, K=3, E=3, D=2304, F=136, counts=(200, 90, 110),
+                                       seed=19), rho="0.7"),
 }
 
 

@@ -55,10 +55,11 @@ def algorithmic_bytes(cfg, N, K_tot):
     e = 2 if cfg.dtype == "bf16" else 4
     T, D, F = cfg.T, cfg.D, cfg.F
     score = (T * D + N * F) * e + N * (4 + 4 + 4)            # G, Phi, alpha, tok -> R
-    # compact reads each token's G (and X) row once and each retained pair's Phi (and H)
-    # row once, and writes every packed row once
+    # compact reads each token's G (and X) row once and each retained pair's Phi row once,
+    # and writes every packed row once (the saved [gate | up] rows are read in place by the
+    # GEMM, not packed)
     if cfg.swiglu:
-        compact = (2 * T * D + 3 * K_tot * F) * e + K_tot * (2 * D + 3 * F) * e
+        compact = (2 * T * D + K_tot * F) * e + K_tot * (2 * D + F) * e
     else:
         compact = (T * D + K_tot * F) * e + K_tot * (D + F) * e
     width = D if cfg.swiglu else F
@@ -177,14 +178,13 @@ def main():
         bufs.setdefault("sel", sel)
         bufs.setdefault("keep", keep)
         rec(2)
-        c = lr.compact(P, G, Phi, alpha, tok, slot, sel=sel, keep=keep, X=ins["X"], H=ins["H"], mode=mode,
-                       out=bufs.get("c"))
+        c = lr.compact(P, G, Phi, alpha, tok, slot, sel=sel, keep=keep, X=ins["X"], mode=mode, out=bufs.get("c"))
         bufs.setdefault("c", c)
         rec(3)
         PhiC = c["PhiC"] if mode == lr.COMPACT_PHYSICAL else Phi
-        HC = c.get("HC") if mode == lr.COMPACT_PHYSICAL else ins["H"]
-        g = lr.grouped_gemm_bwd(P, c["Dlt"], PhiC, ins["W2"], XC=c.get("XC"), HC=HC, W1=ins["W1"], mode=mode,
-                                out=bufs.get("g"))
+        hc_rows = sel if (mode == lr.COMPACT_PHYSICAL and cfg.swiglu) else None
+        g = lr.grouped_gemm_bwd(P, c["Dlt"], PhiC, ins["W2"], XC=c.get("XC"), HC=ins["H"], W1=ins["W1"], mode=mode,
+                                out=bufs.get("g"), hc_rows=hc_rows)
         bufs.setdefault("g", g)
         rec(4)
         ctok, cslot = (c["ctok"], c["cslot"]) if mode == lr.COMPACT_PHYSICAL else (tok, slot)

@@ -124,6 +124,9 @@ lrmoe_status lrmoe_select(const lrmoe_problem* p, const float* R, const int64_t*
  *   PhiC[c] = Phi[j];  XC[c] = X[t];  HC[c] = H[j];  ctok[c] = t;  cslot[c] = slot[j]
  *   Dlt, XC [K_tot x D]; PhiC [K_tot x F]; HC [K_tot x 2F]; ctok, cslot [K_tot] int32.
  *   X, H, XC, HC are used only when swiglu = 1 (else pass NULL). keep is ignored.
+ *   HC is optional (NULL: not written, and H may be NULL): the grouped GEMM reads the saved
+ *   [gate | up] rows only in its SwiGLU epilogue and can read them in place from H through
+ *   sel (its hc_rows argument), which saves the copy.
  *   Each (token, slot) position holds at most one pair (a token routes to an expert through
  *   one slot); the gather runs token by token through a [T x K] position map kept in ws, so
  *   a token's G and X rows are read from HBM once for all of its retained pairs. A packed
@@ -148,15 +151,19 @@ lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, cons
  *   dH        = [dPhi*up*silu'(gate), dPhi*silu(gate)] storage dtype [rows x 2F], out
  *   dW1[e] (+)= XC_e^T dH_e                           f32 [E x D x 2F]
  *   dIn       = dH_e W1[e]^T                          storage dtype [rows x D]
- * with gate = HC[:, :F], up = HC[:, F:]. For swiglu = 0 only dW2 and dIn = dPhi
- * [rows x F] are produced (dH, XC, HC, W1, dW1 must be NULL).
+ * with gate = HC[r, :F], up = HC[r, F:] for packed row c, where r = hc_rows[c] (hc_rows
+ * [rows] int32) or r = c when hc_rows is NULL. PHYSICAL mode with HC = H and hc_rows = sel
+ * reads the saved rows in place; ZERO_MASKED passes HC = H and hc_rows = NULL.
+ * For swiglu = 0 only dW2 and dIn = dPhi [rows x F] are produced (dH, XC, HC, hc_rows,
+ * W1, dW1 must be NULL).
  * accumulate = 0 overwrites dW1/dW2 (experts with no rows get 0); 1 adds to them.
  * bf16: MFMA with fp32 accumulation. f32: fp32 FMA throughout. */
 lrmoe_status lrmoe_grouped_gemm_bwd(const lrmoe_problem* p, lrmoe_compact_mode mode,
                                     const int64_t* row_off_d, const void* Dlt, const void* PhiC,
-                                    const void* XC, const void* HC, const void* W2, const void* W1,
-                                    float* dW2, float* dW1, void* dH, void* dIn, int32_t accumulate,
-                                    void* ws, size_t ws_bytes, lrmoe_stream_t stream);
+                                    const void* XC, const void* HC, const int32_t* hc_rows,
+                                    const void* W2, const void* W1, float* dW2, float* dW1, void* dH,
+                                    void* dIn, int32_t accumulate, void* ws, size_t ws_bytes,
+                                    lrmoe_stream_t stream);
 
 /* Step 5 - inverse mapping (section 3.1; Algorithm 1's ScatterWithZeros).
  * rows [n_rows x width] of dtype rows_dtype; row c belongs to pair (ctok[c], cslot[c]),

@@ -115,6 +115,8 @@ def select(p: Problem, R, sel=None, keep=None, want_keep=True, stream=None):
 
 def compact(p: Problem, G, Phi, alpha, tok, slot, sel=None, keep=None, X=None, H=None,
             mode=COMPACT_PHYSICAL, out=None, stream=None):
+    """Physical mode packs HC only when H is given; without it the grouped GEMM reads H in
+    place through sel."""
     rows = p.rows(mode)
     dt = p.torch_dtype
     o = dict(out or {})
@@ -122,7 +124,7 @@ def compact(p: Problem, G, Phi, alpha, tok, slot, sel=None, keep=None, X=None, H
     o.setdefault("Dlt", torch.empty(max(rows, 1), p.D, dtype=dt, device=dev))
     if mode == COMPACT_PHYSICAL:
         o.setdefault("PhiC", torch.empty(max(rows, 1), p.F, dtype=dt, device=dev))
-        if p.swiglu:
+        if p.swiglu and H is not None:
             o.setdefault("HC", torch.empty(max(rows, 1), 2 * p.F, dtype=dt, device=dev))
     if p.swiglu:
         o.setdefault("XC", torch.empty(max(rows, 1), p.D, dtype=dt, device=dev))
@@ -137,7 +139,9 @@ def compact(p: Problem, G, Phi, alpha, tok, slot, sel=None, keep=None, X=None, H
 
 
 def grouped_gemm_bwd(p: Problem, Dlt, PhiC, W2, XC=None, HC=None, W1=None, mode=COMPACT_PHYSICAL,
-                     out=None, accumulate=False, stream=None):
+                     out=None, accumulate=False, hc_rows=None, stream=None):
+    """``HC`` holds the saved [gate | up] rows the SwiGLU backward reads: packed rows, or the
+    pair rows ``H`` themselves with ``hc_rows`` (e.g. ``sel``) mapping packed row -> row."""
     rows = p.rows(mode)
     dt = p.torch_dtype
     dev = p.device
@@ -151,7 +155,8 @@ def grouped_gemm_bwd(p: Problem, Dlt, PhiC, W2, XC=None, HC=None, W1=None, mode=
         o.setdefault("dIn", torch.empty(max(rows, 1), p.F, dtype=dt, device=dev))
     ws = p.workspace()
     _lib.check(library().lrmoe_grouped_gemm_bwd(
-        ctypes.byref(p.c), mode, _ptr(p.row_off_d(mode)), _ptr(Dlt), _ptr(PhiC), _ptr(XC), _ptr(HC), _ptr(W2),
+        ctypes.byref(p.c), mode, _ptr(p.row_off_d(mode)), _ptr(Dlt), _ptr(PhiC), _ptr(XC), _ptr(HC), _ptr(hc_rows),
+        _ptr(W2),
         _ptr(W1), _ptr(o["dW2"]), _ptr(o.get("dW1")), _ptr(o.get("dH")), _ptr(o["dIn"]), int(bool(accumulate)),
         _ptr(ws), ws.numel(), _stream(stream)), "lrmoe_grouped_gemm_bwd")
     res = dict(o)
@@ -186,13 +191,14 @@ def backward(p: Problem, *, G, Phi, alpha, tok, slot, W2, X=None, H=None, W1=Non
     sel, keep = select(p, b["R"], sel=b.get("sel_full"), keep=b.get("keep_full"), stream=stream)
     b.setdefault("sel_full", sel)
     b.setdefault("keep_full", keep)
-    c = compact(p, G, Phi, alpha, tok, slot, sel=sel, keep=keep, X=X, H=H, mode=mode, out=b.get("compact"),
+    # the saved [gate | up] rows are not packed: the GEMM reads H in place through sel
+    c = compact(p, G, Phi, alpha, tok, slot, sel=sel, keep=keep, X=X, mode=mode, out=b.get("compact"),
                 stream=stream)
     b.setdefault("compact", c)
     PhiC = c["PhiC"] if mode == COMPACT_PHYSICAL else Phi
-    HC = c.get("HC") if mode == COMPACT_PHYSICAL else H
-    g = grouped_gemm_bwd(p, c["Dlt"], PhiC, W2, XC=c.get("XC"), HC=HC, W1=W1, mode=mode, out=b.get("gemm"),
-                         stream=stream)
+    hc_rows = sel if (mode == COMPACT_PHYSICAL and p.swiglu) else None
+    g = grouped_gemm_bwd(p, c["Dlt"], PhiC, W2, XC=c.get("XC"), HC=H, W1=W1, mode=mode, out=b.get("gemm"),
+                         hc_rows=hc_rows, stream=stream)
     b.setdefault("gemm", g)
     if mode == COMPACT_PHYSICAL:
         ctok, cslot = c["ctok"], c["cslot"]

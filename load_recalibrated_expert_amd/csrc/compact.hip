@@ -3,7 +3,8 @@
 // contiguous expert segments so the grouped GEMMs see only retained rows, with no
 // padding. Row c of every packed buffer belongs to the retained pair j = sel[c]:
 //   Dlt[c] = alpha_j * g_{tok_j} (the weighted cotangent, appendix 7.1 Eq. 5; alpha is
-//   applied here exactly once), PhiC[c] = Phi[j], XC[c] = X[tok_j], HC[c] = H[j].
+//   applied here exactly once), PhiC[c] = Phi[j], XC[c] = X[tok_j], and on request HC[c] = H[j]
+//   (the grouped GEMM can instead read H in place through sel).
 // The zero-masked baseline of section 3.4 keeps all N rows and zeroes the dropped pairs'
 // gradient rows instead.
 //
@@ -60,7 +61,8 @@ __device__ __forceinline__ void copy_row(uint4* __restrict__ dst, const uint4* _
   }
 }
 
-// Writes packed row c of pair j (token t): Dlt, and unless MASKED PhiC/HC; XC when gated.
+// Writes packed row c of pair j (token t): Dlt, and unless MASKED PhiC (and HC if given);
+// XC when gated.
 template <bool BF16, bool SWIGLU, bool MASKED>
 __device__ __forceinline__ void gather_row(int64_t c, int64_t j, int t, bool tok_ok, bool kept, float a, int dch,
                                            int fch, int lane, const uint4* __restrict__ G,
@@ -87,7 +89,7 @@ __device__ __forceinline__ void gather_row(int64_t c, int64_t j, int t, bool tok
   }
   if (!MASKED) {
     copy_row<true>(PhiC + c * fch, Phi + j * fch, fch, lane);
-    if (SWIGLU) copy_row<true>(HC + c * 2 * fch, H + j * 2 * fch, 2 * fch, lane);
+    if (SWIGLU && HC != nullptr) copy_row<true>(HC + c * 2 * fch, H + j * 2 * fch, 2 * fch, lane);
   }
   if (SWIGLU) {
     if (tok_ok) copy_row<false>(XC + c * dch, X + (int64_t)t * dch, dch, lane);
@@ -192,13 +194,14 @@ __global__ __launch_bounds__(kThreads) void compact_token_reg_kernel(
   }
   int32_t c = __builtin_amdgcn_readfirstlane(map[(int64_t)t * K + k]);
   int64_t j = __builtin_amdgcn_readfirstlane(sel[c]);
+  const bool with_hc = SWIGLU && HC != nullptr;
   uint4 ph[FL], hh[HL];
 #pragma unroll
   for (int u = 0; u < FL; ++u) {
     const int cc = lane + u * kWave;
     ph[u] = cc < fch ? ld_stream(Phi + j * fch + cc) : make_uint4(0, 0, 0, 0);
   }
-  if (SWIGLU) {
+  if (with_hc) {
 #pragma unroll
     for (int u = 0; u < HL; ++u) {
       const int cc = lane + u * kWave;
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void compact_token_reg_kernel(
         const int cc = lane + u * kWave;
         phn[u] = cc < fch ? ld_stream(Phi + jn * fch + cc) : make_uint4(0, 0, 0, 0);
       }
-      if (SWIGLU) {
+      if (with_hc) {
 #pragma unroll
         for (int u = 0; u < HL; ++u) {
           const int cc = lane + u * kWave;
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void compact_token_reg_kernel(
       const int cc = lane + u * kWave;
       if (cc < fch) PhiC[(int64_t)c * fch + cc] = ph[u];
     }
-    if (SWIGLU) {
+    if (with_hc) {
 #pragma unroll
       for (int u = 0; u < HL; ++u) {
         const int cc = lane + u * kWave;
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void compact_token_reg_kernel(
     j = jn;
 #pragma unroll
     for (int u = 0; u < FL; ++u) ph[u] = phn[u];
-    if (SWIGLU) {
+    if (with_hc) {
 #pragma unroll
       for (int u = 0; u < HL; ++u) hh[u] = hhn[u];
     }

@@ -313,7 +313,8 @@ struct DgradArgs {
   const int64_t* row_off;
   int E;
   // epilogue
-  const uint16_t* HC;  // SwiGLU: [rows x 2F] saved [gate | up]
+  const uint16_t* HC;  // SwiGLU: saved [gate | up] rows, 2F wide
+  const int32_t* hc_rows;  // row of HC for packed row c (nullptr: row c)
   uint16_t* out;       // SwiGLU: dH [rows x 2F]; STORE: [rows x N]
   int64_t ldo;
   int F;
@@ -355,8 +356,10 @@ __global__ __launch_bounds__(NTHR) void dgrad_kernel(DgradArgs g) {
     epilogue_staged(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&dphi)[8]) {
       if (tr < rows_valid && tc < n_valid) {
         const int64_t rowb = (row0 + tr) * ld + n0 + tc;
-        const uint4 gw = *(const uint4*)(hc + rowb);
-        const uint4 uw = *(const uint4*)(hc + rowb + F);
+        const int64_t hrow = g.hc_rows != nullptr ? (int64_t)g.hc_rows[row0 + tr] : row0 + tr;
+        const int64_t hb = hrow * ld + n0 + tc;
+        const uint4 gw = *(const uint4*)(hc + hb);
+        const uint4 uw = *(const uint4*)(hc + hb + F);
         const uint32_t gg[4] = {gw.x, gw.y, gw.z, gw.w}, uu[4] = {uw.x, uw.y, uw.z, uw.w};
         float dg[8], du[8];
 #pragma unroll
@@ -606,8 +609,9 @@ __global__ __launch_bounds__(NTHR) void f32_dgrad_kernel(const float* __restrict
                                                          const float* __restrict__ W, int64_t ldw,
                                                          int64_t w_estride, int N, int K,
                                                          const int64_t* __restrict__ row_off, int E,
-                                                         const float* __restrict__ HC, float* __restrict__ out,
-                                                         int64_t ldo, int F) {
+                                                         const float* __restrict__ HC,
+                                                         const int32_t* __restrict__ hc_rows,
+                                                         float* __restrict__ out, int64_t ldo, int F) {
   const int64_t r = blockIdx.x;
   const int n = blockIdx.y * NTHR + threadIdx.x;
   if (n >= N) return;
@@ -617,7 +621,8 @@ __global__ __launch_bounds__(NTHR) void f32_dgrad_kernel(const float* __restrict
   float acc = 0.0f;
   for (int k = 0; k < K; ++k) acc = fmaf(a[k], w[k], acc);
   if (EPI == EPI_SWIGLU) {
-    const float gate = HC[r * 2 * F + n], up = HC[r * 2 * F + F + n];
+    const int64_t hr = hc_rows != nullptr ? (int64_t)hc_rows[r] : r;
+    const float gate = HC[hr * 2 * F + n], up = HC[hr * 2 * F + F + n];
     const float s = 1.0f / (1.0f + expf(-gate));
     out[r * 2 * F + n] = acc * up * (s * (1.0f + gate * (1.0f - s)));
     out[r * 2 * F + F + n] = acc * (gate * s);
@@ -736,7 +741,8 @@ size_t gemm_ws_bytes(const lrmoe_problem* p, const int64_t* row_off_h) {
 
 lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_off_h,
                                      const int64_t* row_off_d, const void* Dlt, const void* PhiC,
-                                     const void* XC, const void* HC, const void* W2, const void* W1,
+                                     const void* XC, const void* HC, const int32_t* hc_rows, const void* W2,
+                                     const void* W1,
                                      float* dW2, float* dW1, void* dH, void* dIn, int accumulate,
                                      void* ws, hipStream_t s) {
   const int E = p->E, D = p->D, F = p->F;
@@ -746,10 +752,11 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
     if (p->swiglu) {
       if (rows > 0) {
         f32_dgrad_kernel<EPI_SWIGLU><<<dim3((unsigned)rows, (unsigned)ceil_div(F, NTHR)), NTHR, 0, s>>>(
-            dl, D, (const float*)W2, D, (int64_t)F * D, F, D, row_off_d, E, (const float*)HC, (float*)dH, 2 * F, F);
+            dl, D, (const float*)W2, D, (int64_t)F * D, F, D, row_off_d, E, (const float*)HC, hc_rows, (float*)dH,
+            2 * F, F);
         f32_dgrad_kernel<EPI_STORE><<<dim3((unsigned)rows, (unsigned)ceil_div(D, NTHR)), NTHR, 0, s>>>(
             (const float*)dH, 2 * F, (const float*)W1, 2 * F, (int64_t)D * 2 * F, D, 2 * F, row_off_d, E, nullptr,
-            (float*)dIn, D, F);
+            nullptr, (float*)dIn, D, F);
       }
       if (E > 0) {
         f32_wgrad_kernel<<<dim3((unsigned)ceil_div(D, NTHR), F, E), NTHR, 0, s>>>(
@@ -760,7 +767,7 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
     } else {
       if (rows > 0)
         f32_dgrad_kernel<EPI_STORE><<<dim3((unsigned)rows, (unsigned)ceil_div(F, NTHR)), NTHR, 0, s>>>(
-            dl, D, (const float*)W2, D, (int64_t)F * D, F, D, row_off_d, E, nullptr, (float*)dIn, F, F);
+            dl, D, (const float*)W2, D, (int64_t)F * D, F, D, row_off_d, E, nullptr, nullptr, (float*)dIn, F, F);
       if (E > 0)
         f32_wgrad_kernel<<<dim3((unsigned)ceil_div(D, NTHR), F, E), NTHR, 0, s>>>(
             (const float*)PhiC, F, dl, D, F, D, row_off_d, dW2, accumulate);
@@ -785,6 +792,7 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
   d2.F = F;
   if (p->swiglu) {
     d2.HC = (const uint16_t*)HC;
+    d2.hc_rows = hc_rows;
     d2.out = (uint16_t*)dH;
     d2.ldo = 2 * F;
     if (mtiles > 0) dgrad_kernel<EPI_SWIGLU><<<(unsigned)(mtiles * d2.ntn), NTHR, 0, s>>>(d2);
@@ -798,6 +806,7 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
     d1.K = 2 * F;
     d1.ntn = (int)ceil_div(D, BN);
     d1.HC = nullptr;
+    d1.hc_rows = nullptr;
     d1.out = (uint16_t*)dIn;
     d1.ldo = D;
     if (mtiles > 0) dgrad_kernel<EPI_STORE><<<(unsigned)(mtiles * d1.ntn), NTHR, 0, s>>>(d1);

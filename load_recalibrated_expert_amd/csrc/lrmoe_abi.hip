@@ -120,7 +120,7 @@ lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, cons
     if (K_tot == 0) return LRMOE_OK;
     if (!sel || !G || !Phi || !alpha || !tok || !slot || !Dlt || !PhiC || !ctok || !cslot)
       return LRMOE_ERR_INVALID_ARG;
-    if (sw && (!X || !H || !XC || !HC)) return LRMOE_ERR_INVALID_ARG;
+    if (sw && (!X || !XC || (HC && !H))) return LRMOE_ERR_INVALID_ARG;
     if (!sw && (X || H || XC || HC)) return LRMOE_ERR_INVALID_ARG;
     if (!ws || ws_bytes < compact_ws_bytes(p)) return LRMOE_ERR_WORKSPACE;
     return launch_compact(p, K_tot, false, sel, nullptr, G, Phi, X, H, alpha, tok, slot, Dlt, PhiC, XC, HC,
@@ -140,8 +140,9 @@ lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, cons
 
 lrmoe_status lrmoe_grouped_gemm_bwd(const lrmoe_problem* p, lrmoe_compact_mode mode, const int64_t* row_off_d,
                                     const void* Dlt, const void* PhiC, const void* XC, const void* HC,
-                                    const void* W2, const void* W1, float* dW2, float* dW1, void* dH, void* dIn,
-                                    int32_t accumulate, void* ws, size_t ws_bytes, lrmoe_stream_t stream) {
+                                    const int32_t* hc_rows, const void* W2, const void* W1, float* dW2, float* dW1,
+                                    void* dH, void* dIn, int32_t accumulate, void* ws, size_t ws_bytes,
+                                    lrmoe_stream_t stream) {
   std::vector<int64_t> cseg;
   LRMOE_TRY(check_problem(p, nullptr, &cseg));
   if (mode != LRMOE_COMPACT_PHYSICAL && mode != LRMOE_COMPACT_ZERO_MASKED) return LRMOE_ERR_INVALID_ARG;
@@ -152,12 +153,12 @@ lrmoe_status lrmoe_grouped_gemm_bwd(const lrmoe_problem* p, lrmoe_compact_mode m
   if (rows > 0 && (!Dlt || !PhiC || !dIn)) return LRMOE_ERR_INVALID_ARG;
   if (p->swiglu) {
     if (!W1 || !dW1 || (rows > 0 && (!XC || !HC || !dH))) return LRMOE_ERR_INVALID_ARG;
-  } else if (W1 || dW1 || dH || XC || HC) {
+  } else if (W1 || dW1 || dH || XC || HC || hc_rows) {
     return LRMOE_ERR_INVALID_ARG;
   }
   if (ws_bytes < gemm_ws_bytes(p, row_off_h) || (!ws && gemm_ws_bytes(p, row_off_h) > 0))
     return LRMOE_ERR_WORKSPACE;
-  return launch_grouped_gemm_bwd(p, row_off_h, row_off_d, Dlt, PhiC, XC, HC, W2, W1, dW2, dW1, dH, dIn,
+  return launch_grouped_gemm_bwd(p, row_off_h, row_off_d, Dlt, PhiC, XC, HC, hc_rows, W2, W1, dW2, dW1, dH, dIn,
                                  accumulate, ws, (hipStream_t)stream);
 }
 

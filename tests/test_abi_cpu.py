@@ -111,7 +111,7 @@ def test_workspace_size_and_host_side_rejections():
                                          None, fake, fake]
     assert lib.lrmoe_compact(ctypes.byref(p), _lib.COMPACT_PHYSICAL, *sw, None, 0, None) == _lib.ERR_WORKSPACE
     q, keep2 = _problem(quota=(6, 0, 7))
-    assert lib.lrmoe_grouped_gemm_bwd(ctypes.byref(q), 0, *([fake] * 11), 0, fake, 1 << 30,
+    assert lib.lrmoe_grouped_gemm_bwd(ctypes.byref(q), 0, *([fake] * 12), 0, fake, 1 << 30,
                                       None) == _lib.ERR_INFEASIBLE_QUOTA
     assert _lib.status_string(_lib.ERR_INFEASIBLE_QUOTA).startswith("infeasible")
 

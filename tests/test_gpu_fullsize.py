@@ -84,7 +84,7 @@ def test_full_compact_sampled_rows(full):
                        X=pr.X, H=pr.H)
     assert np.array_equal(bits(res["Dlt"][rows_t]), oracle.round_bf16(c["Dlt"]))
     assert np.array_equal(bits(res["PhiC"][rows_t]), pr.Phi[sel[rows]])
-    assert np.array_equal(bits(res["HC"][rows_t]), pr.H[sel[rows]])
+    assert "HC" not in res  # the path reads H in place through sel
     assert np.array_equal(bits(res["XC"][rows_t]), pr.X[pr.routing.tok[sel[rows]]])
     assert np.array_equal(res["ctok"][rows_t].cpu().numpy(), c["ctok"])
     assert np.array_equal(res["cslot"][rows_t].cpu().numpy(), c["cslot"])

@@ -101,8 +101,12 @@ def test_compact(case):
     sel = ref["sel"]
     assert np.array_equal(bits(res["PhiC"]), pr.Phi[sel])
     if pr.cfg.swiglu:
-        assert np.array_equal(bits(res["HC"]), pr.H[sel])
+        assert "HC" not in res  # the path reads H in place through sel
         assert np.array_equal(bits(res["XC"]), pr.X[pr.routing.tok[sel]])
+        # packing HC on request: bitwise H[sel]
+        c = lr.compact(s.P, s.G, s.Phi, s.alpha, s.tok, s.slot, sel=res["sel"], keep=res["keep"], X=s.X, H=s.H)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(c["HC"]), pr.H[sel])
     if dt == "bf16":
         assert np.array_equal(bits(res["Dlt"]), oracle.round_bf16(ref["Dlt"]))
     else:
@@ -213,11 +217,24 @@ def test_accumulate_adds_to_weight_gradients():
     res = s.backward()
     base2, base1 = res["dW2"].clone(), res["dW1"].clone()
     c = res
-    g = lr.grouped_gemm_bwd(s.P, c["Dlt"], c["PhiC"], s.W2, XC=c["XC"], HC=c["HC"], W1=s.W1,
+    g = lr.grouped_gemm_bwd(s.P, c["Dlt"], c["PhiC"], s.W2, XC=c["XC"], HC=s.H, hc_rows=c["sel"], W1=s.W1,
                             out={"dW2": base2.clone(), "dW1": base1.clone()}, accumulate=True)
     torch.cuda.synchronize()
     assert torch.allclose(g["dW2"], 2 * base2, rtol=1e-6, atol=1e-6)
     assert torch.allclose(g["dW1"], 2 * base1, rtol=1e-6, atol=1e-6)
+
+
+def test_packed_gate_up_rows_match_reading_them_in_place():
+    """The SwiGLU backward reads [gate | up] either from packed HC rows or from H through
+    sel; both give bit-identical gradients."""
+    pr = _make("swiglu_ragged")
+    s = Staged(pr)
+    res = s.backward()
+    c = lr.compact(s.P, s.G, s.Phi, s.alpha, s.tok, s.slot, sel=res["sel"], keep=res["keep"], X=s.X, H=s.H)
+    g = lr.grouped_gemm_bwd(s.P, c["Dlt"], c["PhiC"], s.W2, XC=c["XC"], HC=c["HC"], W1=s.W1)
+    torch.cuda.synchronize()
+    for k in ("dW1", "dW2", "dH", "dIn"):
+        assert torch.equal(g[k], res[k]), k
 
 
 def test_all_equal_scores_break_ties_by_index():

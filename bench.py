@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--rho", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-masked", action="store_true")
+    ap.add_argument("--packed", action="store_true",
+                    help="compaction also packs the saved Phi and X rows (PhiC, XC) and the GEMMs read the "
+                         "packed copies, instead of reading Phi and X in place through sel and ctok")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="before timing, run 3 device-to-device copies of this many MiB (a plain copy kernel "
                          "of known size, used to scale hardware byte counters)")
@@ -50,15 +53,17 @@ def to_dev(np_mod, torch, a, dtype, dev):
     return torch.from_numpy(a).to(dev)
 
 
-def algorithmic_bytes(cfg, N, K_tot):
+def algorithmic_bytes(cfg, N, K_tot, packed=False):
     """Bytes each step reads once and writes once (storage dtype e; f32 scores/outputs)."""
     e = 2 if cfg.dtype == "bf16" else 4
     T, D, F = cfg.T, cfg.D, cfg.F
     score = (T * D + N * F) * e + N * (4 + 4 + 4)            # G, Phi, alpha, tok -> R
-    # compact reads each token's G (and X) row once and each retained pair's Phi row once,
-    # and writes every packed row once (the saved [gate | up] rows are read in place by the
-    # GEMM, not packed)
-    if cfg.swiglu:
+    # compact reads each token's G row once and writes every retained pair's Dlt row once;
+    # packed, it also reads each token's X row and each retained pair's Phi row once and
+    # writes their copies (the saved [gate | up] rows are always read in place by the GEMM)
+    if not packed:
+        compact = T * D * e + K_tot * D * e
+    elif cfg.swiglu:
         compact = (2 * T * D + K_tot * F) * e + K_tot * (2 * D + F) * e
     else:
         compact = (T * D + K_tot * F) * e + K_tot * (D + F) * e
@@ -178,16 +183,23 @@ def main():
         bufs.setdefault("sel", sel)
         bufs.setdefault("keep", keep)
         rec(2)
-        c = lr.compact(P, G, Phi, alpha, tok, slot, sel=sel, keep=keep, X=ins["X"], mode=mode, out=bufs.get("c"))
+        phys = mode == lr.COMPACT_PHYSICAL
+        c = lr.compact(P, G, Phi, alpha, tok, slot, sel=sel, keep=keep, X=ins["X"] if args.packed else None,
+                       mode=mode, out=bufs.get("c"), pack_phi=args.packed)
         bufs.setdefault("c", c)
         rec(3)
-        PhiC = c["PhiC"] if mode == lr.COMPACT_PHYSICAL else Phi
-        hc_rows = sel if (mode == lr.COMPACT_PHYSICAL and cfg.swiglu) else None
-        g = lr.grouped_gemm_bwd(P, c["Dlt"], PhiC, ins["W2"], XC=c.get("XC"), HC=ins["H"], W1=ins["W1"], mode=mode,
-                                out=bufs.get("g"), hc_rows=hc_rows)
+        ctok, cslot = (c["ctok"], c["cslot"]) if phys else (tok, slot)
+        hc_rows = sel if (phys and cfg.swiglu) else None
+        if args.packed:
+            PhiC, XC, phi_rows, x_rows = (c["PhiC"] if phys else Phi), c.get("XC"), None, None
+        else:  # Phi and X read in place: pair rows through sel, token rows through ctok (tok)
+            PhiC, XC = Phi, ins["X"]
+            phi_rows = sel if phys else None
+            x_rows = ctok if cfg.swiglu else None
+        g = lr.grouped_gemm_bwd(P, c["Dlt"], PhiC, ins["W2"], XC=XC, HC=ins["H"], W1=ins["W1"], mode=mode,
+                                out=bufs.get("g"), hc_rows=hc_rows, phi_rows=phi_rows, x_rows=x_rows)
         bufs.setdefault("g", g)
         rec(4)
-        ctok, cslot = (c["ctok"], c["cslot"]) if mode == lr.COMPACT_PHYSICAL else (tok, slot)
         out = lr.scatter(P, g["dIn"], ctok, cslot, n_rows=P.rows(mode), out=bufs.get("out"))
         bufs.setdefault("out", out)
         rec(5)
@@ -216,7 +228,7 @@ def main():
     wall, per = measure(lr.COMPACT_PHYSICAL)
     ms = wall / args.steps * 1e3
     value = P.K_tot * args.steps / wall
-    bytes_ = algorithmic_bytes(cfg, P.N, P.K_tot)
+    bytes_ = algorithmic_bytes(cfg, P.N, P.K_tot, packed=args.packed)
     fl = gemm_flops(cfg, P.K_tot)
     peak = BF16_PEAK_TFLOPS if dt == "bf16" else FP32_PEAK_TFLOPS
     gemm_tf = fl / (per["grouped_gemm_bwd"] * 1e-3) / 1e12

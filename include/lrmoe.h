@@ -124,16 +124,17 @@ lrmoe_status lrmoe_select(const lrmoe_problem* p, const float* R, const int64_t*
  *   PhiC[c] = Phi[j];  XC[c] = X[t];  HC[c] = H[j];  ctok[c] = t;  cslot[c] = slot[j]
  *   Dlt, XC [K_tot x D]; PhiC [K_tot x F]; HC [K_tot x 2F]; ctok, cslot [K_tot] int32.
  *   X, H, XC, HC are used only when swiglu = 1 (else pass NULL). keep is ignored.
- *   HC is optional (NULL: not written, and H may be NULL): the grouped GEMM reads the saved
- *   [gate | up] rows only in its SwiGLU epilogue and can read them in place from H through
- *   sel (its hc_rows argument), which saves the copy.
+ *   PhiC, XC and HC are optional (NULL: not written; Phi, X, H may then be NULL): the
+ *   grouped GEMM can read the saved rows in place through sel and ctok (its row maps),
+ *   which saves the copies.
  *   Each (token, slot) position holds at most one pair (a token routes to an expert through
  *   one slot); the gather runs token by token through a [T x K] position map kept in ws, so
  *   a token's G and X rows are read from HBM once for all of its retained pairs. A packed
  *   row whose pair has tok outside [0,T) or slot outside [0,K) is left untouched.
  * ZERO_MASKED, for every pair j < N: Dlt[j] = keep[j] ? alpha[j] * G[tok[j]] : 0 and
- *   XC[j] = X[tok[j]] (swiglu); sel is ignored; PhiC and HC must be NULL (the GEMMs read
- *   Phi and H in place); ctok/cslot, if not NULL, receive copies of tok/slot. ws may be NULL.
+ *   XC[j] = X[tok[j]] (swiglu; XC optional, the GEMM can read X through tok); sel is
+ *   ignored; PhiC and HC must be NULL (the GEMMs read Phi and H in place); ctok/cslot, if
+ *   not NULL, receive copies of tok/slot. ws may be NULL.
  * ws: scratch of at least lrmoe_workspace_size bytes (PHYSICAL), else LRMOE_ERR_WORKSPACE. */
 lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, const int32_t* sel,
                            const uint8_t* keep, const void* G, const void* Phi, const void* X,
@@ -152,18 +153,26 @@ lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, cons
  *   dW1[e] (+)= XC_e^T dH_e                           f32 [E x D x 2F]
  *   dIn       = dH_e W1[e]^T                          storage dtype [rows x D]
  * with gate = HC[r, :F], up = HC[r, F:] for packed row c, where r = hc_rows[c] (hc_rows
- * [rows] int32) or r = c when hc_rows is NULL. PHYSICAL mode with HC = H and hc_rows = sel
- * reads the saved rows in place; ZERO_MASKED passes HC = H and hc_rows = NULL.
+ * [rows] int32) or r = c when hc_rows is NULL.
+ * Row maps (each [rows] int32 or NULL = identity) let the saved activations be read in
+ * place instead of packed: row c of PhiC is PhiC[phi_rows[c]], of XC is XC[x_rows[c]], of
+ * HC is HC[hc_rows[c]]. A mapped PhiC or HC has N rows (pair rows), a mapped XC has T rows
+ * (token rows); a mapped row outside that range reads as zeros. With a mapped PhiC or XC
+ * the matrix must be under 2 GiB (else LRMOE_ERR_UNSUPPORTED).
+ *   PHYSICAL, in place: PhiC = Phi, phi_rows = sel; XC = X, x_rows = ctok; HC = H,
+ *                       hc_rows = sel (compaction then writes only Dlt, ctok, cslot).
+ *   PHYSICAL, packed:   the compacted PhiC, XC, HC and NULL maps.
+ *   ZERO_MASKED:        PhiC = Phi, HC = H, XC = X with x_rows = tok (or the masked XC).
  * For swiglu = 0 only dW2 and dIn = dPhi [rows x F] are produced (dH, XC, HC, hc_rows,
- * W1, dW1 must be NULL).
+ * x_rows, W1, dW1 must be NULL).
  * accumulate = 0 overwrites dW1/dW2 (experts with no rows get 0); 1 adds to them.
  * bf16: MFMA with fp32 accumulation. f32: fp32 FMA throughout. */
 lrmoe_status lrmoe_grouped_gemm_bwd(const lrmoe_problem* p, lrmoe_compact_mode mode,
                                     const int64_t* row_off_d, const void* Dlt, const void* PhiC,
                                     const void* XC, const void* HC, const int32_t* hc_rows,
-                                    const void* W2, const void* W1, float* dW2, float* dW1, void* dH,
-                                    void* dIn, int32_t accumulate, void* ws, size_t ws_bytes,
-                                    lrmoe_stream_t stream);
+                                    const int32_t* phi_rows, const int32_t* x_rows, const void* W2,
+                                    const void* W1, float* dW2, float* dW1, void* dH, void* dIn,
+                                    int32_t accumulate, void* ws, size_t ws_bytes, lrmoe_stream_t stream);
 
 /* Step 5 - inverse mapping (section 3.1; Algorithm 1's ScatterWithZeros).
  * rows [n_rows x width] of dtype rows_dtype; row c belongs to pair (ctok[c], cslot[c]),

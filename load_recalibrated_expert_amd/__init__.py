@@ -114,19 +114,22 @@ def select(p: Problem, R, sel=None, keep=None, want_keep=True, stream=None):
 
 
 def compact(p: Problem, G, Phi, alpha, tok, slot, sel=None, keep=None, X=None, H=None,
-            mode=COMPACT_PHYSICAL, out=None, stream=None):
-    """Physical mode packs HC only when H is given; without it the grouped GEMM reads H in
-    place through sel."""
+            mode=COMPACT_PHYSICAL, out=None, pack_phi=True, stream=None):
+    """Always writes Dlt (and ctok/cslot). The saved rows are packed only on request:
+    PhiC when ``pack_phi`` (physical mode), XC when X is given, HC when H is given
+    (physical mode). The grouped GEMM can read each of them in place instead, through
+    its row maps (sel for Phi and H, ctok or tok for X)."""
     rows = p.rows(mode)
     dt = p.torch_dtype
     o = dict(out or {})
     dev = p.device
     o.setdefault("Dlt", torch.empty(max(rows, 1), p.D, dtype=dt, device=dev))
     if mode == COMPACT_PHYSICAL:
-        o.setdefault("PhiC", torch.empty(max(rows, 1), p.F, dtype=dt, device=dev))
+        if pack_phi:
+            o.setdefault("PhiC", torch.empty(max(rows, 1), p.F, dtype=dt, device=dev))
         if p.swiglu and H is not None:
             o.setdefault("HC", torch.empty(max(rows, 1), 2 * p.F, dtype=dt, device=dev))
-    if p.swiglu:
+    if p.swiglu and X is not None:
         o.setdefault("XC", torch.empty(max(rows, 1), p.D, dtype=dt, device=dev))
     o.setdefault("ctok", torch.empty(max(rows, 1), dtype=torch.int32, device=dev))
     o.setdefault("cslot", torch.empty(max(rows, 1), dtype=torch.int32, device=dev))
@@ -139,9 +142,11 @@ def compact(p: Problem, G, Phi, alpha, tok, slot, sel=None, keep=None, X=None, H
 
 
 def grouped_gemm_bwd(p: Problem, Dlt, PhiC, W2, XC=None, HC=None, W1=None, mode=COMPACT_PHYSICAL,
-                     out=None, accumulate=False, hc_rows=None, stream=None):
-    """``HC`` holds the saved [gate | up] rows the SwiGLU backward reads: packed rows, or the
-    pair rows ``H`` themselves with ``hc_rows`` (e.g. ``sel``) mapping packed row -> row."""
+                     out=None, accumulate=False, hc_rows=None, phi_rows=None, x_rows=None, stream=None):
+    """``PhiC``, ``XC`` and ``HC`` are packed rows, or the saved matrices themselves (Phi,
+    X, H) with a row map giving, for each packed row, the row to read: ``phi_rows`` and
+    ``hc_rows`` index pair rows (e.g. ``sel``), ``x_rows`` token rows (``ctok``, or ``tok``
+    in zero-masked mode)."""
     rows = p.rows(mode)
     dt = p.torch_dtype
     dev = p.device
@@ -156,7 +161,7 @@ def grouped_gemm_bwd(p: Problem, Dlt, PhiC, W2, XC=None, HC=None, W1=None, mode=
     ws = p.workspace()
     _lib.check(library().lrmoe_grouped_gemm_bwd(
         ctypes.byref(p.c), mode, _ptr(p.row_off_d(mode)), _ptr(Dlt), _ptr(PhiC), _ptr(XC), _ptr(HC), _ptr(hc_rows),
-        _ptr(W2),
+        _ptr(phi_rows), _ptr(x_rows), _ptr(W2),
         _ptr(W1), _ptr(o["dW2"]), _ptr(o.get("dW1")), _ptr(o.get("dH")), _ptr(o["dIn"]), int(bool(accumulate)),
         _ptr(ws), ws.numel(), _stream(stream)), "lrmoe_grouped_gemm_bwd")
     res = dict(o)
@@ -191,19 +196,23 @@ def backward(p: Problem, *, G, Phi, alpha, tok, slot, W2, X=None, H=None, W1=Non
     sel, keep = select(p, b["R"], sel=b.get("sel_full"), keep=b.get("keep_full"), stream=stream)
     b.setdefault("sel_full", sel)
     b.setdefault("keep_full", keep)
-    # the saved [gate | up] rows are not packed: the GEMM reads H in place through sel
-    c = compact(p, G, Phi, alpha, tok, slot, sel=sel, keep=keep, X=X, mode=mode, out=b.get("compact"),
-                stream=stream)
+    # only the new gradient rows are packed: the GEMMs read the saved Phi, X and H rows in
+    # place through sel and the packed rows' tokens
+    c = compact(p, G, Phi, alpha, tok, slot, sel=sel, keep=keep, mode=mode, out=b.get("compact"),
+                pack_phi=False, stream=stream)
     b.setdefault("compact", c)
-    PhiC = c["PhiC"] if mode == COMPACT_PHYSICAL else Phi
-    hc_rows = sel if (mode == COMPACT_PHYSICAL and p.swiglu) else None
-    g = grouped_gemm_bwd(p, c["Dlt"], PhiC, W2, XC=c.get("XC"), HC=H, W1=W1, mode=mode, out=b.get("gemm"),
-                         hc_rows=hc_rows, stream=stream)
-    b.setdefault("gemm", g)
     if mode == COMPACT_PHYSICAL:
         ctok, cslot = c["ctok"], c["cslot"]
+        phi_rows = sel
+        hc_rows = sel if p.swiglu else None
+        x_rows = ctok if p.swiglu else None
     else:
         ctok, cslot = tok, slot
+        phi_rows = hc_rows = None
+        x_rows = tok if p.swiglu else None
+    g = grouped_gemm_bwd(p, c["Dlt"], Phi, W2, XC=X, HC=H, W1=W1, mode=mode, out=b.get("gemm"),
+                         hc_rows=hc_rows, phi_rows=phi_rows, x_rows=x_rows, stream=stream)
+    b.setdefault("gemm", g)
     out = scatter(p, g["dIn"], ctok, cslot, n_rows=p.rows(mode), mode=scatter_mode, out=b.get("out"),
                   stream=stream)
     b.setdefault("out", out)

@@ -102,7 +102,8 @@ size_t compact_ws_bytes(const lrmoe_problem* p);
 size_t gemm_ws_bytes(const lrmoe_problem* p, const int64_t* row_off_h);
 lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_off_h,
                                      const int64_t* row_off_d, const void* Dlt, const void* PhiC,
-                                     const void* XC, const void* HC, const int32_t* hc_rows, const void* W2,
+                                     const void* XC, const void* HC, const int32_t* hc_rows,
+                                     const int32_t* phi_rows, const int32_t* x_rows, const void* W2,
                                      const void* W1,
                                      float* dW2, float* dW1, void* dH, void* dIn, int accumulate,
                                      void* ws, hipStream_t s);

@@ -3,8 +3,9 @@
 // contiguous expert segments so the grouped GEMMs see only retained rows, with no
 // padding. Row c of every packed buffer belongs to the retained pair j = sel[c]:
 //   Dlt[c] = alpha_j * g_{tok_j} (the weighted cotangent, appendix 7.1 Eq. 5; alpha is
-//   applied here exactly once), PhiC[c] = Phi[j], XC[c] = X[tok_j], and on request HC[c] = H[j]
-//   (the grouped GEMM can instead read H in place through sel).
+//   applied here exactly once), and on request PhiC[c] = Phi[j], XC[c] = X[tok_j],
+//   HC[c] = H[j] (the grouped GEMM can instead read Phi, X and H in place through sel and
+//   ctok, so only the new gradient rows are written).
 // The zero-masked baseline of section 3.4 keeps all N rows and zeroes the dropped pairs'
 // gradient rows instead.
 //
@@ -61,8 +62,8 @@ __device__ __forceinline__ void copy_row(uint4* __restrict__ dst, const uint4* _
   }
 }
 
-// Writes packed row c of pair j (token t): Dlt, and unless MASKED PhiC (and HC if given);
-// XC when gated.
+// Writes packed row c of pair j (token t): Dlt, and those of PhiC, XC (gated), HC (gated)
+// that are given (never PhiC or HC when MASKED).
 template <bool BF16, bool SWIGLU, bool MASKED>
 __device__ __forceinline__ void gather_row(int64_t c, int64_t j, int t, bool tok_ok, bool kept, float a, int dch,
                                            int fch, int lane, const uint4* __restrict__ G,
@@ -88,10 +89,10 @@ __device__ __forceinline__ void gather_row(int64_t c, int64_t j, int t, bool tok
     }
   }
   if (!MASKED) {
-    copy_row<true>(PhiC + c * fch, Phi + j * fch, fch, lane);
+    if (PhiC != nullptr) copy_row<true>(PhiC + c * fch, Phi + j * fch, fch, lane);
     if (SWIGLU && HC != nullptr) copy_row<true>(HC + c * 2 * fch, H + j * 2 * fch, 2 * fch, lane);
   }
-  if (SWIGLU) {
+  if (SWIGLU && XC != nullptr) {
     if (tok_ok) copy_row<false>(XC + c * dch, X + (int64_t)t * dch, dch, lane);
   }
 }
@@ -185,21 +186,23 @@ __global__ __launch_bounds__(kThreads) void compact_token_reg_kernel(
   };
   int k = next_slot(0);
   if (k >= K) return;
+  const bool with_phi = PhiC != nullptr, with_xc = SWIGLU && XC != nullptr, with_hc = SWIGLU && HC != nullptr;
   uint4 g[DL], x[SWIGLU ? DL : 1];
 #pragma unroll
   for (int u = 0; u < DL; ++u) {
     const int cc = lane + u * kWave;
     g[u] = cc < dch ? G[(int64_t)t * dch + cc] : make_uint4(0, 0, 0, 0);
-    if (SWIGLU) x[u] = cc < dch ? X[(int64_t)t * dch + cc] : make_uint4(0, 0, 0, 0);
+    if (with_xc) x[u] = cc < dch ? X[(int64_t)t * dch + cc] : make_uint4(0, 0, 0, 0);
   }
   int32_t c = __builtin_amdgcn_readfirstlane(map[(int64_t)t * K + k]);
   int64_t j = __builtin_amdgcn_readfirstlane(sel[c]);
-  const bool with_hc = SWIGLU && HC != nullptr;
   uint4 ph[FL], hh[HL];
+  if (with_phi) {
 #pragma unroll
-  for (int u = 0; u < FL; ++u) {
-    const int cc = lane + u * kWave;
-    ph[u] = cc < fch ? ld_stream(Phi + j * fch + cc) : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < FL; ++u) {
+      const int cc = lane + u * kWave;
+      ph[u] = cc < fch ? ld_stream(Phi + j * fch + cc) : make_uint4(0, 0, 0, 0);
+    }
   }
   if (with_hc) {
 #pragma unroll
@@ -217,10 +220,12 @@ __global__ __launch_bounds__(kThreads) void compact_token_reg_kernel(
     if (kn < K) {  // uniform
       cn = __builtin_amdgcn_readfirstlane(map[(int64_t)t * K + kn]);
       jn = __builtin_amdgcn_readfirstlane(sel[cn]);
+      if (with_phi) {
 #pragma unroll
-      for (int u = 0; u < FL; ++u) {
-        const int cc = lane + u * kWave;
-        phn[u] = cc < fch ? ld_stream(Phi + jn * fch + cc) : make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < FL; ++u) {
+          const int cc = lane + u * kWave;
+          phn[u] = cc < fch ? ld_stream(Phi + jn * fch + cc) : make_uint4(0, 0, 0, 0);
+        }
       }
       if (with_hc) {
 #pragma unroll
@@ -235,13 +240,15 @@ __global__ __launch_bounds__(kThreads) void compact_token_reg_kernel(
       const int cc = lane + u * kWave;
       if (cc < dch) {
         Dlt[(int64_t)c * dch + cc] = BF16 ? scale_bf16x8(a, g[u]) : scale_f32x4(a, g[u]);
-        if (SWIGLU) XC[(int64_t)c * dch + cc] = x[u];
+        if (with_xc) XC[(int64_t)c * dch + cc] = x[u];
       }
     }
+    if (with_phi) {
 #pragma unroll
-    for (int u = 0; u < FL; ++u) {
-      const int cc = lane + u * kWave;
-      if (cc < fch) PhiC[(int64_t)c * fch + cc] = ph[u];
+      for (int u = 0; u < FL; ++u) {
+        const int cc = lane + u * kWave;
+        if (cc < fch) PhiC[(int64_t)c * fch + cc] = ph[u];
+      }
     }
     if (with_hc) {
 #pragma unroll
@@ -258,8 +265,10 @@ __global__ __launch_bounds__(kThreads) void compact_token_reg_kernel(
     k = kn;
     c = cn;
     j = jn;
+    if (with_phi) {
 #pragma unroll
-    for (int u = 0; u < FL; ++u) ph[u] = phn[u];
+      for (int u = 0; u < FL; ++u) ph[u] = phn[u];
+    }
     if (with_hc) {
 #pragma unroll
       for (int u = 0; u < HL; ++u) hh[u] = hhn[u];

@@ -81,6 +81,11 @@ __device__ __forceinline__ void dma16(rsrc_t r, const uint4* lds_wave_base, uint
 // 512 bytes per row as eight 64-byte segments; segment s of row k sits in slot s ^ (k & 3),
 // so the 4-row transpose reads of one half-wavefront cover all 64 banks.
 
+struct StageBufs {
+  uint4 a[STAGES][kTileU4];
+  uint4 b[STAGES][kTileU4];
+};
+
 // uint4 index of chunk c of row r in a K-contiguous stage
 __device__ __forceinline__ int nt_slot(int r, int c) { return (r & 127) * 8 + ((((r >> 7) << 2) | c) ^ (r & 7)); }
 
@@ -109,6 +114,9 @@ struct DmaK {
     const bool kok = k0 + col < kend;
     dma16(r, stage + wbase + j * 64, (kok && off[j] != kOOB) ? off[j] + (uint32_t)k0 * 2u : kOOB);
   }
+  __device__ __forceinline__ void start() {}
+  __device__ __forceinline__ void fetch(int) {}
+  __device__ __forceinline__ void advance(int) {}
 };
 
 // Direct-to-LDS loader of a row-major-in-K operand. A 1 KB direct load fills 2 K rows;
@@ -134,6 +142,80 @@ struct DmaT {
   }
   __device__ __forceinline__ void issue_one(int j, const uint4* stage, int k0, int kend, uint32_t kstep) const {
     dma16(r, stage + wbase + j * 64, (off[j] != kOOB && k0 + row[j] < kend) ? off[j] + (uint32_t)k0 * kstep : kOOB);
+  }
+  __device__ __forceinline__ void start() {}
+  __device__ __forceinline__ void fetch(int) {}
+  __device__ __forceinline__ void advance(int) {}
+};
+
+typedef __attribute__((address_space(4))) const int32_t const_i32_t;
+
+// The same operand with gathered K rows: K row k of the item is row idx[k] of the matrix
+// (saved activations read in place instead of packed). A lane's 16-byte chunk sits at
+// row * pitch + its column offset, so the buffer resource spans the whole matrix (under
+// 2 GiB; the host checks). Rows outside [0, nrows) read as zeros. A wavefront needs 4 row
+// indices per stage, rows 4w + 2j + h for its loads j = 0, 1 and halves h = 0, 1. It reads
+// them with scalar loads (the index array is constant during the kernel), issued at the top
+// of the loop iteration whose end turns them into the load offsets of a later stage: scalar
+// loads count towards the LDS counter, and the wait for them falls together with the wait
+// for the iteration's own LDS reads. Vector loads of the indices into registers instead,
+// interleaved with the direct loads into LDS, cost several percent. Reads are clamped to
+// [0, klen) so they never leave the item's part of the index array.
+struct DmaTG {
+  rsrc_t r;                        // the matrix
+  const_i32_t* idx;                // the item's row indices
+  uint32_t coff[DMA_PER_WAVE];     // column offset in bytes, or kOOB past the tile's columns
+  int row[DMA_PER_WAVE];           // K row within a stage
+  int wbase, w, h;
+  uint32_t pitch, nrows;
+  int klen;
+  int32_t e[4];                    // indices of rows 4w .. 4w+3 of the stage being prepared
+  uint32_t off[DMA_PER_WAVE];      // byte offsets of the stage to issue next (kOOB: zeros)
+  static_assert(DMA_PER_WAVE == 2, "index layout assumes two direct loads per wavefront");
+  __device__ __forceinline__ void init(const uint16_t* p, int64_t ld, int mn_valid, const int32_t* idx_, int klen_,
+                                       int64_t nrows_) {
+    r = make_rsrc(p);
+    idx = (const_i32_t*)idx_;
+    klen = klen_;
+    nrows = (uint32_t)nrows_;
+    pitch = (uint32_t)(ld * 2);
+    const int lane = threadIdx.x & 63;
+    w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    h = lane >> 5;
+    wbase = w * DMA_PER_WAVE * 64;
+#pragma unroll
+    for (int j = 0; j < DMA_PER_WAVE; ++j) {
+      const int k = (w * DMA_PER_WAVE + j) * 2 + h;
+      const int pc = lane & 31;
+      const int c = (((pc >> 2) ^ (k & 3)) << 2) | (pc & 3);
+      row[j] = k;
+      coff[j] = c * 8 < mn_valid ? (uint32_t)(c * 8 * 2) : kOOB;
+      off[j] = kOOB;
+    }
+  }
+  __device__ __forceinline__ void load_indices(int s) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e[i] = idx[min(s * BK + 4 * w + i, klen - 1)];
+  }
+  __device__ __forceinline__ void start() {
+    load_indices(0);
+    advance(0);
+  }
+  // at the top of loop iteration kt, whose end prepares stage kt + STAGES
+  __device__ __forceinline__ void fetch(int kt) { load_indices(kt + STAGES); }
+  // stage s's load offsets from its indices (loaded by load_indices(s)), computed ahead (at
+  // the end of the previous loop iteration, where the wavefront waits anyway) so that issuing
+  // the loads costs no arithmetic
+  __device__ __forceinline__ void advance(int s) {
+    const int32_t mrow[DMA_PER_WAVE] = {h ? e[1] : e[0], h ? e[3] : e[2]};
+#pragma unroll
+    for (int j = 0; j < DMA_PER_WAVE; ++j) {
+      const bool ok = s * BK + row[j] < klen && (uint32_t)mrow[j] < nrows && coff[j] != kOOB;
+      off[j] = ok ? (uint32_t)mrow[j] * pitch + coff[j] : kOOB;
+    }
+  }
+  __device__ __forceinline__ void issue_one(int j, const uint4* stage, int, int, uint32_t) const {
+    dma16(r, stage + wbase + j * 64, off[j]);
   }
 };
 
@@ -186,11 +268,6 @@ __device__ __forceinline__ void zero_acc(f32x16_t (&acc)[NB][MB]) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 }
 
-struct StageBufs {
-  uint4 a[STAGES][kTileU4];
-  uint4 b[STAGES][kTileU4];
-};
-
 __device__ __forceinline__ void mfma(f32x16_t& acc, const bf16x8_t& n_frag, const bf16x8_t& m_frag) {
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(n_frag, m_frag, acc, 0, 0, 0);
 }
@@ -204,19 +281,28 @@ __device__ __forceinline__ void mfma(f32x16_t& acc, const bf16x8_t& n_frag, cons
 // direct loads of stage kt+3 and the fragments of the second step; during the second step
 // the fragments of stage kt+1's first step, so MFMAs start right after the next barrier.
 template <bool TN, class LA, class LB>
-__device__ __forceinline__ void gemm_mainloop(StageBufs& sm, const LA& la, const LB& lb, int kend, uint32_t kstep_a,
+__device__ __forceinline__ void gemm_mainloop(StageBufs& sm, LA& la, LB& lb, int kend, uint32_t kstep_a,
                                               uint32_t kstep_b, f32x16_t (&acc)[NB][MB], int wm, int wn, int lane) {
   constexpr int NM = NB * MB;
   const int nk = (kend + BK - 1) / BK;
   if (nk <= 0) return;
+  la.start();
+  lb.start();
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
+  for (int s = 0; s < STAGES - 1; ++s) {
 #pragma unroll
     for (int j = 0; j < DMA_PER_WAVE; ++j) {
       la.issue_one(j, sm.a[s], s * BK, kend, kstep_a);
       lb.issue_one(j, sm.b[s], s * BK, kend, kstep_b);
     }
-  // stage 0 landed: the loads of stages 1..STAGES-2 may still be in flight
+    la.fetch(s + 1 - STAGES);  // the indices of stage s + 1
+    lb.fetch(s + 1 - STAGES);
+    la.advance(s + 1);
+    lb.advance(s + 1);
+  }
+  // stage 0 landed: the loads of stages 1..STAGES-2 may still be in flight (row-index loads
+  // come before some stage's data loads in program order, so they only make these waits
+  // stricter)
   constexpr int kPro = (STAGES - 2) * 2 * DMA_PER_WAVE, kLoop = (STAGES - 3) * 2 * DMA_PER_WAVE;
   static_assert(kPro < 64, "vmcnt field");
   __builtin_amdgcn_s_waitcnt(0x0F70 | (kPro & 0xF) | ((kPro >> 4) << 14));
@@ -232,6 +318,8 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs& sm, const LA& la, const
     // stage kt+1 landed: the loads of stages kt+2..kt+STAGES-2 may still be in flight
     __builtin_amdgcn_s_waitcnt(0x0F70 | (kLoop & 0xF) | ((kLoop >> 4) << 14));
     __syncthreads();
+    la.fetch(kt);
+    lb.fetch(kt);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       mfma(acc[i / MB][i % MB], fb[0][i / MB], fa[0][i % MB]);
@@ -250,6 +338,8 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs& sm, const LA& la, const
       else if (i < MB + NB) fb[0][i - MB] = load_frag<TN>(sm.b[nxt], wn * 32 * NB + (i - MB) * 32, 0, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
+    la.advance(kt + STAGES);
+    lb.advance(kt + STAGES);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the loop
 }
@@ -315,6 +405,7 @@ struct DgradArgs {
   // epilogue
   const uint16_t* HC;  // SwiGLU: saved [gate | up] rows, 2F wide
   const int32_t* hc_rows;  // row of HC for packed row c (nullptr: row c)
+  int64_t hc_nrows;        // rows of HC: a mapped row outside [0, hc_nrows) reads as zeros
   uint16_t* out;       // SwiGLU: dH [rows x 2F]; STORE: [rows x N]
   int64_t ldo;
   int F;
@@ -358,8 +449,9 @@ __global__ __launch_bounds__(NTHR) void dgrad_kernel(DgradArgs g) {
         const int64_t rowb = (row0 + tr) * ld + n0 + tc;
         const int64_t hrow = g.hc_rows != nullptr ? (int64_t)g.hc_rows[row0 + tr] : row0 + tr;
         const int64_t hb = hrow * ld + n0 + tc;
-        const uint4 gw = *(const uint4*)(hc + hb);
-        const uint4 uw = *(const uint4*)(hc + hb + F);
+        const bool hok = hrow >= 0 && hrow < g.hc_nrows;
+        const uint4 gw = hok ? *(const uint4*)(hc + hb) : make_uint4(0, 0, 0, 0);
+        const uint4 uw = hok ? *(const uint4*)(hc + hb + F) : make_uint4(0, 0, 0, 0);
         const uint32_t gg[4] = {gw.x, gw.y, gw.z, gw.w}, uu[4] = {uw.x, uw.y, uw.z, uw.w};
         float dg[8], du[8];
 #pragma unroll
@@ -385,8 +477,10 @@ __global__ __launch_bounds__(NTHR) void dgrad_kernel(DgradArgs g) {
 // ---------------------------------------------------------------- weight-gradient kernels
 
 struct WgradType {
-  const uint16_t* A;  // [rows x M] (M contiguous)
+  const uint16_t* A;  // [rows x M] (M contiguous), or the matrix that a_rows gathers from
   int64_t lda;
+  const int32_t* a_rows;  // packed row c is row a_rows[c] of A (nullptr: row c)
+  int64_t a_nrows;        // rows of A when gathered
   const uint16_t* B;  // [rows x N] (N contiguous)
   int64_t ldb;
   float* out;         // [E x M x N]
@@ -462,6 +556,9 @@ __global__ __launch_bounds__(NTHR) void wgrad_plan_kernel(WgradArgs g) {
   }
 }
 
+// G0, G1: the A operand of weight-gradient type 0 (FC2: Phi) / type 1 (FC1: X) is gathered
+// through its row map (a compile-time choice, so neither loader carries the other's code).
+template <bool G0, bool G1>
 __global__ __launch_bounds__(NTHR) void wgrad_kernel(WgradArgs g) {
   __shared__ StageBufs lds;
   // hardware sends block i to XCD i % 8; the grid holds 8 x (largest range) blocks
@@ -492,10 +589,17 @@ __global__ __launch_bounds__(NTHR) void wgrad_kernel(WgradArgs g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN;
   f32x16_t acc[NB][MB];
   zero_acc(acc);
-  DmaT la, lb;
-  la.init(T.A + (r0 + k_begin) * T.lda + m0, T.lda, m_valid);
+  DmaT lb;
   lb.init(T.B + (r0 + k_begin) * T.ldb + n0, T.ldb, n_valid);
-  gemm_mainloop<true>(lds, la, lb, klen, (uint32_t)(T.lda * 2), (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
+  if ((G0 || G1) && (ty == 0 ? G0 : G1)) {
+    DmaTG la;
+    la.init(T.A + m0, T.lda, m_valid, T.a_rows + r0 + k_begin, klen, T.a_nrows);
+    gemm_mainloop<true>(lds, la, lb, klen, 0, (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
+  } else {
+    DmaT la;
+    la.init(T.A + (r0 + k_begin) * T.lda + m0, T.lda, m_valid);
+    gemm_mainloop<true>(lds, la, lb, klen, (uint32_t)(T.lda * 2), (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
+  }
 
   if (s > 1) {
     float* __restrict__ p = g.partials + (g.plan_pbase[e] + (int64_t)chunk * tiles + rem) * (int64_t)(BM * BN);
@@ -610,7 +714,7 @@ __global__ __launch_bounds__(NTHR) void f32_dgrad_kernel(const float* __restrict
                                                          int64_t w_estride, int N, int K,
                                                          const int64_t* __restrict__ row_off, int E,
                                                          const float* __restrict__ HC,
-                                                         const int32_t* __restrict__ hc_rows,
+                                                         const int32_t* __restrict__ hc_rows, int64_t hc_nrows,
                                                          float* __restrict__ out, int64_t ldo, int F) {
   const int64_t r = blockIdx.x;
   const int n = blockIdx.y * NTHR + threadIdx.x;
@@ -622,7 +726,8 @@ __global__ __launch_bounds__(NTHR) void f32_dgrad_kernel(const float* __restrict
   for (int k = 0; k < K; ++k) acc = fmaf(a[k], w[k], acc);
   if (EPI == EPI_SWIGLU) {
     const int64_t hr = hc_rows != nullptr ? (int64_t)hc_rows[r] : r;
-    const float gate = HC[hr * 2 * F + n], up = HC[hr * 2 * F + F + n];
+    const bool ok = hr >= 0 && hr < hc_nrows;  // rows outside HC read as zeros
+    const float gate = ok ? HC[hr * 2 * F + n] : 0.0f, up = ok ? HC[hr * 2 * F + F + n] : 0.0f;
     const float s = 1.0f / (1.0f + expf(-gate));
     out[r * 2 * F + n] = acc * up * (s * (1.0f + gate * (1.0f - s)));
     out[r * 2 * F + F + n] = acc * (gate * s);
@@ -631,8 +736,10 @@ __global__ __launch_bounds__(NTHR) void f32_dgrad_kernel(const float* __restrict
   }
 }
 
-// out[e][i][j] (+)= sum over rows r of expert e of A[r][i] * B[r][j]
+// out[e][i][j] (+)= sum over rows r of expert e of A[ar(r)][i] * B[r][j], with ar(r) =
+// a_rows[r] (rows outside [0, a_nrows) read as zeros) or r when a_rows is nullptr
 __global__ __launch_bounds__(NTHR) void f32_wgrad_kernel(const float* __restrict__ A, int64_t lda,
+                                                         const int32_t* __restrict__ a_rows, int64_t a_nrows,
                                                          const float* __restrict__ B, int64_t ldb, int M, int N,
                                                          const int64_t* __restrict__ row_off,
                                                          float* __restrict__ out, int accumulate) {
@@ -640,7 +747,11 @@ __global__ __launch_bounds__(NTHR) void f32_wgrad_kernel(const float* __restrict
   const int j = blockIdx.x * NTHR + threadIdx.x;
   if (j >= N) return;
   float acc = 0.0f;
-  for (int64_t r = row_off[e]; r < row_off[e + 1]; ++r) acc = fmaf(A[r * lda + i], B[r * ldb + j], acc);
+  for (int64_t r = row_off[e]; r < row_off[e + 1]; ++r) {
+    const int64_t ar = a_rows != nullptr ? (int64_t)a_rows[r] : r;
+    const float a = (a_rows == nullptr || (ar >= 0 && ar < a_nrows)) ? A[ar * lda + i] : 0.0f;
+    acc = fmaf(a, B[r * ldb + j], acc);
+  }
   float* q = out + ((int64_t)e * M + i) * N + j;
   *q = accumulate ? *q + acc : acc;
 }
@@ -741,36 +852,40 @@ size_t gemm_ws_bytes(const lrmoe_problem* p, const int64_t* row_off_h) {
 
 lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_off_h,
                                      const int64_t* row_off_d, const void* Dlt, const void* PhiC,
-                                     const void* XC, const void* HC, const int32_t* hc_rows, const void* W2,
+                                     const void* XC, const void* HC, const int32_t* hc_rows,
+                                     const int32_t* phi_rows, const int32_t* x_rows, const void* W2,
                                      const void* W1,
                                      float* dW2, float* dW1, void* dH, void* dIn, int accumulate,
                                      void* ws, hipStream_t s) {
   const int E = p->E, D = p->D, F = p->F;
   const int64_t rows = row_off_h[E];
+  // rows of the (possibly gathered) saved matrices: pair rows or token rows when mapped
+  const int64_t hc_nrows = hc_rows ? p->N : rows, phi_nrows = phi_rows ? p->N : rows;
+  const int64_t x_nrows = x_rows ? (int64_t)p->T : rows;
   if (p->dtype == LRMOE_F32) {
     const float* dl = (const float*)Dlt;
     if (p->swiglu) {
       if (rows > 0) {
         f32_dgrad_kernel<EPI_SWIGLU><<<dim3((unsigned)rows, (unsigned)ceil_div(F, NTHR)), NTHR, 0, s>>>(
-            dl, D, (const float*)W2, D, (int64_t)F * D, F, D, row_off_d, E, (const float*)HC, hc_rows, (float*)dH,
-            2 * F, F);
+            dl, D, (const float*)W2, D, (int64_t)F * D, F, D, row_off_d, E, (const float*)HC, hc_rows, hc_nrows,
+            (float*)dH, 2 * F, F);
         f32_dgrad_kernel<EPI_STORE><<<dim3((unsigned)rows, (unsigned)ceil_div(D, NTHR)), NTHR, 0, s>>>(
             (const float*)dH, 2 * F, (const float*)W1, 2 * F, (int64_t)D * 2 * F, D, 2 * F, row_off_d, E, nullptr,
-            nullptr, (float*)dIn, D, F);
+            nullptr, 0, (float*)dIn, D, F);
       }
       if (E > 0) {
         f32_wgrad_kernel<<<dim3((unsigned)ceil_div(D, NTHR), F, E), NTHR, 0, s>>>(
-            (const float*)PhiC, F, dl, D, F, D, row_off_d, dW2, accumulate);
+            (const float*)PhiC, F, phi_rows, phi_nrows, dl, D, F, D, row_off_d, dW2, accumulate);
         f32_wgrad_kernel<<<dim3((unsigned)ceil_div(2 * F, NTHR), D, E), NTHR, 0, s>>>(
-            (const float*)XC, D, (const float*)dH, 2 * F, D, 2 * F, row_off_d, dW1, accumulate);
+            (const float*)XC, D, x_rows, x_nrows, (const float*)dH, 2 * F, D, 2 * F, row_off_d, dW1, accumulate);
       }
     } else {
       if (rows > 0)
         f32_dgrad_kernel<EPI_STORE><<<dim3((unsigned)rows, (unsigned)ceil_div(F, NTHR)), NTHR, 0, s>>>(
-            dl, D, (const float*)W2, D, (int64_t)F * D, F, D, row_off_d, E, nullptr, nullptr, (float*)dIn, F, F);
+            dl, D, (const float*)W2, D, (int64_t)F * D, F, D, row_off_d, E, nullptr, nullptr, 0, (float*)dIn, F, F);
       if (E > 0)
         f32_wgrad_kernel<<<dim3((unsigned)ceil_div(D, NTHR), F, E), NTHR, 0, s>>>(
-            (const float*)PhiC, F, dl, D, F, D, row_off_d, dW2, accumulate);
+            (const float*)PhiC, F, phi_rows, phi_nrows, dl, D, F, D, row_off_d, dW2, accumulate);
     }
     return launch_status();
   }
@@ -793,6 +908,7 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
   if (p->swiglu) {
     d2.HC = (const uint16_t*)HC;
     d2.hc_rows = hc_rows;
+    d2.hc_nrows = hc_nrows;
     d2.out = (uint16_t*)dH;
     d2.ldo = 2 * F;
     if (mtiles > 0) dgrad_kernel<EPI_SWIGLU><<<(unsigned)(mtiles * d2.ntn), NTHR, 0, s>>>(d2);
@@ -818,11 +934,11 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
 
   const WgradLayout L = wgrad_layout(p, row_off_h);
   WgradArgs w{};
-  w.t[0] = WgradType{(const uint16_t*)PhiC, F, (const uint16_t*)Dlt, D, dW2, F, D,
+  w.t[0] = WgradType{(const uint16_t*)PhiC, F, phi_rows, phi_nrows, (const uint16_t*)Dlt, D, dW2, F, D,
                      (int)ceil_div(F, BM), (int)ceil_div(D, BN), wgrad_tiles(F, D)};
   w.ntypes = 1;
   if (p->swiglu) {
-    w.t[1] = WgradType{(const uint16_t*)XC, D, (const uint16_t*)dH, 2 * F, dW1, D, 2 * F,
+    w.t[1] = WgradType{(const uint16_t*)XC, D, x_rows, x_nrows, (const uint16_t*)dH, 2 * F, dW1, D, 2 * F,
                        (int)ceil_div(D, BM), (int)ceil_div(2 * F, BN), wgrad_tiles(D, 2 * F)};
     w.ntypes = 2;
   }
@@ -839,7 +955,14 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
   if (E > 0) {
     const int64_t per_xcd = wgrad_xcd_ranges(p, row_off_h, w.xlo);
     wgrad_plan_kernel<<<1, NTHR, 0, s>>>(w);
-    if (per_xcd > 0) wgrad_kernel<<<(unsigned)(8 * per_xcd), NTHR, 0, s>>>(w);
+    const unsigned grid = (unsigned)(8 * per_xcd);
+    const bool g0 = phi_rows != nullptr, g1 = x_rows != nullptr;
+    if (per_xcd > 0) {
+      if (g0 && g1) wgrad_kernel<true, true><<<grid, NTHR, 0, s>>>(w);
+      else if (g0) wgrad_kernel<true, false><<<grid, NTHR, 0, s>>>(w);
+      else if (g1) wgrad_kernel<false, true><<<grid, NTHR, 0, s>>>(w);
+      else wgrad_kernel<false, false><<<grid, NTHR, 0, s>>>(w);
+    }
     if (L.nreduce > 0) wgrad_reduce_kernel<<<(unsigned)(L.nreduce * kRedParts), NTHR, 0, s>>>(w);
   }
   return launch_status();

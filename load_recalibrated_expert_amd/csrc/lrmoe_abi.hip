@@ -118,9 +118,9 @@ lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, cons
   const bool sw = p->swiglu != 0;
   if (mode == LRMOE_COMPACT_PHYSICAL) {
     if (K_tot == 0) return LRMOE_OK;
-    if (!sel || !G || !Phi || !alpha || !tok || !slot || !Dlt || !PhiC || !ctok || !cslot)
+    if (!sel || !G || !alpha || !tok || !slot || !Dlt || !ctok || !cslot || (PhiC && !Phi))
       return LRMOE_ERR_INVALID_ARG;
-    if (sw && (!X || !XC || (HC && !H))) return LRMOE_ERR_INVALID_ARG;
+    if (sw && ((XC && !X) || (HC && !H))) return LRMOE_ERR_INVALID_ARG;
     if (!sw && (X || H || XC || HC)) return LRMOE_ERR_INVALID_ARG;
     if (!ws || ws_bytes < compact_ws_bytes(p)) return LRMOE_ERR_WORKSPACE;
     return launch_compact(p, K_tot, false, sel, nullptr, G, Phi, X, H, alpha, tok, slot, Dlt, PhiC, XC, HC,
@@ -130,7 +130,7 @@ lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, cons
     if (p->N == 0) return LRMOE_OK;
     if (!keep || !G || !alpha || !tok || !Dlt || PhiC || HC) return LRMOE_ERR_INVALID_ARG;
     if ((ctok || cslot) && !slot) return LRMOE_ERR_INVALID_ARG;
-    if (sw && (!X || !XC)) return LRMOE_ERR_INVALID_ARG;
+    if (sw && XC && !X) return LRMOE_ERR_INVALID_ARG;
     if (!sw && (X || XC)) return LRMOE_ERR_INVALID_ARG;
     return launch_compact(p, p->N, true, nullptr, keep, G, Phi, X, H, alpha, tok, slot, Dlt, nullptr, XC,
                           nullptr, ctok, cslot, nullptr, (hipStream_t)stream);
@@ -140,9 +140,9 @@ lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, cons
 
 lrmoe_status lrmoe_grouped_gemm_bwd(const lrmoe_problem* p, lrmoe_compact_mode mode, const int64_t* row_off_d,
                                     const void* Dlt, const void* PhiC, const void* XC, const void* HC,
-                                    const int32_t* hc_rows, const void* W2, const void* W1, float* dW2, float* dW1,
-                                    void* dH, void* dIn, int32_t accumulate, void* ws, size_t ws_bytes,
-                                    lrmoe_stream_t stream) {
+                                    const int32_t* hc_rows, const int32_t* phi_rows, const int32_t* x_rows,
+                                    const void* W2, const void* W1, float* dW2, float* dW1, void* dH, void* dIn,
+                                    int32_t accumulate, void* ws, size_t ws_bytes, lrmoe_stream_t stream) {
   std::vector<int64_t> cseg;
   LRMOE_TRY(check_problem(p, nullptr, &cseg));
   if (mode != LRMOE_COMPACT_PHYSICAL && mode != LRMOE_COMPACT_ZERO_MASKED) return LRMOE_ERR_INVALID_ARG;
@@ -153,13 +153,17 @@ lrmoe_status lrmoe_grouped_gemm_bwd(const lrmoe_problem* p, lrmoe_compact_mode m
   if (rows > 0 && (!Dlt || !PhiC || !dIn)) return LRMOE_ERR_INVALID_ARG;
   if (p->swiglu) {
     if (!W1 || !dW1 || (rows > 0 && (!XC || !HC || !dH))) return LRMOE_ERR_INVALID_ARG;
-  } else if (W1 || dW1 || dH || XC || HC || hc_rows) {
+  } else if (W1 || dW1 || dH || XC || HC || hc_rows || x_rows) {
     return LRMOE_ERR_INVALID_ARG;
   }
+  // the gathering loads address a gathered matrix with 32-bit byte offsets
+  const int64_t esz = p->dtype == LRMOE_BF16 ? 2 : 4, kLim = (int64_t)1 << 31;
+  if ((phi_rows && p->N * p->F * esz >= kLim) || (x_rows && (int64_t)p->T * p->D * esz >= kLim))
+    return LRMOE_ERR_UNSUPPORTED;
   if (ws_bytes < gemm_ws_bytes(p, row_off_h) || (!ws && gemm_ws_bytes(p, row_off_h) > 0))
     return LRMOE_ERR_WORKSPACE;
-  return launch_grouped_gemm_bwd(p, row_off_h, row_off_d, Dlt, PhiC, XC, HC, hc_rows, W2, W1, dW2, dW1, dH, dIn,
-                                 accumulate, ws, (hipStream_t)stream);
+  return launch_grouped_gemm_bwd(p, row_off_h, row_off_d, Dlt, PhiC, XC, HC, hc_rows, phi_rows, x_rows, W2, W1,
+                                 dW2, dW1, dH, dIn, accumulate, ws, (hipStream_t)stream);
 }
 
 lrmoe_status lrmoe_scatter(const lrmoe_problem* p, lrmoe_scatter_mode mode, int64_t n_rows, int32_t width,

@@ -111,9 +111,43 @@ def test_workspace_size_and_host_side_rejections():
                                          None, fake, fake]
     assert lib.lrmoe_compact(ctypes.byref(p), _lib.COMPACT_PHYSICAL, *sw, None, 0, None) == _lib.ERR_WORKSPACE
     q, keep2 = _problem(quota=(6, 0, 7))
-    assert lib.lrmoe_grouped_gemm_bwd(ctypes.byref(q), 0, *([fake] * 12), 0, fake, 1 << 30,
+    assert lib.lrmoe_grouped_gemm_bwd(ctypes.byref(q), 0, *([fake] * 14), 0, fake, 1 << 30,
                                       None) == _lib.ERR_INFEASIBLE_QUOTA
     assert _lib.status_string(_lib.ERR_INFEASIBLE_QUOTA).startswith("infeasible")
+    # packing PhiC needs Phi; packing XC needs X
+    args = [fake, None, fake, None, None, None, fake, fake, fake, fake, fake, None, None, fake, fake]
+    assert lib.lrmoe_compact(ctypes.byref(p), _lib.COMPACT_PHYSICAL, *args, fake, 1 << 30,
+                             None) == _lib.ERR_INVALID_ARG
+    args = [fake, None, fake, fake, None, None, fake, fake, fake, fake, None, fake, None, fake, fake]
+    assert lib.lrmoe_compact(ctypes.byref(p), _lib.COMPACT_PHYSICAL, *args, fake, 1 << 30,
+                             None) == _lib.ERR_INVALID_ARG
+
+
+def _gemm(p, phi_rows=None, x_rows=None, swiglu=True):
+    """lrmoe_grouped_gemm_bwd with fake device pointers (only host checks can pass)."""
+    fake = ctypes.c_void_p(0x1000)
+    w1 = fake if swiglu else None
+    return _lib.load().lrmoe_grouped_gemm_bwd(
+        ctypes.byref(p), _lib.COMPACT_PHYSICAL, fake, fake, fake, w1, w1, w1, phi_rows, x_rows, fake, w1, fake, w1,
+        w1, fake, 0, None, 0, None)
+
+
+def test_row_maps_limited_to_2gib_matrices():
+    """Gathered weight-gradient operands are addressed with 32-bit byte offsets: a mapped
+    Phi (N x F) or X (T x D) of 2 GiB or more is refused on the host."""
+    fake = ctypes.c_void_p(0x1000)
+    # N * F * 2 bytes = 2^20 * 1024 * 2 = 2 GiB
+    p, keep = _problem(E=1, T=1 << 20, K=1, D=64, F=1024, counts=(1 << 20,), quota=(3,))
+    assert _gemm(p, phi_rows=fake) == _lib.ERR_UNSUPPORTED
+    # T * D * 2 bytes = 2^24 * 64 * 2 = 2 GiB
+    p, keep = _problem(E=1, T=1 << 24, K=1, D=64, F=32, counts=(8,), quota=(3,))
+    assert _gemm(p, x_rows=fake) == _lib.ERR_UNSUPPORTED
+    # just under: the checks move on (to the missing workspace)
+    p, keep = _problem(E=1, T=(1 << 24) - 1, K=1, D=64, F=32, counts=(8,), quota=(3,))
+    assert _gemm(p, x_rows=fake) == _lib.ERR_WORKSPACE
+    # an X row map without SwiGLU is an argument error
+    p, keep = _problem(swiglu=0)
+    assert _gemm(p, x_rows=fake, swiglu=False) == _lib.ERR_INVALID_ARG
 
 
 def test_product_path_does_not_touch_the_oracle():

@@ -83,9 +83,8 @@ def test_full_compact_sampled_rows(full):
     c = oracle.compact(sel[rows], pr.routing.tok, pr.routing.slot, pr.routing.alpha, pr.G, pr.Phi, "bf16",
                        X=pr.X, H=pr.H)
     assert np.array_equal(bits(res["Dlt"][rows_t]), oracle.round_bf16(c["Dlt"]))
-    assert np.array_equal(bits(res["PhiC"][rows_t]), pr.Phi[sel[rows]])
-    assert "HC" not in res  # the path reads H in place through sel
-    assert np.array_equal(bits(res["XC"][rows_t]), pr.X[pr.routing.tok[sel[rows]]])
+    # the path packs only the gradient rows: the GEMMs read Phi, X and H in place
+    assert "PhiC" not in res and "XC" not in res and "HC" not in res
     assert np.array_equal(res["ctok"][rows_t].cpu().numpy(), c["ctok"])
     assert np.array_equal(res["cslot"][rows_t].cpu().numpy(), c["cslot"])
 

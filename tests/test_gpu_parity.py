@@ -99,13 +99,16 @@ def test_compact(case):
     assert np.array_equal(res["ctok"].cpu().numpy(), ref["ctok"])
     assert np.array_equal(res["cslot"].cpu().numpy(), ref["cslot"])
     sel = ref["sel"]
-    assert np.array_equal(bits(res["PhiC"]), pr.Phi[sel])
+    # the path packs only the gradient rows: the GEMMs read Phi, X and H in place
+    assert "PhiC" not in res and "XC" not in res and "HC" not in res
+    # packing the saved rows on request: bitwise Phi[sel], X[tok[sel]], H[sel]
+    c = lr.compact(s.P, s.G, s.Phi, s.alpha, s.tok, s.slot, sel=res["sel"], keep=res["keep"],
+                   X=s.X if pr.cfg.swiglu else None, H=s.H if pr.cfg.swiglu else None)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(c["PhiC"]), pr.Phi[sel])
+    assert torch.equal(c["Dlt"], res["Dlt"])
     if pr.cfg.swiglu:
-        assert "HC" not in res  # the path reads H in place through sel
-        assert np.array_equal(bits(res["XC"]), pr.X[pr.routing.tok[sel]])
-        # packing HC on request: bitwise H[sel]
-        c = lr.compact(s.P, s.G, s.Phi, s.alpha, s.tok, s.slot, sel=res["sel"], keep=res["keep"], X=s.X, H=s.H)
-        torch.cuda.synchronize()
+        assert np.array_equal(bits(c["XC"]), pr.X[pr.routing.tok[sel]])
         assert np.array_equal(bits(c["HC"]), pr.H[sel])
     if dt == "bf16":
         assert np.array_equal(bits(res["Dlt"]), oracle.round_bf16(ref["Dlt"]))
@@ -217,24 +220,80 @@ def test_accumulate_adds_to_weight_gradients():
     res = s.backward()
     base2, base1 = res["dW2"].clone(), res["dW1"].clone()
     c = res
-    g = lr.grouped_gemm_bwd(s.P, c["Dlt"], c["PhiC"], s.W2, XC=c["XC"], HC=s.H, hc_rows=c["sel"], W1=s.W1,
-                            out={"dW2": base2.clone(), "dW1": base1.clone()}, accumulate=True)
+    g = lr.grouped_gemm_bwd(s.P, c["Dlt"], s.Phi, s.W2, XC=s.X, HC=s.H, hc_rows=c["sel"], phi_rows=c["sel"],
+                            x_rows=c["ctok"], W1=s.W1, out={"dW2": base2.clone(), "dW1": base1.clone()},
+                            accumulate=True)
     torch.cuda.synchronize()
     assert torch.allclose(g["dW2"], 2 * base2, rtol=1e-6, atol=1e-6)
     assert torch.allclose(g["dW1"], 2 * base1, rtol=1e-6, atol=1e-6)
 
 
-def test_packed_gate_up_rows_match_reading_them_in_place():
-    """The SwiGLU backward reads [gate | up] either from packed HC rows or from H through
-    sel; both give bit-identical gradients."""
-    pr = _make("swiglu_ragged")
+@pytest.mark.parametrize("name", ["swiglu_ragged", "swiglu_split_k", "swiglu_f32", "linear_bf16"])
+def test_packed_rows_match_reading_them_in_place(name):
+    """The GEMMs read Phi, X and [gate | up] either from packed rows or in place through
+    sel / ctok, in any mix; every combination gives bit-identical gradients (the same
+    products in the same order, only the loads differ)."""
+    pr = _make(name)
+    s = Staged(pr)
+    res = s.backward()
+    sw = pr.cfg.swiglu
+    c = lr.compact(s.P, s.G, s.Phi, s.alpha, s.tok, s.slot, sel=res["sel"], keep=res["keep"],
+                   X=s.X if sw else None, H=s.H if sw else None)
+    sel, ctok = res["sel"], res["ctok"]
+    keys = ("dW1", "dW2", "dH", "dIn") if sw else ("dW2", "dIn")
+    for phi_packed in (True, False):
+        for x_packed in ((True, False) if sw else (None,)):
+            for h_packed in ((True, False) if sw else (None,)):
+                kw = dict(PhiC=c["PhiC"] if phi_packed else s.Phi, phi_rows=None if phi_packed else sel)
+                if sw:
+                    kw.update(XC=c["XC"] if x_packed else s.X, x_rows=None if x_packed else ctok,
+                              HC=c["HC"] if h_packed else s.H, hc_rows=None if h_packed else sel, W1=s.W1)
+                g = lr.grouped_gemm_bwd(s.P, c["Dlt"], W2=s.W2, **kw)
+                torch.cuda.synchronize()
+                for k in keys:
+                    assert torch.equal(g[k], res[k]), (k, phi_packed, x_packed, h_packed)
+
+
+@pytest.mark.parametrize("name", ["swiglu_ragged", "swiglu_f32"])
+def test_zero_masked_packed_x_matches_reading_x_through_tok(name):
+    pr = _make(name)
+    s = Staged(pr)
+    m = s.backward(mode=lr.COMPACT_ZERO_MASKED)
+    c = lr.compact(s.P, s.G, s.Phi, s.alpha, s.tok, s.slot, keep=m["keep"], X=s.X, mode=lr.COMPACT_ZERO_MASKED)
+    g = lr.grouped_gemm_bwd(s.P, c["Dlt"], s.Phi, s.W2, XC=c["XC"], HC=s.H, W1=s.W1, mode=lr.COMPACT_ZERO_MASKED)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(c["XC"]), pr.X[pr.routing.tok])
+    for k in ("dW1", "dW2", "dH", "dIn"):
+        assert torch.equal(g[k], m[k]), k
+
+
+@pytest.mark.parametrize("name", ["swiglu_ragged", "swiglu_f32"])
+def test_row_maps_out_of_range_read_zeros(name):
+    """A mapped row outside the matrix reads as zeros: same gradients, bit for bit, as
+    packed rows that are zero there."""
+    pr = _make(name)
     s = Staged(pr)
     res = s.backward()
     c = lr.compact(s.P, s.G, s.Phi, s.alpha, s.tok, s.slot, sel=res["sel"], keep=res["keep"], X=s.X, H=s.H)
-    g = lr.grouped_gemm_bwd(s.P, c["Dlt"], c["PhiC"], s.W2, XC=c["XC"], HC=c["HC"], W1=s.W1)
+    torch.cuda.synchronize()
+    K_tot = s.P.K_tot
+    rng = np.random.default_rng(3)
+    bad = rng.choice(K_tot, size=max(1, K_tot // 10), replace=False)
+    bad_t = torch.from_numpy(bad).to(DEV)
+    sel = res["sel"].clone()
+    ctok = res["ctok"].clone()
+    sel[bad_t] = torch.from_numpy(np.where(bad % 2 == 0, -1, s.P.N + 7).astype(np.int32)).to(DEV)
+    ctok[bad_t] = torch.from_numpy(np.where(bad % 2 == 0, pr.cfg.T, -5).astype(np.int32)).to(DEV)
+    PhiC, XC, HC = c["PhiC"].clone(), c["XC"].clone(), c["HC"].clone()
+    PhiC[bad_t] = 0
+    XC[bad_t] = 0
+    HC[bad_t] = 0
+    want = lr.grouped_gemm_bwd(s.P, c["Dlt"], PhiC, s.W2, XC=XC, HC=HC, W1=s.W1)
+    got = lr.grouped_gemm_bwd(s.P, c["Dlt"], s.Phi, s.W2, XC=s.X, HC=s.H, W1=s.W1, phi_rows=sel, x_rows=ctok,
+                              hc_rows=sel)
     torch.cuda.synchronize()
     for k in ("dW1", "dW2", "dH", "dIn"):
-        assert torch.equal(g[k], res[k]), k
+        assert torch.equal(got[k], want[k]), k
 
 
 def test_all_equal_scores_break_ties_by_index():

@@ -276,6 +276,48 @@ __global__ __launch_bounds__(kThreads) void compact_token_reg_kernel(
   }
 }
 
+// Gradient rows only (the saved rows are read in place by the GEMMs), one wavefront per
+// token, for K <= 64 slots and rows of at most DL x 64 16-byte chunks. All of the token's
+// bookkeeping loads run lane-parallel (lane k: the packed row of slot k, its pair, alpha and
+// slot), three dependent round trips in all, while its G row loads into registers; then every
+// retained slot's row is written from the registers.
+template <bool BF16, int DL>
+__global__ __launch_bounds__(kThreads) void compact_dlt_kernel(int T, int K, int dch, const int32_t* __restrict__ map,
+                                                               const int32_t* __restrict__ sel,
+                                                               const uint4* __restrict__ G,
+                                                               const float* __restrict__ alpha,
+                                                               const int32_t* __restrict__ slot,
+                                                               uint4* __restrict__ Dlt, int32_t* __restrict__ ctok,
+                                                               int32_t* __restrict__ cslot) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (t >= T) return;  // whole wavefront
+  uint4 g[DL];
+#pragma unroll
+  for (int u = 0; u < DL; ++u) {
+    const int cc = lane + u * kWave;
+    g[u] = cc < dch ? G[(int64_t)t * dch + cc] : make_uint4(0, 0, 0, 0);
+  }
+  const int32_t c = lane < K ? map[(int64_t)t * K + lane] : -1;
+  const int64_t j = c >= 0 ? (int64_t)sel[c] : -1;
+  const float a = j >= 0 ? alpha[j] : 0.0f;
+  if (c >= 0) {
+    ctok[c] = t;
+    cslot[c] = slot[j];
+  }
+  for (int k = 0; k < K; ++k) {
+    const int32_t ck = __builtin_amdgcn_readlane(c, k);
+    if (ck < 0) continue;  // uniform
+    const float ak = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), k));
+    uint4* dst = Dlt + (int64_t)ck * dch;
+#pragma unroll
+    for (int u = 0; u < DL; ++u) {
+      const int cc = lane + u * kWave;
+      if (cc < dch) dst[cc] = BF16 ? scale_bf16x8(ak, g[u]) : scale_f32x4(ak, g[u]);
+    }
+  }
+}
+
 template <bool BF16, bool SWIGLU>
 void launch(int64_t rows, bool masked, const lrmoe_problem* p, const int32_t* sel, const uint8_t* keep,
             const void* G, const void* Phi, const void* X, const void* H, const float* alpha, const int32_t* tok,
@@ -294,7 +336,14 @@ void launch(int64_t rows, bool masked, const lrmoe_problem* p, const int32_t* se
   position_map_kernel<<<(unsigned)ceil_div(rows, kThreads), kThreads, 0, s>>>(rows, p->N, p->T, p->K, sel, tok, slot,
                                                                               map);
   const unsigned grid = (unsigned)ceil_div(p->T, kRowsPerBlock);
-  if (dch <= 4 * kWave && fch <= 2 * kWave)
+  const bool dlt_only = PhiC == nullptr && XC == nullptr && HC == nullptr;
+  if (dlt_only && p->K <= kWave && dch <= 4 * kWave)
+    compact_dlt_kernel<BF16, 4><<<grid, kThreads, 0, s>>>(p->T, p->K, dch, map, sel, (const uint4*)G, alpha, slot,
+                                                           (uint4*)Dlt, ctok, cslot);
+  else if (dlt_only && p->K <= kWave && dch <= 8 * kWave)
+    compact_dlt_kernel<BF16, 8><<<grid, kThreads, 0, s>>>(p->T, p->K, dch, map, sel, (const uint4*)G, alpha, slot,
+                                                           (uint4*)Dlt, ctok, cslot);
+  else if (dch <= 4 * kWave && fch <= 2 * kWave)
     compact_token_reg_kernel<BF16, SWIGLU, 4, 2><<<grid, kThreads, 0, s>>>(
         p->T, p->K, dch, fch, map, sel, (const uint4*)G, (const uint4*)Phi, (const uint4*)X, (const uint4*)H, alpha,
         slot, (uint4*)Dlt, (uint4*)PhiC, (uint4*)XC, (uint4*)HC, ctok, cslot);

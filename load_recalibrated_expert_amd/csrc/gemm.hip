@@ -411,6 +411,120 @@ struct DgradArgs {
   int F;
 };
 
+// SwiGLU backward epilogue of the FC2 data gradient: the tile's dPhi (the accumulators) gives
+// dH = [dPhi * up * silu'(gate), dPhi * silu(gate)] with gate, up read from the saved rows.
+// Staged through LDS in two halves like epilogue_staged. A thread handles 8 rows per half:
+// it loads their 8 row indices together, then their [gate | up] chunks in batches (all 8 in
+// the second half; 4 and 4 in the first, where the other half's accumulators still occupy
+// registers), and stores a batch's dH only after computing all of it, so a half costs two
+// or three memory round trips instead of three per row. Loads always read a valid address
+// (row 0 for a row outside the tile or outside HC) and invalid rows are zeroed at use, so
+// the compiler neither branches around the loads nor waits between them.
+template <int B>
+struct HcBatch {
+  uint4 gw[B], uw[B];
+  uint32_t okm;
+};
+
+__device__ __forceinline__ void epilogue_swiglu(StageBufs& sm, const f32x16_t (&acc)[NB][MB], int wm, int wn,
+                                                int lane, const DgradArgs& g, int64_t row0, int rows_valid, int n0,
+                                                int n_valid) {
+  constexpr int kIt = (BM / WM) * (BN / 8) / NTHR;  // rows per thread per half (8)
+  constexpr int kRowStep = NTHR / (BN / 8);          // 16
+  const int tr0 = threadIdx.x / (BN / 8), tc = (threadIdx.x % (BN / 8)) * 8;
+  const int64_t ld = 2 * (int64_t)g.F;
+  const int F = g.F;
+  const bool col_ok = tc < n_valid;
+  const uint16_t* __restrict__ hc = g.HC;
+  uint16_t* __restrict__ dh = g.out;
+  float4* st = reinterpret_cast<float4*>(&sm);
+  auto issue = [&](auto& bt, const int64_t (&hrow)[kIt], int half, int i0) {
+    constexpr int NBt = sizeof(bt.gw) / sizeof(uint4);
+    bt.okm = 0;
+#pragma unroll
+    for (int b = 0; b < NBt; ++b) {
+      const int i = i0 + b;
+      const int tr = half * (BM / WM) + tr0 + kRowStep * i;
+      const bool ok = tr < rows_valid && col_ok && hrow[i] >= 0 && hrow[i] < g.hc_nrows;
+      bt.okm |= ok ? 1u << b : 0u;
+      const int64_t hb = ok ? hrow[i] * ld + n0 + tc : 0;
+      bt.gw[b] = *(const uint4*)(hc + hb);
+      bt.uw[b] = *(const uint4*)(hc + hb + F);
+    }
+  };
+  auto finish = [&](auto& bt, int half, int i0) {
+    constexpr int NBt = sizeof(bt.gw) / sizeof(uint4);
+#pragma unroll
+    for (int b = 0; b < NBt; ++b) {
+      const int r = tr0 + kRowStep * (i0 + b), c8 = tc / 8;
+      const float4 lo = st[r * 64 + ((2 * c8) ^ (r & 15))];
+      const float4 hi = st[r * 64 + ((2 * c8 + 1) ^ (r & 15))];
+      const float dphi[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      const bool ok = (bt.okm >> b) & 1u;  // rows outside the tile or HC read as zeros
+      const uint32_t gg[4] = {ok ? bt.gw[b].x : 0u, ok ? bt.gw[b].y : 0u, ok ? bt.gw[b].z : 0u, ok ? bt.gw[b].w : 0u};
+      const uint32_t uu[4] = {ok ? bt.uw[b].x : 0u, ok ? bt.uw[b].y : 0u, ok ? bt.uw[b].z : 0u, ok ? bt.uw[b].w : 0u};
+      float dg[8], du[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float gate = (c & 1) ? bf16_hi(gg[c >> 1]) : bf16_lo(gg[c >> 1]);
+        const float up = (c & 1) ? bf16_hi(uu[c >> 1]) : bf16_lo(uu[c >> 1]);
+        const float sg = 1.0f / (1.0f + expf(-gate));
+        dg[c] = dphi[c] * up * (sg * (1.0f + gate * (1.0f - sg)));
+        du[c] = dphi[c] * (gate * sg);
+      }
+      bt.gw[b] = pack_bf16x8(dg);
+      bt.uw[b] = pack_bf16x8(du);
+    }
+#pragma unroll
+    for (int b = 0; b < NBt; ++b) {
+      const int tr = half * (BM / WM) + tr0 + kRowStep * (i0 + b);
+      if (tr < rows_valid && col_ok) {
+        const int64_t rowb = (row0 + tr) * ld + n0 + tc;
+        *(uint4*)(dh + rowb) = bt.gw[b];
+        *(uint4*)(dh + rowb + F) = bt.uw[b];
+      }
+    }
+  };
+#pragma unroll
+  for (int half = 0; half < WM; ++half) {
+    int64_t hrow[kIt];
+    if (g.hc_rows != nullptr) {
+#pragma unroll
+      for (int i = 0; i < kIt; ++i)
+        hrow[i] = g.hc_rows[row0 + min(half * (BM / WM) + tr0 + kRowStep * i, rows_valid - 1)];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kIt; ++i) hrow[i] = row0 + half * (BM / WM) + tr0 + kRowStep * i;
+    }
+    HcBatch<kIt / 2> b0, b1;
+    HcBatch<kIt> ball;
+    if (half == 0) issue(b0, hrow, half, 0);
+    else issue(ball, hrow, half, 0);
+    __syncthreads();
+    if (wm == half) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = mb * 32 + (lane & 31);
+            const int c = (wn * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5)) >> 2;
+            st[r * 64 + (c ^ (r & 15))] =
+                make_float4(acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
+          }
+    }
+    __syncthreads();
+    if (half == 0) {
+      finish(b0, half, 0);
+      issue(b1, hrow, half, kIt / 2);
+      finish(b1, half, kIt / 2);
+    } else {
+      finish(ball, half, 0);
+    }
+  }
+}
+
 template <int EPI>
 __global__ __launch_bounds__(NTHR) void dgrad_kernel(DgradArgs g) {
   __shared__ StageBufs lds;
@@ -440,32 +554,7 @@ __global__ __launch_bounds__(NTHR) void dgrad_kernel(DgradArgs g) {
   gemm_mainloop<false>(lds, la, lb, g.K, 0, 0, acc, wm, wn, lane);
 
   if (EPI == EPI_SWIGLU) {
-    const int64_t ld = 2 * (int64_t)g.F;
-    const uint16_t* __restrict__ hc = g.HC;
-    uint16_t* __restrict__ dh = g.out;
-    const int F = g.F;
-    epilogue_staged(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&dphi)[8]) {
-      if (tr < rows_valid && tc < n_valid) {
-        const int64_t rowb = (row0 + tr) * ld + n0 + tc;
-        const int64_t hrow = g.hc_rows != nullptr ? (int64_t)g.hc_rows[row0 + tr] : row0 + tr;
-        const int64_t hb = hrow * ld + n0 + tc;
-        const bool hok = hrow >= 0 && hrow < g.hc_nrows;
-        const uint4 gw = hok ? *(const uint4*)(hc + hb) : make_uint4(0, 0, 0, 0);
-        const uint4 uw = hok ? *(const uint4*)(hc + hb + F) : make_uint4(0, 0, 0, 0);
-        const uint32_t gg[4] = {gw.x, gw.y, gw.z, gw.w}, uu[4] = {uw.x, uw.y, uw.z, uw.w};
-        float dg[8], du[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const float gate = (c & 1) ? bf16_hi(gg[c >> 1]) : bf16_lo(gg[c >> 1]);
-          const float up = (c & 1) ? bf16_hi(uu[c >> 1]) : bf16_lo(uu[c >> 1]);
-          const float s = 1.0f / (1.0f + expf(-gate));
-          dg[c] = dphi[c] * up * (s * (1.0f + gate * (1.0f - s)));
-          du[c] = dphi[c] * (gate * s);
-        }
-        *(uint4*)(dh + rowb) = pack_bf16x8(dg);
-        *(uint4*)(dh + rowb + F) = pack_bf16x8(du);
-      }
-    });
+    epilogue_swiglu(lds, acc, wm, wn, lane, g, row0, rows_valid, n0, n_valid);
   } else {
     uint16_t* __restrict__ out = g.out;
     epilogue_staged(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {

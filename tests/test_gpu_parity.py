@@ -51,6 +51,13 @@ SMALL = {
     # rows wider than the token compaction keeps in registers (D = 2304 bf16 elements)
     "wide_rows": dict(cfg=synth.custom("wide_rows", T=150, K=3, E=3, D=2304, F=136, counts=(200, 90, 110),
                                        seed=19), rho="0.7"),
+    # more routing slots than a wavefront has lanes (K = 72): the generic compaction and
+    # scatter paths, tokens meeting one expert in several slots
+    "many_slots": dict(cfg=synth.custom("many_slots", T=20, K=72, E=3, D=256, F=128, counts=(700, 400, 300),
+                                        seed=20), rho="0.6"),
+    # rows wider than any register-held compaction (D = 4160 > 512 16-byte chunks)
+    "widest_rows": dict(cfg=synth.custom("widest_rows", T=60, K=2, E=2, D=4160, F=64, counts=(70, 40),
+                                         seed=21), rho="0.5"),
 }
 
 

@@ -35,6 +35,9 @@ def parse():
     ap.add_argument("--rho", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-masked", action="store_true")
+    ap.add_argument("--overlap", action="store_true",
+                    help="run the scatter on a second stream as soon as the input gradients are complete (under "
+                         "the weight gradients) instead of after the whole grouped GEMM call on the same stream")
     ap.add_argument("--packed", action="store_true",
                     help="compaction also packs the saved Phi and X rows (PhiC, XC) and the GEMMs read the "
                          "packed copies, instead of reading Phi and X in place through sel and ctok")
@@ -170,11 +173,20 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    overlap = args.overlap
+
     def run(mode, bufs, timing=None):
-        """One step; with `timing`, HIP events bracket each step's call on the launch stream."""
+        """One step; with `timing`, HIP events bracket each step's call on the stream it runs on
+        (the scatter's on the second stream when it overlaps the weight gradients)."""
         G, Phi, alpha, tok, slot = ins["G"], ins["Phi"], ins["alpha"], ins["tok"], ins["slot"]
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)] if timing is not None else None
-        rec = (lambda i: ev[i].record()) if ev else (lambda i: None)
+        main = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)] if timing is not None else None
+        rec = (lambda i, s=None: ev[i].record(s if s is not None else main)) if ev else (lambda i, s=None: None)
+        if overlap and "side" not in bufs:
+            bufs["side"] = torch.cuda.Stream(device=dev)
+            bufs["din_ready"] = torch.cuda.Event()
+            bufs["side_ws"] = torch.empty_like(P.workspace())
+            bufs["out"] = torch.empty(P.T, cfg.D if cfg.swiglu else cfg.F, dtype=torch.float32, device=dev)
         rec(0)
         R = lr.score(P, G, Phi, alpha, tok, R=bufs.get("R"))
         bufs["R"] = R
@@ -197,11 +209,21 @@ def main():
             phi_rows = sel if phys else None
             x_rows = ctok if cfg.swiglu else None
         g = lr.grouped_gemm_bwd(P, c["Dlt"], PhiC, ins["W2"], XC=XC, HC=ins["H"], W1=ins["W1"], mode=mode,
-                                out=bufs.get("g"), hc_rows=hc_rows, phi_rows=phi_rows, x_rows=x_rows)
+                                out=bufs.get("g"), hc_rows=hc_rows, phi_rows=phi_rows, x_rows=x_rows,
+                                din_ready=bufs["din_ready"] if overlap else None)
         bufs.setdefault("g", g)
         rec(4)
-        out = lr.scatter(P, g["dIn"], ctok, cslot, n_rows=P.rows(mode), out=bufs.get("out"))
-        bufs.setdefault("out", out)
+        if overlap:  # the scatter runs under the weight gradients, on the second stream
+            side = bufs["side"]
+            side.wait_event(bufs["din_ready"])
+            rec(6, side)
+            lr.scatter(P, g["dIn"], ctok, cslot, n_rows=P.rows(mode), out=bufs["out"], ws=bufs["side_ws"],
+                       stream=side)
+            rec(7, side)
+            main.wait_stream(side)
+        else:
+            out = lr.scatter(P, g["dIn"], ctok, cslot, n_rows=P.rows(mode), out=bufs.get("out"))
+            bufs.setdefault("out", out)
         rec(5)
         if ev:
             timing.append(ev)
@@ -223,6 +245,8 @@ def main():
         torch.cuda.synchronize()
         names = ["score", "select", "compact", "grouped_gemm_bwd", "scatter"]
         per = {n: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in timing])) for i, n in enumerate(names)}
+        if overlap:
+            per["scatter"] = float(np.mean([ev[6].elapsed_time(ev[7]) for ev in timing]))
         return wall, per
 
     wall, per = measure(lr.COMPACT_PHYSICAL)
@@ -248,7 +272,8 @@ def main():
         "vs_baseline": None, "dtype": dt, "data": "synthetic (seeded; pages' shapes, no dataset)",
         "config": {"workload": cfg.name, "T": cfg.T, "top_k": cfg.K, "local_experts": cfg.E, "D": cfg.D,
                    "F": cfg.F, "swiglu": cfg.swiglu, "rho": rho, "pairs": P.N, "retained_pairs": P.K_tot,
-                   "mode": "physical compaction"},
+                   "mode": "physical compaction",
+                   "scatter": "second stream, under the weight gradients" if overlap else "after the GEMM call"},
         "roofline": {"bound": "mfma", "achieved": gemm_tf, "peak": peak, "unit": "TFLOP/s",
                      "frac": gemm_tf / peak, "traffic": recorded_traffic(cfg.name),
                      "kernel": "lrmoe_grouped_gemm_bwd (FC2 dgrad+SwiGLU, FC1 dgrad, FC1+FC2 wgrad launches)",

@@ -49,8 +49,9 @@
 extern "C" {
 #endif
 
-/* Same type as HIP's hipStream_t. */
+/* Same types as HIP's hipStream_t and hipEvent_t. */
 typedef struct ihipStream_t* lrmoe_stream_t;
+typedef struct ihipEvent_t* lrmoe_event_t;
 
 typedef enum lrmoe_status {
   LRMOE_OK = 0,
@@ -166,13 +167,18 @@ lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, cons
  * For swiglu = 0 only dW2 and dIn = dPhi [rows x F] are produced (dH, XC, HC, hc_rows,
  * x_rows, W1, dW1 must be NULL).
  * accumulate = 0 overwrites dW1/dW2 (experts with no rows get 0); 1 adds to them.
+ * din_ready (may be NULL): an event the caller created; it is recorded on `stream` as soon
+ * as dIn is complete, before the weight-gradient launches, so the caller can start the
+ * scatter of dIn on another stream while the weight gradients are computed. A failed
+ * record returns LRMOE_ERR_HIP.
  * bf16: MFMA with fp32 accumulation. f32: fp32 FMA throughout. */
 lrmoe_status lrmoe_grouped_gemm_bwd(const lrmoe_problem* p, lrmoe_compact_mode mode,
                                     const int64_t* row_off_d, const void* Dlt, const void* PhiC,
                                     const void* XC, const void* HC, const int32_t* hc_rows,
                                     const int32_t* phi_rows, const int32_t* x_rows, const void* W2,
                                     const void* W1, float* dW2, float* dW1, void* dH, void* dIn,
-                                    int32_t accumulate, void* ws, size_t ws_bytes, lrmoe_stream_t stream);
+                                    int32_t accumulate, void* ws, size_t ws_bytes, lrmoe_stream_t stream,
+                                    lrmoe_event_t din_ready);
 
 /* Step 5 - inverse mapping (section 3.1; Algorithm 1's ScatterWithZeros).
  * rows [n_rows x width] of dtype rows_dtype; row c belongs to pair (ctok[c], cslot[c]),

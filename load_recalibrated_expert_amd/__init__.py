@@ -43,6 +43,16 @@ def _stream(stream=None):
     return s.cuda_stream
 
 
+def _event(ev, stream=None):
+    """Raw handle of a torch.cuda.Event (None -> NULL). torch creates the HIP event on its
+    first record, so an event never recorded is recorded once here, on `stream`."""
+    if ev is None:
+        return None
+    if not ev.cuda_event:
+        ev.record(stream if stream is not None else torch.cuda.current_stream())
+    return ev.cuda_event
+
+
 class Problem:
     """Shapes, pair segments and quotas of one layer invocation (host + device copies).
 
@@ -142,11 +152,13 @@ def compact(p: Problem, G, Phi, alpha, tok, slot, sel=None, keep=None, X=None, H
 
 
 def grouped_gemm_bwd(p: Problem, Dlt, PhiC, W2, XC=None, HC=None, W1=None, mode=COMPACT_PHYSICAL,
-                     out=None, accumulate=False, hc_rows=None, phi_rows=None, x_rows=None, stream=None):
+                     out=None, accumulate=False, hc_rows=None, phi_rows=None, x_rows=None, din_ready=None,
+                     stream=None):
     """``PhiC``, ``XC`` and ``HC`` are packed rows, or the saved matrices themselves (Phi,
     X, H) with a row map giving, for each packed row, the row to read: ``phi_rows`` and
     ``hc_rows`` index pair rows (e.g. ``sel``), ``x_rows`` token rows (``ctok``, or ``tok``
-    in zero-masked mode)."""
+    in zero-masked mode). ``din_ready`` (a torch.cuda.Event) is recorded on the stream as
+    soon as dIn is complete, before the weight-gradient launches."""
     rows = p.rows(mode)
     dt = p.torch_dtype
     dev = p.device
@@ -163,7 +175,7 @@ def grouped_gemm_bwd(p: Problem, Dlt, PhiC, W2, XC=None, HC=None, W1=None, mode=
         ctypes.byref(p.c), mode, _ptr(p.row_off_d(mode)), _ptr(Dlt), _ptr(PhiC), _ptr(XC), _ptr(HC), _ptr(hc_rows),
         _ptr(phi_rows), _ptr(x_rows), _ptr(W2),
         _ptr(W1), _ptr(o["dW2"]), _ptr(o.get("dW1")), _ptr(o.get("dH")), _ptr(o["dIn"]), int(bool(accumulate)),
-        _ptr(ws), ws.numel(), _stream(stream)), "lrmoe_grouped_gemm_bwd")
+        _ptr(ws), ws.numel(), _stream(stream), _event(din_ready, stream)), "lrmoe_grouped_gemm_bwd")
     res = dict(o)
     res["dIn"] = o["dIn"][:rows]
     if "dH" in o:
@@ -171,14 +183,16 @@ def grouped_gemm_bwd(p: Problem, Dlt, PhiC, W2, XC=None, HC=None, W1=None, mode=
     return res
 
 
-def scatter(p: Problem, rows_t, ctok, cslot, n_rows=None, mode=SCATTER_TOKEN, out=None, stream=None):
+def scatter(p: Problem, rows_t, ctok, cslot, n_rows=None, mode=SCATTER_TOKEN, out=None, ws=None, stream=None):
+    """``ws`` defaults to the problem's workspace; a scatter running concurrently with
+    another call of the same problem (on another stream) needs its own."""
     n_rows = rows_t.shape[0] if n_rows is None else n_rows
     width = rows_t.shape[1]
     rdt = BF16 if rows_t.dtype == torch.bfloat16 else F32
     if out is None:
         nout = p.T if mode == SCATTER_TOKEN else p.T * p.K
         out = torch.empty(max(nout, 1), width, dtype=torch.float32, device=p.device)
-    ws = p.workspace()
+    ws = p.workspace() if ws is None else ws
     _lib.check(library().lrmoe_scatter(ctypes.byref(p.c), mode, n_rows, width, rdt, _ptr(rows_t), _ptr(ctok),
                                        _ptr(cslot), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
                "lrmoe_scatter")
@@ -186,12 +200,18 @@ def scatter(p: Problem, rows_t, ctok, cslot, n_rows=None, mode=SCATTER_TOKEN, ou
 
 
 def backward(p: Problem, *, G, Phi, alpha, tok, slot, W2, X=None, H=None, W1=None, mode=COMPACT_PHYSICAL,
-             scatter_mode=SCATTER_TOKEN, bufs=None, stream=None):
+             scatter_mode=SCATTER_TOKEN, bufs=None, overlap_scatter=False, stream=None):
     """The whole path: score -> select -> compact -> grouped GEMMs -> scatter.
 
     ``bufs`` (a dict, optional) carries preallocated outputs between calls; it is
-    filled on first use. Returns a dict of every intermediate and output."""
+    filled on first use. With ``overlap_scatter`` the scatter runs on a second stream as
+    soon as the input gradients are complete, while the weight gradients are computed
+    (with a workspace of its own); the calling stream waits for it before returning. On
+    one MI355X this gains nothing at the benchmark shapes (the two share the memory system:
+    the scatter doubles in length and the weight gradients slow down as much), so it is
+    off by default. Returns a dict of every intermediate and output."""
     b = bufs if bufs is not None else {}
+    main = stream if stream is not None else torch.cuda.current_stream()
     b["R"] = score(p, G, Phi, alpha, tok, R=b.get("R"), stream=stream)
     sel, keep = select(p, b["R"], sel=b.get("sel_full"), keep=b.get("keep_full"), stream=stream)
     b.setdefault("sel_full", sel)
@@ -210,10 +230,26 @@ def backward(p: Problem, *, G, Phi, alpha, tok, slot, W2, X=None, H=None, W1=Non
         ctok, cslot = tok, slot
         phi_rows = hc_rows = None
         x_rows = tok if p.swiglu else None
+    if overlap_scatter:
+        if "side" not in b:
+            b["side"] = torch.cuda.Stream(device=p.device)
+            b["din_ready"] = torch.cuda.Event()
+            b["side_ws"] = torch.empty_like(p.workspace())
+        if "out" not in b:
+            nout = p.T if scatter_mode == SCATTER_TOKEN else p.T * p.K
+            b["out"] = torch.empty(max(nout, 1), p.D if p.swiglu else p.F, dtype=torch.float32, device=p.device)
     g = grouped_gemm_bwd(p, c["Dlt"], Phi, W2, XC=X, HC=H, W1=W1, mode=mode, out=b.get("gemm"),
-                         hc_rows=hc_rows, phi_rows=phi_rows, x_rows=x_rows, stream=stream)
+                         hc_rows=hc_rows, phi_rows=phi_rows, x_rows=x_rows,
+                         din_ready=b["din_ready"] if overlap_scatter else None, stream=main)
     b.setdefault("gemm", g)
-    out = scatter(p, g["dIn"], ctok, cslot, n_rows=p.rows(mode), mode=scatter_mode, out=b.get("out"),
-                  stream=stream)
+    if overlap_scatter:
+        side = b["side"]
+        side.wait_event(b["din_ready"])
+        out = scatter(p, g["dIn"], ctok, cslot, n_rows=p.rows(mode), mode=scatter_mode, out=b["out"],
+                      ws=b["side_ws"], stream=side)
+        main.wait_stream(side)
+    else:
+        out = scatter(p, g["dIn"], ctok, cslot, n_rows=p.rows(mode), mode=scatter_mode, out=b.get("out"),
+                      stream=main)
     b.setdefault("out", out)
     return {"R": b["R"], "sel": sel, "keep": keep, **c, **g, "out": out}

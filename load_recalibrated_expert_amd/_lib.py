@@ -66,7 +66,7 @@ def load() -> ctypes.CDLL:
         "lrmoe_compact": [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                           ctypes.c_size_t, vp],
         "lrmoe_grouped_gemm_bwd": [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
-                                   sz, vp],
+                                   sz, vp, vp],
         "lrmoe_scatter": [P, ctypes.c_int, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp],
     }
     for name, args in sigs.items():

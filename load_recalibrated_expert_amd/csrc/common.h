@@ -106,7 +106,7 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
                                      const int32_t* phi_rows, const int32_t* x_rows, const void* W2,
                                      const void* W1,
                                      float* dW2, float* dW1, void* dH, void* dIn, int accumulate,
-                                     void* ws, hipStream_t s);
+                                     void* ws, hipStream_t s, hipEvent_t din_ready);
 
 size_t scatter_ws_bytes(const lrmoe_problem* p);
 lrmoe_status launch_scatter(const lrmoe_problem* p, int mode, int64_t n_rows, int width, int rows_dtype,

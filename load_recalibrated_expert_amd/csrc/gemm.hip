@@ -945,8 +945,13 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
                                      const int32_t* phi_rows, const int32_t* x_rows, const void* W2,
                                      const void* W1,
                                      float* dW2, float* dW1, void* dH, void* dIn, int accumulate,
-                                     void* ws, hipStream_t s) {
+                                     void* ws, hipStream_t s, hipEvent_t din_ready) {
   const int E = p->E, D = p->D, F = p->F;
+  // dIn is complete once the data-gradient launches are; the weight gradients follow
+  auto mark_din = [&]() -> lrmoe_status {
+    if (din_ready == nullptr) return LRMOE_OK;
+    return hipEventRecord(din_ready, s) == hipSuccess ? LRMOE_OK : LRMOE_ERR_HIP;
+  };
   const int64_t rows = row_off_h[E];
   // rows of the (possibly gathered) saved matrices: pair rows or token rows when mapped
   const int64_t hc_nrows = hc_rows ? p->N : rows, phi_nrows = phi_rows ? p->N : rows;
@@ -962,6 +967,7 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
             (const float*)dH, 2 * F, (const float*)W1, 2 * F, (int64_t)D * 2 * F, D, 2 * F, row_off_d, E, nullptr,
             nullptr, 0, (float*)dIn, D, F);
       }
+      if (mark_din() != LRMOE_OK) return LRMOE_ERR_HIP;
       if (E > 0) {
         f32_wgrad_kernel<<<dim3((unsigned)ceil_div(D, NTHR), F, E), NTHR, 0, s>>>(
             (const float*)PhiC, F, phi_rows, phi_nrows, dl, D, F, D, row_off_d, dW2, accumulate);
@@ -972,6 +978,7 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
       if (rows > 0)
         f32_dgrad_kernel<EPI_STORE><<<dim3((unsigned)rows, (unsigned)ceil_div(F, NTHR)), NTHR, 0, s>>>(
             dl, D, (const float*)W2, D, (int64_t)F * D, F, D, row_off_d, E, nullptr, nullptr, 0, (float*)dIn, F, F);
+      if (mark_din() != LRMOE_OK) return LRMOE_ERR_HIP;
       if (E > 0)
         f32_wgrad_kernel<<<dim3((unsigned)ceil_div(D, NTHR), F, E), NTHR, 0, s>>>(
             (const float*)PhiC, F, phi_rows, phi_nrows, dl, D, F, D, row_off_d, dW2, accumulate);
@@ -1020,6 +1027,7 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
     d2.ldo = F;
     if (mtiles > 0) dgrad_kernel<EPI_STORE><<<(unsigned)(mtiles * d2.ntn), NTHR, 0, s>>>(d2);
   }
+  if (mark_din() != LRMOE_OK) return LRMOE_ERR_HIP;
 
   const WgradLayout L = wgrad_layout(p, row_off_h);
   WgradArgs w{};

@@ -142,7 +142,8 @@ lrmoe_status lrmoe_grouped_gemm_bwd(const lrmoe_problem* p, lrmoe_compact_mode m
                                     const void* Dlt, const void* PhiC, const void* XC, const void* HC,
                                     const int32_t* hc_rows, const int32_t* phi_rows, const int32_t* x_rows,
                                     const void* W2, const void* W1, float* dW2, float* dW1, void* dH, void* dIn,
-                                    int32_t accumulate, void* ws, size_t ws_bytes, lrmoe_stream_t stream) {
+                                    int32_t accumulate, void* ws, size_t ws_bytes, lrmoe_stream_t stream,
+                                    lrmoe_event_t din_ready) {
   std::vector<int64_t> cseg;
   LRMOE_TRY(check_problem(p, nullptr, &cseg));
   if (mode != LRMOE_COMPACT_PHYSICAL && mode != LRMOE_COMPACT_ZERO_MASKED) return LRMOE_ERR_INVALID_ARG;
@@ -163,7 +164,7 @@ lrmoe_status lrmoe_grouped_gemm_bwd(const lrmoe_problem* p, lrmoe_compact_mode m
   if (ws_bytes < gemm_ws_bytes(p, row_off_h) || (!ws && gemm_ws_bytes(p, row_off_h) > 0))
     return LRMOE_ERR_WORKSPACE;
   return launch_grouped_gemm_bwd(p, row_off_h, row_off_d, Dlt, PhiC, XC, HC, hc_rows, phi_rows, x_rows, W2, W1,
-                                 dW2, dW1, dH, dIn, accumulate, ws, (hipStream_t)stream);
+                                 dW2, dW1, dH, dIn, accumulate, ws, (hipStream_t)stream, (hipEvent_t)din_ready);
 }
 
 lrmoe_status lrmoe_scatter(const lrmoe_problem* p, lrmoe_scatter_mode mode, int64_t n_rows, int32_t width,

@@ -112,7 +112,7 @@ def test_workspace_size_and_host_side_rejections():
     assert lib.lrmoe_compact(ctypes.byref(p), _lib.COMPACT_PHYSICAL, *sw, None, 0, None) == _lib.ERR_WORKSPACE
     q, keep2 = _problem(quota=(6, 0, 7))
     assert lib.lrmoe_grouped_gemm_bwd(ctypes.byref(q), 0, *([fake] * 14), 0, fake, 1 << 30,
-                                      None) == _lib.ERR_INFEASIBLE_QUOTA
+                                      None, None) == _lib.ERR_INFEASIBLE_QUOTA
     assert _lib.status_string(_lib.ERR_INFEASIBLE_QUOTA).startswith("infeasible")
     # packing PhiC needs Phi; packing XC needs X
     args = [fake, None, fake, None, None, None, fake, fake, fake, fake, fake, None, None, fake, fake]
@@ -129,7 +129,7 @@ def _gemm(p, phi_rows=None, x_rows=None, swiglu=True):
     w1 = fake if swiglu else None
     return _lib.load().lrmoe_grouped_gemm_bwd(
         ctypes.byref(p), _lib.COMPACT_PHYSICAL, fake, fake, fake, w1, w1, w1, phi_rows, x_rows, fake, w1, fake, w1,
-        w1, fake, 0, None, 0, None)
+        w1, fake, 0, None, 0, None, None)
 
 
 def test_row_maps_limited_to_2gib_matrices():

@@ -221,6 +221,18 @@ def test_deterministic(case):
         assert torch.equal(res[k], again[k]), k
 
 
+def test_scatter_overlapped_with_weight_gradients_matches_serial(case):
+    """backward(overlap_scatter=True) runs the scatter on a second stream once dIn is
+    complete (the GEMM call records an event for it); it gives the same bits as running it
+    after the whole GEMM call on one stream."""
+    name, pr, s, res, ref = case
+    over = lr.backward(s.P, G=s.G, Phi=s.Phi, alpha=s.alpha, tok=s.tok, slot=s.slot, W2=s.W2, X=s.X, H=s.H,
+                       W1=s.W1, overlap_scatter=True)
+    torch.cuda.synchronize()
+    for k in ("out", "dIn", "dW2") + (("dW1",) if pr.cfg.swiglu else ()):
+        assert torch.equal(over[k], res[k]), k
+
+
 def test_accumulate_adds_to_weight_gradients():
     pr = _make("swiglu_ragged")
     s = Staged(pr)

@@ -338,3 +338,23 @@ def test_infeasible_quota_raises_before_launch():
     with pytest.raises(lr.InfeasibleQuotaError):
         lr.Problem(E=2, T=16, K=2, D=64, F=32, swiglu=True, dtype=lr.BF16, seg_off=r.seg_off,
                    quota=np.array([11, 5], dtype=np.int32), device=DEV)
+
+
+@pytest.mark.parametrize("counts,dtype", [((30, 0, 20), "bf16"), ((0, 0, 0), "bf16"), ((30, 0, 20), "f32")],
+                         ids=["no_retained_bf16", "no_pairs_bf16", "no_retained_f32"])
+def test_nothing_retained(counts, dtype):
+    """All quotas zero (K_tot = 0), or no routed pairs at all (N = 0): every step runs, the
+    weight gradients are overwritten with zeros (not left as they were) and the token-order
+    gradient is zero, as the oracle gives."""
+    cfg = synth.custom("empty", T=32, K=2, E=3, D=128, F=64, counts=counts, dtype=dtype, seed=5)
+    pr = synth.make_problem(cfg, quota=(0, 0, 0))
+    s = Staged(pr)
+    assert s.P.K_tot == 0
+    bufs = {"gemm": {"dW1": torch.full((3, 128, 128), 7.0, device=DEV),
+                     "dW2": torch.full((3, 64, 128), 7.0, device=DEV)},
+            "out": torch.full((32, 128), 7.0, device=DEV)}
+    res = s.backward(bufs=bufs)
+    torch.cuda.synchronize()
+    assert res["sel"].numel() == 0
+    for k in ("dW1", "dW2", "out"):
+        assert torch.count_nonzero(res[k]).item() == 0, k

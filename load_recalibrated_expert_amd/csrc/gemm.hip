@@ -156,11 +156,10 @@ typedef __attribute__((address_space(4))) const int32_t const_i32_t;
 // 2 GiB; the host checks). Rows outside [0, nrows) read as zeros. A wavefront needs 4 row
 // indices per stage, rows 4w + 2j + h for its loads j = 0, 1 and halves h = 0, 1. It reads
 // them with scalar loads (the index array is constant during the kernel), issued at the top
-// of the loop iteration whose end turns them into the load offsets of a later stage: scalar
-// loads count towards the LDS counter, and the wait for them falls together with the wait
-// for the iteration's own LDS reads. Vector loads of the indices into registers instead,
-// interleaved with the direct loads into LDS, cost several percent. Reads are clamped to
-// [0, klen) so they never leave the item's part of the index array.
+// of the loop iteration whose end turns them into the load offsets of a later stage. Scalar
+// loads are not counted by the vector-memory counter whose fixed counts the K loop waits
+// on, and the wait for them falls together with the loop's wait for its own LDS reads.
+// Reads are clamped to [0, klen) so they never leave the item's part of the index array.
 struct DmaTG {
   rsrc_t r;                        // the matrix
   const_i32_t* idx;                // the item's row indices
@@ -300,9 +299,8 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs& sm, LA& la, LB& lb, int
     la.advance(s + 1);
     lb.advance(s + 1);
   }
-  // stage 0 landed: the loads of stages 1..STAGES-2 may still be in flight (row-index loads
-  // come before some stage's data loads in program order, so they only make these waits
-  // stricter)
+  // stage 0 landed: the loads of stages 1..STAGES-2 may still be in flight (every stage
+  // issues 2 * DMA_PER_WAVE direct loads per wavefront and nothing else on this counter)
   constexpr int kPro = (STAGES - 2) * 2 * DMA_PER_WAVE, kLoop = (STAGES - 3) * 2 * DMA_PER_WAVE;
   static_assert(kPro < 64, "vmcnt field");
   __builtin_amdgcn_s_waitcnt(0x0F70 | (kPro & 0xF) | ((kPro >> 4) << 14));

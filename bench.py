@@ -138,7 +138,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU's expert share; --gpus {args.gpus} is not supported "
-              f"(multi-GPU sharding is described in DESIGN.md, not run).", file=sys.stderr)
+              f"(it runs on one GPU; the expert-parallel sharding across GPUs is a design, not code here).",
+              file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -21,13 +21,14 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_floa
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// float -> bf16, round to nearest, ties to even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
+// Two floats -> packed bf16 (lo in bits 0..15), round to nearest, ties to even, with gfx950's
+// v_cvt_pk_bf16_f32: one instruction per pair. For finite inputs (denormals, ties, overflow to
+// infinity included) it gives the same bits as adding 0x7FFF plus the kept lsb and truncating.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // bf16 nearest (ties to even) of the *exact* product a*b, for a, b finite floats whose

@@ -466,7 +466,9 @@ __device__ __forceinline__ void epilogue_swiglu(StageBufs& sm, const f32x16_t (&
       for (int c = 0; c < 8; ++c) {
         const float gate = (c & 1) ? bf16_hi(gg[c >> 1]) : bf16_lo(gg[c >> 1]);
         const float up = (c & 1) ? bf16_hi(uu[c >> 1]) : bf16_lo(uu[c >> 1]);
-        const float sg = 1.0f / (1.0f + expf(-gate));
+        // sigmoid from the hardware base-2 exponential and reciprocal (about 1 ulp each; the
+        // result is rounded to bf16): 1 / (1 + 2^(-gate log2 e))
+        const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gate * -1.44269504088896341f));
         dg[c] = dphi[c] * up * (sg * (1.0f + gate * (1.0f - sg)));
         du[c] = dphi[c] * (gate * sg);
       }

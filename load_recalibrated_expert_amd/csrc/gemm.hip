@@ -37,15 +37,27 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-constexpr int BM = 256, BN = 256, BK = 32, STAGES = 4;
-// 8 wavefronts (two per SIMD) per 256x256 tile: a 2 x 4 grid of 128 x 64 wave tiles, so each
-// wavefront holds 2 x 4 MFMA accumulators (128 registers) and the SIMD can issue one
-// wavefront's MFMAs while the other waits on memory.
-constexpr int NWAVE = 8, NTHR = NWAVE * 64;
-constexpr int WN = 4, WM = NWAVE / WN;          // wave grid over the tile (N x M)
-constexpr int NB = BN / WN / 32, MB = BM / WM / 32;  // 32-wide MFMA blocks per wave (2 x 4)
+constexpr int BM = 256, BK = 32;
+// Block tile configuration: every wavefront owns a 128 x 64 sub-tile held as 2 x 4 MFMA
+// accumulators (128 registers), on a 2 x WN grid of wavefronts, two wavefronts per SIMD.
+// Both GEMM kinds use one block of 8 wavefronts per CU, 256 x 256 tiles and four 32 KB
+// stages. (Two blocks of 4 wavefronts per CU with 256 x 128 tiles and three 24 KB stages
+// each, so that one block's epilogue overlaps the other's MFMAs, ran the data gradients 7%
+// slower: with one stage less, each direct load has a single K step to land.)
+template <int NWAVE_, int BN_, int STAGES_>
+struct TileCfg {
+  static constexpr int NWAVE = NWAVE_, NTHR = NWAVE_ * 64, BN = BN_, STAGES = STAGES_;
+  static constexpr int WM = 2, WN = NWAVE_ / 2;  // wave grid over the tile (M x N)
+  static constexpr int MB = 4, NB = 2;           // 32-wide MFMA blocks per wavefront
+  static constexpr int A_U4 = BM * BK * 2 / 16, B_U4 = BN_ * BK * 2 / 16;  // uint4 per stage
+  static_assert(WN * NB * 32 == BN_ && WM * MB * 32 == BM, "wave tiles cover the block tile");
+};
+using CfgW = TileCfg<8, 256, 4>;  // weight gradients
+using CfgD = TileCfg<8, 256, 4>;  // data gradients
+// the weight-gradient configuration, also used by the host side and the small kernels
+constexpr int BN = CfgW::BN, STAGES = CfgW::STAGES, NWAVE = CfgW::NWAVE, NTHR = CfgW::NTHR;
+constexpr int WN = CfgW::WN, WM = CfgW::WM, NB = CfgW::NB, MB = CfgW::MB;
 constexpr int DMA_PER_WAVE = BM * BK * 2 / 1024 / NWAVE;  // 1 KB direct loads per operand per stage
-constexpr int kTileU4 = BM * BK * 2 / 16;  // uint4 per operand tile per stage (16 KB)
 constexpr int64_t kKcMax = 12288;          // max packed rows per weight-gradient chunk
 constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past num_records: the load returns 0
 
@@ -71,31 +83,39 @@ __device__ __forceinline__ void dma16(rsrc_t r, const uint4* lds_wave_base, uint
 
 // ---------------------------------------------------------------- LDS layouts
 //
-// K-contiguous operand (data-gradient GEMMs): a stage holds 256 rows x 32 K values (64 bytes
-// per row, four 16-byte chunks). Rows r and r + 128 share one 128-byte LDS line: line
-// L = r % 128 holds eight 16-byte slots, and chunk c of row r sits in slot
-// (4 (r / 128) + c) ^ (L % 8). MFMA fragment reads (one 16-byte chunk of each of 32
+// K-contiguous operand (data-gradient GEMMs): a stage holds R rows (256 or 128) x 32 K values
+// (64 bytes per row, four 16-byte chunks). Rows r and r + R/2 share one 128-byte LDS line:
+// line L = r % (R/2) holds eight 16-byte slots, and chunk c of row r sits in slot
+// (4 (r / (R/2)) + c) ^ (L % 8). MFMA fragment reads (one 16-byte chunk of each of 32
 // consecutive rows) then run at the full LDS rate; with a 64-byte line pitch they ran at half.
 //
 // Row-major-in-K operand (weight-gradient GEMMs): a stage holds 32 K rows x 256 columns,
 // 512 bytes per row as eight 64-byte segments; segment s of row k sits in slot s ^ (k & 3),
 // so the 4-row transpose reads of one half-wavefront cover all 64 banks.
 
+template <class C>
 struct StageBufs {
-  uint4 a[STAGES][kTileU4];
-  uint4 b[STAGES][kTileU4];
+  uint4 a[C::STAGES][C::A_U4];
+  uint4 b[C::STAGES][C::B_U4];
 };
 
-// uint4 index of chunk c of row r in a K-contiguous stage
-__device__ __forceinline__ int nt_slot(int r, int c) { return (r & 127) * 8 + ((((r >> 7) << 2) | c) ^ (r & 7)); }
+// uint4 index of chunk c of row r in a K-contiguous stage of 2 HALF rows
+template <int HALF>
+__device__ __forceinline__ int nt_slot(int r, int c) {
+  return (r & (HALF - 1)) * 8 + (((int)(((unsigned)r / HALF) << 2) | c) ^ (r & 7));
+}
 
-// Direct-to-LDS loader of a K-contiguous operand. A 1 KB direct load fills 8 LDS lines
-// (16 tile rows); wave w issues loads j = 0..DMA_PER_WAVE-1 covering lines
-// 8 (w*DMA_PER_WAVE + j) + l/8, and lane l fetches the chunk that belongs in slot l % 8 of
-// its line: slot s holds chunk (s ^ line%8) % 4 of row 128 ((s ^ line%8) / 4) + line.
+// Direct-to-LDS loader of a K-contiguous operand of ROWS rows per stage, for blocks of
+// NWAVE wavefronts. A 1 KB direct load fills 8 LDS lines (16 tile rows); wave w issues
+// loads j = 0..NL-1 covering lines 8 (w*NL + j) + l/8, and lane l fetches the chunk that
+// belongs in slot l % 8 of its line: slot s holds chunk (s ^ line%8) % 4 of row
+// (ROWS/2) ((s ^ line%8) / 4) + line.
+template <int NWAVE_, int ROWS>
 struct DmaK {
+  static constexpr int HALF = ROWS / 2, NL = HALF / 8 / NWAVE_;  // direct loads per wavefront
+  static_assert(NL * 8 * NWAVE_ == HALF, "whole loads per wavefront");
   rsrc_t r;
-  uint32_t off[DMA_PER_WAVE];
+  uint32_t off[NL];
   int col;    // first K element of this lane's chunk within the stage
   int wbase;  // uint4 offset of this wave's region in a stage
   __device__ __forceinline__ void init(const uint16_t* p, int64_t ld, int rows_valid) {
@@ -103,10 +123,10 @@ struct DmaK {
     const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int logical = (l & 7) ^ ((l >> 3) & 7);  // line % 8 == (l / 8) % 8
     col = (logical & 3) * 8;
-    wbase = w * DMA_PER_WAVE * 64;
+    wbase = w * NL * 64;
 #pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; ++j) {
-      const int row = (logical >> 2) * 128 + (w * DMA_PER_WAVE + j) * 8 + (l >> 3);
+    for (int j = 0; j < NL; ++j) {
+      const int row = (logical >> 2) * HALF + (w * NL + j) * 8 + (l >> 3);
       off[j] = row < rows_valid ? (uint32_t)((row * ld + col) * 2) : kOOB;
     }
   }
@@ -123,6 +143,7 @@ struct DmaK {
 // wave w issues loads j covering rows 2 (w*DMA_PER_WAVE + j) + l/32, and lane l fetches the
 // chunk that belongs in 16-byte slot l % 32 of its row.
 struct DmaT {
+  static constexpr int NL = DMA_PER_WAVE;
   rsrc_t r;
   uint32_t off[DMA_PER_WAVE];
   int row[DMA_PER_WAVE];
@@ -161,6 +182,7 @@ typedef __attribute__((address_space(4))) const int32_t const_i32_t;
 // on, and the wait for them falls together with the loop's wait for its own LDS reads.
 // Reads are clamped to [0, klen) so they never leave the item's part of the index array.
 struct DmaTG {
+  static constexpr int NL = DMA_PER_WAVE;
   rsrc_t r;                        // the matrix
   const_i32_t* idx;                // the item's row indices
   uint32_t coff[DMA_PER_WAVE];     // column offset in bytes, or kOOB past the tile's columns
@@ -248,13 +270,14 @@ __device__ __forceinline__ bf16x8_t frag_tr(const uint4* stage, int col0, int k0
 // The MFMA takes the n fragment first, so each lane's accumulator holds 4 consecutive
 // output columns of one output row: acc[nb][mb][v] is output row
 // wm*(32 MB) + mb*32 + lane%32, column wn*(32 NB) + nb*32 + 8*(v/4) + 4*(lane/32) + v%4.
-// One MFMA fragment: rows row0..row0+31 of an operand stage, K16 step kk.
-template <bool TN>
+// One MFMA fragment: rows row0..row0+31 of an operand stage, K16 step kk (a K-contiguous
+// stage holds 2 HALF rows).
+template <bool TN, int HALF>
 __device__ __forceinline__ bf16x8_t load_frag(const uint4* __restrict__ stage, int row0, int kk, int lane) {
   if constexpr (TN) {
     return frag_tr(stage, row0, kk * 16, lane);
   } else {
-    return __builtin_bit_cast(bf16x8_t, stage[nt_slot(row0 + (lane & 31), kk * 2 + (lane >> 5))]);
+    return __builtin_bit_cast(bf16x8_t, stage[nt_slot<HALF>(row0 + (lane & 31), kk * 2 + (lane >> 5))]);
   }
 }
 
@@ -271,18 +294,21 @@ __device__ __forceinline__ void mfma(f32x16_t& acc, const bf16x8_t& n_frag, cons
   acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(n_frag, m_frag, acc, 0, 0, 0);
 }
 
-// The K loop shared by every bf16 GEMM. Four LDS stages of 32 K values per operand are
-// filled by direct loads issued three stages ahead. At the top of stage kt each wave waits
-// for its own loads of stage kt+1, and one barrier then makes stage kt+1 visible and frees
-// stage kt-1's buffer, into which stage kt+3 is loaded. A stage is two K16 steps of
-// NB x MB MFMAs. The wavefront issues in order, so every memory instruction sits right
-// behind an MFMA (hard scheduling fences keep that order): during the first step the
-// direct loads of stage kt+3 and the fragments of the second step; during the second step
-// the fragments of stage kt+1's first step, so MFMAs start right after the next barrier.
-template <bool TN, class LA, class LB>
-__device__ __forceinline__ void gemm_mainloop(StageBufs& sm, LA& la, LB& lb, int kend, uint32_t kstep_a,
+// The K loop shared by every bf16 GEMM. S = C::STAGES LDS stages of 32 K values per operand
+// (four for the weight gradients, three for the data gradients) are filled by direct loads
+// issued S-1 stages ahead. At the top of stage kt each wave waits for its own loads of stage
+// kt+1, and one barrier then makes stage kt+1 visible and frees stage kt-1's buffer, into
+// which stage kt+S-1 is loaded. A stage is two K16 steps of NB x MB MFMAs. The wavefront
+// issues in order, so every memory instruction sits right behind an MFMA (hard scheduling
+// fences keep that order): during the first step the direct loads of stage kt+S-1 and the
+// fragments of the second step; during the second step the fragments of stage kt+1's first
+// step, so MFMAs start right after the next barrier.
+template <class C, bool TN, class LA, class LB>
+__device__ __forceinline__ void gemm_mainloop(StageBufs<C>& sm, LA& la, LB& lb, int kend, uint32_t kstep_a,
                                               uint32_t kstep_b, f32x16_t (&acc)[NB][MB], int wm, int wn, int lane) {
-  constexpr int NM = NB * MB;
+  constexpr int NM = NB * MB, STAGES = C::STAGES, NLA = LA::NL, NLB = LB::NL;
+  constexpr int HA = BM / 2, HB = C::BN / 2;  // K-contiguous stage halves
+  static_assert(NLA + NLB <= NM, "one direct load per MFMA slot of the first K16 step");
   const int nk = (kend + BK - 1) / BK;
   if (nk <= 0) return;
   la.start();
@@ -290,9 +316,9 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs& sm, LA& la, LB& lb, int
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) {
 #pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; ++j) {
-      la.issue_one(j, sm.a[s], s * BK, kend, kstep_a);
-      lb.issue_one(j, sm.b[s], s * BK, kend, kstep_b);
+    for (int j = 0; j < (NLA > NLB ? NLA : NLB); ++j) {
+      if (j < NLA) la.issue_one(j, sm.a[s], s * BK, kend, kstep_a);
+      if (j < NLB) lb.issue_one(j, sm.b[s], s * BK, kend, kstep_b);
     }
     la.fetch(s + 1 - STAGES);  // the indices of stage s + 1
     lb.fetch(s + 1 - STAGES);
@@ -300,16 +326,16 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs& sm, LA& la, LB& lb, int
     lb.advance(s + 1);
   }
   // stage 0 landed: the loads of stages 1..STAGES-2 may still be in flight (every stage
-  // issues 2 * DMA_PER_WAVE direct loads per wavefront and nothing else on this counter)
-  constexpr int kPro = (STAGES - 2) * 2 * DMA_PER_WAVE, kLoop = (STAGES - 3) * 2 * DMA_PER_WAVE;
-  static_assert(kPro < 64, "vmcnt field");
+  // issues NLA + NLB direct loads per wavefront and nothing else on this counter)
+  constexpr int kPro = (STAGES - 2) * (NLA + NLB), kLoop = (STAGES - 3) * (NLA + NLB);
+  static_assert(kPro < 64 && kLoop >= 0, "vmcnt field");
   __builtin_amdgcn_s_waitcnt(0x0F70 | (kPro & 0xF) | ((kPro >> 4) << 14));
   __syncthreads();
   bf16x8_t fa[2][MB], fb[2][NB];
 #pragma unroll
-  for (int i = 0; i < MB; ++i) fa[0][i] = load_frag<TN>(sm.a[0], wm * 32 * MB + i * 32, 0, lane);
+  for (int i = 0; i < MB; ++i) fa[0][i] = load_frag<TN, HA>(sm.a[0], wm * 32 * MB + i * 32, 0, lane);
 #pragma unroll
-  for (int i = 0; i < NB; ++i) fb[0][i] = load_frag<TN>(sm.b[0], wn * 32 * NB + i * 32, 0, lane);
+  for (int i = 0; i < NB; ++i) fb[0][i] = load_frag<TN, HB>(sm.b[0], wn * 32 * NB + i * 32, 0, lane);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt % STAGES, nxt = (kt + 1) % STAGES, ldst = (kt + STAGES - 1) % STAGES;
     const int k_ld = (kt + STAGES - 1) * BK;
@@ -322,18 +348,18 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs& sm, LA& la, LB& lb, int
     for (int i = 0; i < NM; ++i) {
       mfma(acc[i / MB][i % MB], fb[0][i / MB], fa[0][i % MB]);
       __builtin_amdgcn_sched_barrier(0);
-      if (i < DMA_PER_WAVE) la.issue_one(i, sm.a[ldst], k_ld, kend, kstep_a);
-      else if (i < 2 * DMA_PER_WAVE) lb.issue_one(i - DMA_PER_WAVE, sm.b[ldst], k_ld, kend, kstep_b);
-      if (i < MB) fa[1][i] = load_frag<TN>(sm.a[cur], wm * 32 * MB + i * 32, 1, lane);
-      else if (i < MB + NB) fb[1][i - MB] = load_frag<TN>(sm.b[cur], wn * 32 * NB + (i - MB) * 32, 1, lane);
+      if (i < NLA) la.issue_one(i, sm.a[ldst], k_ld, kend, kstep_a);
+      else if (i < NLA + NLB) lb.issue_one(i - NLA, sm.b[ldst], k_ld, kend, kstep_b);
+      if (i < MB) fa[1][i] = load_frag<TN, HA>(sm.a[cur], wm * 32 * MB + i * 32, 1, lane);
+      else if (i < MB + NB) fb[1][i - MB] = load_frag<TN, HB>(sm.b[cur], wn * 32 * NB + (i - MB) * 32, 1, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       mfma(acc[i / MB][i % MB], fb[1][i / MB], fa[1][i % MB]);
       __builtin_amdgcn_sched_barrier(0);
-      if (i < MB) fa[0][i] = load_frag<TN>(sm.a[nxt], wm * 32 * MB + i * 32, 0, lane);
-      else if (i < MB + NB) fb[0][i - MB] = load_frag<TN>(sm.b[nxt], wn * 32 * NB + (i - MB) * 32, 0, lane);
+      if (i < MB) fa[0][i] = load_frag<TN, HA>(sm.a[nxt], wm * 32 * MB + i * 32, 0, lane);
+      else if (i < MB + NB) fb[0][i - MB] = load_frag<TN, HB>(sm.b[nxt], wn * 32 * NB + (i - MB) * 32, 0, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
     la.advance(kt + STAGES);
@@ -345,17 +371,20 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs& sm, LA& la, LB& lb, int
 // ---------------------------------------------------------------- epilogue through LDS
 
 // Writes the accumulators out through LDS so that every output row is handled by
-// consecutive threads with 16-byte accesses. The 256x256 fp32 tile is staged in two halves
-// of 128 rows (the wavefronts with wm = 0, then wm = 1), each filling the 128 KB of stage
-// buffers. A staged row holds 64 chunks of 4 floats; chunk c of row r sits in slot
-// c ^ (r & 15), so the accumulator writes (32 rows per instruction) and the row reads both
-// spread over the banks. BODY(row, col, v[8]) receives 8 consecutive columns of one tile row.
-template <class Body>
-__device__ __forceinline__ void epilogue_staged(StageBufs& sm, const f32x16_t (&acc)[NB][MB], int wm, int wn,
+// consecutive threads with 16-byte accesses. The 256 x BN fp32 tile is staged in two halves
+// of 128 rows (the wavefronts with wm = 0, then wm = 1), each filling the stage buffers
+// (128 x 256 x 4 = 128 KB, or 128 x 128 x 4 = 64 KB of 72 KB). A staged row holds BN/4 chunks
+// of 4 floats; chunk c of row r sits in slot c ^ (r & 15), so the accumulator writes (32 rows
+// per instruction) and the row reads both spread over the banks.
+// BODY(row, col, v[8]) receives 8 consecutive columns of one tile row.
+template <class C, class Body>
+__device__ __forceinline__ void epilogue_staged(StageBufs<C>& sm, const f32x16_t (&acc)[NB][MB], int wm, int wn,
                                                 int lane, Body body) {
+  constexpr int P = C::BN / 4, NT = C::NTHR;
+  static_assert((BM / 2) * C::BN * 4 <= (int)sizeof(StageBufs<C>), "a staged half fits the stage buffers");
   float4* st = reinterpret_cast<float4*>(&sm);
 #pragma unroll
-  for (int half = 0; half < WM; ++half) {
+  for (int half = 0; half < C::WM; ++half) {
     __syncthreads();
     if (wm == half) {
 #pragma unroll
@@ -366,19 +395,19 @@ __device__ __forceinline__ void epilogue_staged(StageBufs& sm, const f32x16_t (&
           for (int q = 0; q < 4; ++q) {
             const int r = mb * 32 + (lane & 31);
             const int c = (wn * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5)) >> 2;
-            st[r * 64 + (c ^ (r & 15))] =
+            st[r * P + (c ^ (r & 15))] =
                 make_float4(acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
           }
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < (BM / WM) * (BN / 8) / NTHR; ++i) {
-      const int id = threadIdx.x + NTHR * i;
-      const int r = id / (BN / 8), c8 = id % (BN / 8);
-      const float4 lo = st[r * 64 + ((2 * c8) ^ (r & 15))];
-      const float4 hi = st[r * 64 + ((2 * c8 + 1) ^ (r & 15))];
+    for (int i = 0; i < (BM / C::WM) * (C::BN / 8) / NT; ++i) {
+      const int id = threadIdx.x + NT * i;
+      const int r = id / (C::BN / 8), c8 = id % (C::BN / 8);
+      const float4 lo = st[r * P + ((2 * c8) ^ (r & 15))];
+      const float4 hi = st[r * P + ((2 * c8 + 1) ^ (r & 15))];
       const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      body(half * (BM / WM) + r, c8 * 8, v);
+      body(half * (BM / C::WM) + r, c8 * 8, v);
     }
   }
 }
@@ -397,7 +426,7 @@ struct DgradArgs {
   const uint16_t* W;   // [E x N x K] weights viewed as rows n with K contiguous
   int64_t ldw, w_estride;
   int N, K;            // output columns, reduction length
-  int ntn;             // ceil(N / BN)
+  int ntn;             // ceil(N / CfgD::BN)
   const int64_t* row_off;
   int E;
   // epilogue
@@ -424,11 +453,14 @@ struct HcBatch {
   uint32_t okm;
 };
 
-__device__ __forceinline__ void epilogue_swiglu(StageBufs& sm, const f32x16_t (&acc)[NB][MB], int wm, int wn,
+template <class C>
+__device__ __forceinline__ void epilogue_swiglu(StageBufs<C>& sm, const f32x16_t (&acc)[NB][MB], int wm, int wn,
                                                 int lane, const DgradArgs& g, int64_t row0, int rows_valid, int n0,
                                                 int n_valid) {
+  constexpr int WM = C::WM, BN = C::BN, NTHR = C::NTHR, P = BN / 4;
   constexpr int kIt = (BM / WM) * (BN / 8) / NTHR;  // rows per thread per half (8)
   constexpr int kRowStep = NTHR / (BN / 8);          // 16
+  static_assert(kIt == 8, "batches of 4 + 4 and 8 rows");
   const int tr0 = threadIdx.x / (BN / 8), tc = (threadIdx.x % (BN / 8)) * 8;
   const int64_t ld = 2 * (int64_t)g.F;
   const int F = g.F;
@@ -455,8 +487,8 @@ __device__ __forceinline__ void epilogue_swiglu(StageBufs& sm, const f32x16_t (&
 #pragma unroll
     for (int b = 0; b < NBt; ++b) {
       const int r = tr0 + kRowStep * (i0 + b), c8 = tc / 8;
-      const float4 lo = st[r * 64 + ((2 * c8) ^ (r & 15))];
-      const float4 hi = st[r * 64 + ((2 * c8 + 1) ^ (r & 15))];
+      const float4 lo = st[r * P + ((2 * c8) ^ (r & 15))];
+      const float4 hi = st[r * P + ((2 * c8 + 1) ^ (r & 15))];
       const float dphi[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       const bool ok = (bt.okm >> b) & 1u;  // rows outside the tile or HC read as zeros
       const uint32_t gg[4] = {ok ? bt.gw[b].x : 0u, ok ? bt.gw[b].y : 0u, ok ? bt.gw[b].z : 0u, ok ? bt.gw[b].w : 0u};
@@ -510,7 +542,7 @@ __device__ __forceinline__ void epilogue_swiglu(StageBufs& sm, const f32x16_t (&
           for (int q = 0; q < 4; ++q) {
             const int r = mb * 32 + (lane & 31);
             const int c = (wn * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5)) >> 2;
-            st[r * 64 + (c ^ (r & 15))] =
+            st[r * P + (c ^ (r & 15))] =
                 make_float4(acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
           }
     }
@@ -525,9 +557,11 @@ __device__ __forceinline__ void epilogue_swiglu(StageBufs& sm, const f32x16_t (&
   }
 }
 
+// One output tile per block.
 template <int EPI>
-__global__ __launch_bounds__(NTHR) void dgrad_kernel(DgradArgs g) {
-  __shared__ StageBufs lds;
+__global__ __launch_bounds__(CfgD::NTHR) void dgrad_kernel(DgradArgs g) {
+  using C = CfgD;
+  __shared__ StageBufs<C> lds;
   const int b = xcd_remap(blockIdx.x, gridDim.x);
   int e = 0, local = b;
   int64_t r0 = 0, m = 0;
@@ -542,22 +576,23 @@ __global__ __launch_bounds__(NTHR) void dgrad_kernel(DgradArgs g) {
   const int mt = local / g.ntn, nt = local % g.ntn;
   const int64_t row0 = r0 + (int64_t)mt * BM;
   const int rows_valid = (int)min<int64_t>(BM, m - (int64_t)mt * BM);
-  const int n0 = nt * BN;
-  const int n_valid = min(BN, g.N - n0);
+  const int n0 = nt * C::BN;
+  const int n_valid = min(C::BN, g.N - n0);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   f32x16_t acc[NB][MB];
   zero_acc(acc);
-  DmaK la, lb;
+  DmaK<C::NWAVE, BM> la;
+  DmaK<C::NWAVE, C::BN> lb;
   la.init(g.A + row0 * g.lda, g.lda, rows_valid);
   lb.init(g.W + (int64_t)e * g.w_estride + (int64_t)n0 * g.ldw, g.ldw, n_valid);
-  gemm_mainloop<false>(lds, la, lb, g.K, 0, 0, acc, wm, wn, lane);
+  gemm_mainloop<C, false>(lds, la, lb, g.K, 0, 0, acc, wm, wn, lane);
 
   if (EPI == EPI_SWIGLU) {
-    epilogue_swiglu(lds, acc, wm, wn, lane, g, row0, rows_valid, n0, n_valid);
+    epilogue_swiglu<C>(lds, acc, wm, wn, lane, g, row0, rows_valid, n0, n_valid);
   } else {
     uint16_t* __restrict__ out = g.out;
-    epilogue_staged(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
+    epilogue_staged<C>(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
       if (tr < rows_valid && tc < n_valid) *(uint4*)(out + (row0 + tr) * g.ldo + n0 + tc) = pack_bf16x8(v);
     });
   }
@@ -649,7 +684,7 @@ __global__ __launch_bounds__(NTHR) void wgrad_plan_kernel(WgradArgs g) {
 // through its row map (a compile-time choice, so neither loader carries the other's code).
 template <bool G0, bool G1>
 __global__ __launch_bounds__(NTHR) void wgrad_kernel(WgradArgs g) {
-  __shared__ StageBufs lds;
+  __shared__ StageBufs<CfgW> lds;
   // hardware sends block i to XCD i % 8; the grid holds 8 x (largest range) blocks
   const int x = blockIdx.x & 7;
   const int b = g.xlo[x] + (int)(blockIdx.x >> 3);
@@ -683,16 +718,16 @@ __global__ __launch_bounds__(NTHR) void wgrad_kernel(WgradArgs g) {
   if ((G0 || G1) && (ty == 0 ? G0 : G1)) {
     DmaTG la;
     la.init(T.A + m0, T.lda, m_valid, T.a_rows + r0 + k_begin, klen, T.a_nrows);
-    gemm_mainloop<true>(lds, la, lb, klen, 0, (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
+    gemm_mainloop<CfgW, true>(lds, la, lb, klen, 0, (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
   } else {
     DmaT la;
     la.init(T.A + (r0 + k_begin) * T.lda + m0, T.lda, m_valid);
-    gemm_mainloop<true>(lds, la, lb, klen, (uint32_t)(T.lda * 2), (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
+    gemm_mainloop<CfgW, true>(lds, la, lb, klen, (uint32_t)(T.lda * 2), (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
   }
 
   if (s > 1) {
     float* __restrict__ p = g.partials + (g.plan_pbase[e] + (int64_t)chunk * tiles + rem) * (int64_t)(BM * BN);
-    epilogue_staged(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
+    epilogue_staged<CfgW>(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
       float4* q4 = (float4*)(p + tr * BN + tc);
       q4[0] = make_float4(v[0], v[1], v[2], v[3]);
       q4[1] = make_float4(v[4], v[5], v[6], v[7]);
@@ -700,7 +735,7 @@ __global__ __launch_bounds__(NTHR) void wgrad_kernel(WgradArgs g) {
   } else {
     float* __restrict__ o = T.out + (int64_t)e * T.M * T.N;
     const bool accum = g.accumulate != 0;
-    epilogue_staged(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
+    epilogue_staged<CfgW>(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
       if (tr < m_valid && tc < n_valid) {
         float4* q4 = (float4*)(o + (int64_t)(m0 + tr) * T.N + n0 + tc);
         float4 a = make_float4(v[0], v[1], v[2], v[3]), b = make_float4(v[4], v[5], v[6], v[7]);
@@ -997,7 +1032,7 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
   d2.w_estride = (int64_t)F * D;
   d2.N = F;
   d2.K = D;
-  d2.ntn = (int)ceil_div(F, BN);
+  d2.ntn = (int)ceil_div(F, CfgD::BN);
   d2.row_off = row_off_d;
   d2.E = E;
   d2.F = F;
@@ -1007,7 +1042,7 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
     d2.hc_nrows = hc_nrows;
     d2.out = (uint16_t*)dH;
     d2.ldo = 2 * F;
-    if (mtiles > 0) dgrad_kernel<EPI_SWIGLU><<<(unsigned)(mtiles * d2.ntn), NTHR, 0, s>>>(d2);
+    if (mtiles > 0) dgrad_kernel<EPI_SWIGLU><<<(unsigned)(mtiles * d2.ntn), CfgD::NTHR, 0, s>>>(d2);
     DgradArgs d1 = d2;
     d1.A = (const uint16_t*)dH;
     d1.lda = 2 * F;
@@ -1016,16 +1051,16 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
     d1.w_estride = (int64_t)D * 2 * F;
     d1.N = D;
     d1.K = 2 * F;
-    d1.ntn = (int)ceil_div(D, BN);
+    d1.ntn = (int)ceil_div(D, CfgD::BN);
     d1.HC = nullptr;
     d1.hc_rows = nullptr;
     d1.out = (uint16_t*)dIn;
     d1.ldo = D;
-    if (mtiles > 0) dgrad_kernel<EPI_STORE><<<(unsigned)(mtiles * d1.ntn), NTHR, 0, s>>>(d1);
+    if (mtiles > 0) dgrad_kernel<EPI_STORE><<<(unsigned)(mtiles * d1.ntn), CfgD::NTHR, 0, s>>>(d1);
   } else {
     d2.out = (uint16_t*)dIn;
     d2.ldo = F;
-    if (mtiles > 0) dgrad_kernel<EPI_STORE><<<(unsigned)(mtiles * d2.ntn), NTHR, 0, s>>>(d2);
+    if (mtiles > 0) dgrad_kernel<EPI_STORE><<<(unsigned)(mtiles * d2.ntn), CfgD::NTHR, 0, s>>>(d2);
   }
   if (mark_din() != LRMOE_OK) return LRMOE_ERR_HIP;
 

@@ -55,6 +55,10 @@ SMALL = {
     # scatter paths, tokens meeting one expert in several slots
     "many_slots": dict(cfg=synth.custom("many_slots", T=20, K=72, E=3, D=256, F=128, counts=(700, 400, 300),
                                         seed=20), rho="0.6"),
+    # more data-gradient tiles than one round of 256 CUs: 106 M-tiles x 3 FC2 N-tiles (the
+    # last one ragged) over three experts
+    "round_split": dict(cfg=synth.custom("round_split", T=16750, K=2, E=3, D=256, F=640,
+                                         counts=(14000, 12000, 7500), seed=22), rho="0.8"),
     # rows wider than any register-held compaction (D = 4160 > 512 16-byte chunks)
     "widest_rows": dict(cfg=synth.custom("widest_rows", T=60, K=2, E=2, D=4160, F=64, counts=(70, 40),
                                          seed=21), rho="0.5"),

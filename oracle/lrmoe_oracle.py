@@ -11,7 +11,9 @@ LRMoE paper's Algorithm 1 ("Resource-constrained layer-wise load calibration",
 its backward-time calibration block) gives them:
 
 1. ``score``    - the Load Recalibration Metric of every routed pair
-                  (section 3.2, Proposition 3.1, Eq. 3; appendix 7.1, Eq. 11-12).
+                  (section 3.2, Proposition 3.1, Eq. 3; appendix 7.1, Eq. 11-12);
+                  ``score_gradient_only`` - the gradient-only criteria it is
+                  compared with in the ablation (section 4.7, Table 2).
 2. ``select``   - per-expert TopK of the scores under fixed quotas
                   (section 3.3; appendix 7.2, Proposition 7.1 and Eq. 17).
 3. ``compact``  - gather of the retained gradient rows and saved activations
@@ -39,7 +41,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "InfeasibleQuota", "widen", "round_bf16", "score", "select", "compact",
+    "InfeasibleQuota", "widen", "round_bf16", "score", "score_gradient_only", "select", "compact",
     "swiglu_expert_backward", "linear_expert_backward", "scatter_tokens", "scatter_slots",
     "backward",
 ]
@@ -97,6 +99,29 @@ def score(G, Phi, alpha, tok, dtype: str, chunk: int = 16384) -> np.ndarray:
         pn[j0:j0 + chunk] = np.sum(p * p, axis=1)
     a = np.asarray(alpha, dtype=np.float64)
     return a * a * gn[np.asarray(tok, dtype=np.int64)] * pn
+
+
+def score_gradient_only(G, tok, dtype: str, criterion: str, chunk: int = 16384) -> np.ndarray:
+    """Gradient-only selection scores, the alternative criteria of the ablation
+    (section 4.7, Table 2: a squared gradient norm and an absolute gradient
+    magnitude). A gradient-only rule sees neither the routing weight nor the saved
+    activation, so every pair of token t gets the same score, from g_t alone:
+
+      "grad_sqnorm"  sum_i g_{t,i}^2    (the squared norm of the upstream gradient)
+      "grad_abs"     sum_i |g_{t,i}|    (its absolute magnitude, read as the L1 sum;
+                                         the plain norm would rank like grad_sqnorm)
+
+    G: [T, D] upstream gradients before the routing weight; tok: [N] token of each
+    pair. Returns float64 [N]. The random-selection baseline of the same table needs
+    no function here: its scores are the random draws themselves, fed to ``select``."""
+    if criterion not in ("grad_sqnorm", "grad_abs"):
+        raise ValueError(f"unknown criterion {criterion!r}")
+    T = G.shape[0]
+    gs = np.empty(T, dtype=np.float64)
+    for t0 in range(0, T, chunk):
+        g = widen(G[t0:t0 + chunk], dtype)
+        gs[t0:t0 + chunk] = np.sum(g * g, axis=1) if criterion == "grad_sqnorm" else np.sum(np.abs(g), axis=1)
+    return gs[np.asarray(tok, dtype=np.int64)]
 
 
 # ---------------------------------------------------------------------------- step 2

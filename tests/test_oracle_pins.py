@@ -139,6 +139,44 @@ def check_score_is_omission_change(o, seed=3):
         assert abs(diff - R[u]) <= 1e-12 * R[u], (u, diff, R[u])
 
 
+def check_gradient_only_brute_force(o, seed=4):
+    """The gradient-only criteria (section 4.7, Table 2) written out element by element with
+    exact rational arithmetic on dyadic bf16 inputs: sum of squares and sum of magnitudes
+    of the pair's token row, independent of its slot, routing weight and expert."""
+    from fractions import Fraction
+    rng = _rng(seed)
+    T, D, N = 5, 7, 11
+    G = (rng.integers(-64, 65, size=(T, D)) / 16.0).astype(np.float32)  # dyadic, exact in bf16
+    tok = rng.integers(0, T, size=N).astype(np.int32)
+    Gb = synth.f32_to_bf16_bits(G)
+    for crit in ("grad_sqnorm", "grad_abs"):
+        R = o.score_gradient_only(Gb, tok, "bf16", crit)
+        for j in range(N):
+            row = [Fraction(float(x)) for x in G[tok[j]]]
+            ref = sum(x * x for x in row) if crit == "grad_sqnorm" else sum(abs(x) for x in row)
+            assert Fraction(float(R[j])) == ref, (crit, j)
+
+
+def check_gradient_only_against_lrm(o, seed=5):
+    """With alpha = 1 and a saved activation of unit norm (one coordinate equal to 1) the LRM
+    score (pinned above by brute-force outer products) reduces to the squared gradient norm;
+    the magnitude criterion scales linearly: |c| times for the rows scaled by c = 2^k."""
+    rng = _rng(seed)
+    T, D, F, N = 6, 9, 4, 13
+    G = rng.standard_normal((T, D)).astype(np.float32)
+    tok = rng.integers(0, T, size=N).astype(np.int32)
+    Phi = np.zeros((N, F), dtype=np.float32)
+    Phi[np.arange(N), rng.integers(0, F, size=N)] = 1.0
+    Gb = synth.f32_to_bf16_bits(G)
+    lrm = o.score(Gb, synth.f32_to_bf16_bits(Phi), np.ones(N, dtype=np.float32), tok, "bf16")
+    assert np.array_equal(o.score_gradient_only(Gb, tok, "bf16", "grad_sqnorm"), lrm)
+    a1 = o.score_gradient_only(Gb, tok, "bf16", "grad_abs")
+    a4 = o.score_gradient_only(synth.f32_to_bf16_bits(-4.0 * G), tok, "bf16", "grad_abs")
+    assert np.array_equal(a4, 4.0 * a1)
+    with pytest.raises(ValueError):
+        o.score_gradient_only(Gb, tok, "bf16", "random")
+
+
 def check_select_exhaustive(o, seed=1, ties=False):
     """Proposition 7.1: per expert, the retained set maximises the retained score sum
     among all subsets of size q_e (and the dropped set minimises Eq. 13; Eq. 16 links
@@ -333,6 +371,8 @@ ALL_CHECKS = {
     "score_outer_product_f32": lambda o: check_score_outer_product(o, "f32"),
     "score_dyadic_exact": check_score_dyadic_exact,
     "score_is_omission_change": check_score_is_omission_change,
+    "gradient_only_brute_force": check_gradient_only_brute_force,
+    "gradient_only_against_lrm": check_gradient_only_against_lrm,
     "select_exhaustive_distinct": lambda o: check_select_exhaustive(o, ties=False),
     "select_exhaustive_ties": lambda o: check_select_exhaustive(o, seed=11, ties=True),
     "select_per_expert": check_select_per_expert,
@@ -399,6 +439,17 @@ def _backward_on(o, *, G, Phi, alpha, tok, slot, seg_off, quota, dtype, T, W2, X
 
 def _score_alpha_not_squared(G, Phi, alpha, tok, dtype, chunk=16384):
     return oracle.score(G, Phi, alpha, tok, dtype) / np.asarray(alpha, dtype=np.float64)
+
+
+def _gradient_only_signed_sum(G, tok, dtype, criterion, chunk=16384):
+    if criterion == "grad_abs":
+        return oracle.widen(G, dtype).sum(axis=1)[np.asarray(tok, dtype=np.int64)]
+    return oracle.score_gradient_only(G, tok, dtype, criterion)
+
+
+def _gradient_only_by_pair_row(G, tok, dtype, criterion, chunk=16384):
+    n = len(tok)
+    return oracle.score_gradient_only(G, np.arange(n) % np.asarray(G).shape[0], dtype, criterion)
 
 
 def _select_smallest(R, seg_off, quota):
@@ -472,6 +523,10 @@ def _round_truncate(x):
 PLANTED = [
     ("score_alpha_not_squared", dict(score=_score_alpha_not_squared),
      ["score_outer_product_bf16", "score_dyadic_exact", "score_is_omission_change"]),
+    ("gradient_abs_without_abs", dict(score_gradient_only=_gradient_only_signed_sum),
+     ["gradient_only_brute_force", "gradient_only_against_lrm"]),
+    ("gradient_only_ignores_token", dict(score_gradient_only=_gradient_only_by_pair_row),
+     ["gradient_only_brute_force", "gradient_only_against_lrm"]),
     ("select_keeps_smallest", dict(select=_select_smallest),
      ["select_exhaustive_distinct", "fig4_worked_example", "select_per_expert"]),
     ("select_layer_wide", dict(select=_select_layer_wide), ["select_per_expert"]),

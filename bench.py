@@ -46,6 +46,9 @@ def parse():
                          "of known size, used to scale hardware byte counters)")
     ap.add_argument("--cpu-sample-frac", type=float, default=1.0,
                     help="fraction of the pairs (smallest experts first) the oracle runs on")
+    ap.add_argument("--criterion", default="lrm", choices=["lrm", "grad_sqnorm", "grad_abs", "random"],
+                    help="selection criterion: the LRM score (default) or an alternative of the ablation; "
+                         "'random' selects on uniform draws made once on the host (no score kernel)")
     return ap.parse_args()
 
 
@@ -56,11 +59,16 @@ def to_dev(np_mod, torch, a, dtype, dev):
     return torch.from_numpy(a).to(dev)
 
 
-def algorithmic_bytes(cfg, N, K_tot, packed=False):
+def algorithmic_bytes(cfg, N, K_tot, packed=False, criterion="lrm"):
     """Bytes each step reads once and writes once (storage dtype e; f32 scores/outputs)."""
     e = 2 if cfg.dtype == "bf16" else 4
     T, D, F = cfg.T, cfg.D, cfg.F
-    score = (T * D + N * F) * e + N * (4 + 4 + 4)            # G, Phi, alpha, tok -> R
+    if criterion == "lrm":
+        score = (T * D + N * F) * e + N * (4 + 4 + 4)        # G, Phi, alpha, tok -> R
+    elif criterion == "random":
+        score = 0                                             # the draws are an input
+    else:
+        score = T * D * e + N * (4 + 4)                       # G, tok -> R
     # compact reads each token's G row once and writes every retained pair's Dlt row once;
     # packed, it also reads each token's X row and each retained pair's Phi row once and
     # writes their copies (the saved [gate | up] rows are always read in place by the GEMM)
@@ -189,8 +197,15 @@ def main():
             bufs["side_ws"] = torch.empty_like(P.workspace())
             bufs["out"] = torch.empty(P.T, cfg.D if cfg.swiglu else cfg.F, dtype=torch.float32, device=dev)
         rec(0)
-        R = lr.score(P, G, Phi, alpha, tok, R=bufs.get("R"))
-        bufs["R"] = R
+        if args.criterion == "random":  # uniform draws made once on the host: the scores are an input
+            if "R" not in bufs:
+                bufs["R"] = torch.from_numpy(np.random.default_rng(cfg.seed).random(P.N).astype(np.float32)).to(dev)
+            R = bufs["R"]
+        else:
+            crit_lrm = args.criterion == "lrm"
+            R = lr.score(P, G, Phi if crit_lrm else None, alpha if crit_lrm else None, tok, R=bufs.get("R"),
+                         criterion=args.criterion)
+            bufs["R"] = R
         rec(1)
         sel, keep = lr.select(P, R, sel=bufs.get("sel"), keep=bufs.get("keep"))
         bufs.setdefault("sel", sel)
@@ -253,13 +268,14 @@ def main():
     wall, per = measure(lr.COMPACT_PHYSICAL)
     ms = wall / args.steps * 1e3
     value = P.K_tot * args.steps / wall
-    bytes_ = algorithmic_bytes(cfg, P.N, P.K_tot, packed=args.packed)
+    bytes_ = algorithmic_bytes(cfg, P.N, P.K_tot, packed=args.packed, criterion=args.criterion)
     fl = gemm_flops(cfg, P.K_tot)
     peak = BF16_PEAK_TFLOPS if dt == "bf16" else FP32_PEAK_TFLOPS
     gemm_tf = fl / (per["grouped_gemm_bwd"] * 1e-3) / 1e12
     kernels = {
-        "score": {"ms": per["score"], "GB/s": bytes_["score"] / per["score"] / 1e6,
-                  "hbm_frac": bytes_["score"] / per["score"] / 1e6 / HBM_PEAK_GBS},
+        "score": ({"ms": per["score"], "GB/s": bytes_["score"] / per["score"] / 1e6,
+                   "hbm_frac": bytes_["score"] / per["score"] / 1e6 / HBM_PEAK_GBS} if bytes_["score"] else
+                  {"ms": per["score"], "note": "no score kernel: uniform draws made once on the host"}),
         "select": {"ms": per["select"]},
         "compact": {"ms": per["compact"], "GB/s": bytes_["compact"] / per["compact"] / 1e6,
                     "hbm_frac": bytes_["compact"] / per["compact"] / 1e6 / HBM_PEAK_GBS},
@@ -273,7 +289,7 @@ def main():
         "vs_baseline": None, "dtype": dt, "data": "synthetic (seeded; pages' shapes, no dataset)",
         "config": {"workload": cfg.name, "T": cfg.T, "top_k": cfg.K, "local_experts": cfg.E, "D": cfg.D,
                    "F": cfg.F, "swiglu": cfg.swiglu, "rho": rho, "pairs": P.N, "retained_pairs": P.K_tot,
-                   "mode": "physical compaction",
+                   "mode": "physical compaction", "criterion": args.criterion,
                    "scatter": "second stream, under the weight gradients" if overlap else "after the GEMM call"},
         "roofline": {"bound": "mfma", "achieved": gemm_tf, "peak": peak, "unit": "TFLOP/s",
                      "frac": gemm_tf / peak, "traffic": recorded_traffic(cfg.name),
@@ -289,7 +305,7 @@ def main():
             "grouped_gemm_ms": mper["grouped_gemm_bwd"], "gemm_rows": P.N, "compact_rows": P.K_tot,
             "gemm_flops": mfl, "speedup_of_compaction": (mwall / args.steps * 1e3) / ms,
         }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.criterion == "lrm":  # the oracle's backward scores with LRM
         cb = cpu_baseline(pr, args.cpu_sample_frac)
         cb.pop("_out", None)
         result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}

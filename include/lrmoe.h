@@ -74,6 +74,13 @@ typedef enum lrmoe_compact_mode { LRMOE_COMPACT_PHYSICAL = 0, LRMOE_COMPACT_ZERO
  *        ((token, routing-slot) positions in a zero-initialised buffer, section 3.1). */
 typedef enum lrmoe_scatter_mode { LRMOE_SCATTER_TOKEN = 0, LRMOE_SCATTER_SLOT = 1 } lrmoe_scatter_mode;
 
+/* Selection criterion of lrmoe_score_criterion (section 4.7, Table 2, the ablation). */
+typedef enum lrmoe_criterion {
+  LRMOE_CRITERION_LRM = 0,          /* the Load Recalibration Metric, as lrmoe_score     */
+  LRMOE_CRITERION_GRAD_SQNORM = 1,  /* squared gradient norm  ||G[tok[j]]||^2            */
+  LRMOE_CRITERION_GRAD_ABS = 2      /* absolute gradient magnitude  sum_i |G[tok[j], i]| */
+} lrmoe_criterion;
+
 typedef struct lrmoe_problem {
   int32_t E;              /* local experts                                          */
   int32_t T;              /* tokens                                                 */
@@ -107,6 +114,18 @@ lrmoe_status lrmoe_workspace_size(const lrmoe_problem* p, lrmoe_compact_mode mod
  * R [N] f32 out. Norms are accumulated in fp64; R is rounded once to f32. */
 lrmoe_status lrmoe_score(const lrmoe_problem* p, const void* G, const void* Phi, const float* alpha,
                          const int32_t* tok, float* R, void* ws, size_t ws_bytes, lrmoe_stream_t stream);
+
+/* Step 1 with another selection criterion: the alternatives the LRM score is compared
+ * with in the ablation (section 4.7, Table 2). The gradient-only criteria score pair j
+ * from its token's upstream gradient row G[tok[j]] alone (no routing weight, no saved
+ * activation): the squared norm, or the sum of magnitudes. LRMOE_CRITERION_LRM is exactly
+ * lrmoe_score. For the gradient-only criteria Phi and alpha may be NULL; a token outside
+ * [0,T) scores 0. Sums in fp64, R rounded once to f32. Workspace as lrmoe_score; an
+ * unknown criterion is LRMOE_ERR_INVALID_ARG. The table's random-selection baseline needs
+ * no kernel: its scores are random draws, which the caller passes to lrmoe_select. */
+lrmoe_status lrmoe_score_criterion(const lrmoe_problem* p, lrmoe_criterion criterion, const void* G,
+                                   const void* Phi, const float* alpha, const int32_t* tok, float* R,
+                                   void* ws, size_t ws_bytes, lrmoe_stream_t stream);
 
 /* Step 2 - per-expert TopK under fixed quotas (section 3.3; appendix 7.2, Prop. 7.1):
  * inside each segment keep the q_e largest R; among equal R the lower pair index wins.

@@ -104,11 +104,23 @@ class Problem:
         return self.cseg_off_d if mode == COMPACT_PHYSICAL else self.seg_off_d
 
 
-def score(p: Problem, G, Phi, alpha, tok, R=None, stream=None):
+CRITERIA = {"lrm": 0, "grad_sqnorm": 1, "grad_abs": 2}
+
+
+def score(p: Problem, G, Phi, alpha, tok, R=None, criterion="lrm", stream=None):
+    """Step 1. ``criterion``: "lrm" (the LRM score), or the gradient-only criteria of the
+    ablation, "grad_sqnorm" / "grad_abs" (Phi and alpha may then be None)."""
     R = R if R is not None else torch.empty(p.N, dtype=torch.float32, device=p.device)
     ws = p.workspace()
-    _lib.check(library().lrmoe_score(ctypes.byref(p.c), _ptr(G), _ptr(Phi), _ptr(alpha), _ptr(tok), _ptr(R),
-                                     _ptr(ws), ws.numel(), _stream(stream)), "lrmoe_score")
+    if criterion == "lrm":
+        _lib.check(library().lrmoe_score(ctypes.byref(p.c), _ptr(G), _ptr(Phi), _ptr(alpha), _ptr(tok), _ptr(R),
+                                         _ptr(ws), ws.numel(), _stream(stream)), "lrmoe_score")
+    else:
+        if criterion not in CRITERIA:
+            raise ValueError(f"unknown criterion {criterion!r}; expected one of {sorted(CRITERIA)}")
+        _lib.check(library().lrmoe_score_criterion(ctypes.byref(p.c), CRITERIA[criterion], _ptr(G), _ptr(Phi),
+                                                   _ptr(alpha), _ptr(tok), _ptr(R), _ptr(ws), ws.numel(),
+                                                   _stream(stream)), "lrmoe_score_criterion")
     return R
 
 

@@ -21,7 +21,7 @@ COMPACT_PHYSICAL, COMPACT_ZERO_MASKED = 0, 1
 SCATTER_TOKEN, SCATTER_SLOT = 0, 1
 
 EXPORTS = ("lrmoe_status_string", "lrmoe_version", "lrmoe_validate", "lrmoe_workspace_size",
-           "lrmoe_score", "lrmoe_select", "lrmoe_compact", "lrmoe_grouped_gemm_bwd", "lrmoe_scatter")
+           "lrmoe_score", "lrmoe_score_criterion", "lrmoe_select", "lrmoe_compact", "lrmoe_grouped_gemm_bwd", "lrmoe_scatter")
 
 
 class LrmoeError(RuntimeError):
@@ -62,6 +62,7 @@ def load() -> ctypes.CDLL:
         "lrmoe_validate": [P, ctypes.POINTER(i64), ctypes.POINTER(i64)],
         "lrmoe_workspace_size": [P, ctypes.c_int, ctypes.POINTER(sz)],
         "lrmoe_score": [P, vp, vp, vp, vp, vp, vp, sz, vp],
+        "lrmoe_score_criterion": [P, i32, vp, vp, vp, vp, vp, vp, sz, vp],
         "lrmoe_select": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
         "lrmoe_compact": [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                           ctypes.c_size_t, vp],

@@ -68,6 +68,22 @@ __device__ __forceinline__ double sumsq_bf16x8(uint4 v) {
   }
   return s;
 }
+// Sum of magnitudes of 8 bf16 values held in a uint4, in fp64.
+__device__ __forceinline__ double sumabs_bf16x8(uint4 v) {
+  double s = 0.0;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s += (double)fabsf(bf16_lo(w[i]));
+    s += (double)fabsf(bf16_hi(w[i]));
+  }
+  return s;
+}
+// Sum of magnitudes of 4 floats held in a uint4, in fp64.
+__device__ __forceinline__ double sumabs_f32x4(uint4 v) {
+  return (double)fabsf(__uint_as_float(v.x)) + (double)fabsf(__uint_as_float(v.y)) +
+         (double)fabsf(__uint_as_float(v.z)) + (double)fabsf(__uint_as_float(v.w));
+}
 // Sum of squares of 4 floats held in a uint4, in fp64.
 __device__ __forceinline__ double sumsq_f32x4(uint4 v) {
   double a = __uint_as_float(v.x), b = __uint_as_float(v.y), c = __uint_as_float(v.z),
@@ -87,6 +103,8 @@ inline lrmoe_status launch_status() {
 
 lrmoe_status launch_score(const lrmoe_problem* p, const void* G, const void* Phi, const float* alpha,
                           const int32_t* tok, float* R, double* gn, hipStream_t s);
+lrmoe_status launch_score_gradient(const lrmoe_problem* p, bool magnitude, const void* G, const int32_t* tok,
+                                    float* R, double* gs, hipStream_t s);
 
 size_t select_ws_bytes(const lrmoe_problem* p);
 lrmoe_status launch_select(const lrmoe_problem* p, const float* R, const int64_t* seg_off_d,

@@ -97,6 +97,19 @@ lrmoe_status lrmoe_score(const lrmoe_problem* p, const void* G, const void* Phi,
   return launch_score(p, G, Phi, alpha, tok, R, (double*)ws, (hipStream_t)stream);
 }
 
+lrmoe_status lrmoe_score_criterion(const lrmoe_problem* p, lrmoe_criterion criterion, const void* G,
+                                   const void* Phi, const float* alpha, const int32_t* tok, float* R, void* ws,
+                                   size_t ws_bytes, lrmoe_stream_t stream) {
+  if (criterion == LRMOE_CRITERION_LRM) return lrmoe_score(p, G, Phi, alpha, tok, R, ws, ws_bytes, stream);
+  if (criterion != LRMOE_CRITERION_GRAD_SQNORM && criterion != LRMOE_CRITERION_GRAD_ABS)
+    return LRMOE_ERR_INVALID_ARG;
+  LRMOE_TRY(check_problem(p, nullptr, nullptr));
+  if ((p->T > 0 && !G) || (p->N > 0 && (!tok || !R))) return LRMOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < align_up(sizeof(double) * (size_t)p->T, 256)) return LRMOE_ERR_WORKSPACE;
+  return launch_score_gradient(p, criterion == LRMOE_CRITERION_GRAD_ABS, G, tok, R, (double*)ws,
+                               (hipStream_t)stream);
+}
+
 lrmoe_status lrmoe_select(const lrmoe_problem* p, const float* R, const int64_t* seg_off_d,
                           const int32_t* quota_d, const int64_t* cseg_off_d, int32_t* sel, uint8_t* keep,
                           void* ws, size_t ws_bytes, lrmoe_stream_t stream) {

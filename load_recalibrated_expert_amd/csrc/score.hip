@@ -14,8 +14,9 @@ namespace {
 constexpr int kScoreThreads = 256;
 constexpr int kUnroll = 4;
 
-// One wavefront per token row; each lane streams 16-byte chunks.
-template <bool BF16>
+// One wavefront per token row; each lane streams 16-byte chunks. ABS: sum of magnitudes
+// instead of squares (the absolute-gradient criterion of the ablation).
+template <bool BF16, bool ABS = false>
 __global__ __launch_bounds__(kScoreThreads) void token_sqnorm_kernel(const uint4* __restrict__ G,
                                                                      int T, int chunks_per_row,
                                                                      double* __restrict__ gn) {
@@ -32,7 +33,10 @@ __global__ __launch_bounds__(kScoreThreads) void token_sqnorm_kernel(const uint4
       v[u] = c < chunks_per_row ? ld_stream(row + c) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) acc += BF16 ? sumsq_bf16x8(v[u]) : sumsq_f32x4(v[u]);
+    for (int u = 0; u < kUnroll; ++u) {
+      if (ABS) acc += BF16 ? sumabs_bf16x8(v[u]) : sumabs_f32x4(v[u]);
+      else acc += BF16 ? sumsq_bf16x8(v[u]) : sumsq_f32x4(v[u]);
+    }
   }
   acc = wave_sum(acc);
   if (lane == 0) gn[t] = acc;
@@ -73,7 +77,33 @@ __global__ __launch_bounds__(kScoreThreads) void pair_score_kernel(const uint4* 
   }
 }
 
+// Gradient-only criteria (section 4.7, Table 2): every pair takes its token's row score.
+__global__ __launch_bounds__(kScoreThreads) void pair_gather_kernel(const int32_t* __restrict__ tok,
+                                                                    const double* __restrict__ gs, int64_t N,
+                                                                    int T, float* __restrict__ R) {
+  const int64_t j = (int64_t)blockIdx.x * kScoreThreads + threadIdx.x;
+  if (j >= N) return;
+  const int t = tok[j];
+  R[j] = (t >= 0 && t < T) ? (float)gs[t] : 0.0f;  // out-of-range tokens score 0
+}
+
 }  // namespace
+
+lrmoe_status launch_score_gradient(const lrmoe_problem* p, bool magnitude, const void* G, const int32_t* tok,
+                                   float* R, double* gs, hipStream_t s) {
+  const bool bf16 = p->dtype == LRMOE_BF16;
+  const int gch = p->D * (bf16 ? 2 : 4) / 16;
+  if (p->T > 0) {
+    dim3 grid((unsigned)ceil_div(p->T, kScoreThreads / kWave));
+    if (bf16 && magnitude) token_sqnorm_kernel<true, true><<<grid, kScoreThreads, 0, s>>>((const uint4*)G, p->T, gch, gs);
+    else if (bf16) token_sqnorm_kernel<true, false><<<grid, kScoreThreads, 0, s>>>((const uint4*)G, p->T, gch, gs);
+    else if (magnitude) token_sqnorm_kernel<false, true><<<grid, kScoreThreads, 0, s>>>((const uint4*)G, p->T, gch, gs);
+    else token_sqnorm_kernel<false, false><<<grid, kScoreThreads, 0, s>>>((const uint4*)G, p->T, gch, gs);
+  }
+  if (p->N > 0)
+    pair_gather_kernel<<<(unsigned)ceil_div(p->N, kScoreThreads), kScoreThreads, 0, s>>>(tok, gs, p->N, p->T, R);
+  return launch_status();
+}
 
 lrmoe_status launch_score(const lrmoe_problem* p, const void* G, const void* Phi, const float* alpha,
                           const int32_t* tok, float* R, double* gn, hipStream_t s) {

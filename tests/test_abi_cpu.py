@@ -123,6 +123,23 @@ def test_workspace_size_and_host_side_rejections():
                              None) == _lib.ERR_INVALID_ARG
 
 
+def test_score_criterion_host_checks():
+    """lrmoe_score_criterion: unknown criteria, missing pointers and workspaces are refused on the
+    host; the gradient-only criteria do not need Phi or alpha (they fail only on the workspace)."""
+    lib = _lib.load()
+    p, keep = _problem()
+    fake = ctypes.c_void_p(0x1000)
+    f = lib.lrmoe_score_criterion
+    assert f(ctypes.byref(p), 3, fake, fake, fake, fake, fake, fake, 1 << 20, None) == _lib.ERR_INVALID_ARG
+    assert f(ctypes.byref(p), -1, fake, fake, fake, fake, fake, fake, 1 << 20, None) == _lib.ERR_INVALID_ARG
+    for crit in (1, 2):
+        assert f(ctypes.byref(p), crit, fake, None, None, fake, fake, None, 0, None) == _lib.ERR_WORKSPACE
+        assert f(ctypes.byref(p), crit, None, None, None, fake, fake, fake, 1 << 20, None) == _lib.ERR_INVALID_ARG
+        assert f(ctypes.byref(p), crit, fake, None, None, None, fake, fake, 1 << 20, None) == _lib.ERR_INVALID_ARG
+    # criterion 0 is lrmoe_score, which needs Phi and alpha
+    assert f(ctypes.byref(p), 0, fake, None, None, fake, fake, fake, 1 << 20, None) == _lib.ERR_INVALID_ARG
+
+
 def _gemm(p, phi_rows=None, x_rows=None, swiglu=True):
     """lrmoe_grouped_gemm_bwd with fake device pointers (only host checks can pass)."""
     fake = ctypes.c_void_p(0x1000)

@@ -59,6 +59,16 @@ def test_full_score(full):
     assert np.all(np.abs(R - ref) <= 1e-6 * ref + 1e-35)
 
 
+@pytest.mark.parametrize("criterion", ["grad_sqnorm", "grad_abs"])
+def test_full_score_gradient_only_criteria(full, criterion):
+    pr, s = full["pr"], full["s"]
+    R = lr.score(s.P, s.G, None, None, s.tok, criterion=criterion)
+    torch.cuda.synchronize()
+    R = R.cpu().numpy().astype(np.float64)
+    ref = oracle.score_gradient_only(pr.G, pr.routing.tok, "bf16", criterion)
+    assert np.all(np.abs(R - ref) <= 1e-6 * ref + 1e-35)
+
+
 def test_full_select(full):
     pr = full["pr"]
     sel = full["res"]["sel"].cpu().numpy().astype(np.int64)

@@ -92,6 +92,34 @@ def test_score(case):
     assert np.all(err <= 1e-6 * ref["R"] + 1e-35), f"{name}: max rel {np.max(err / np.maximum(ref['R'], 1e-30))}"
 
 
+@pytest.mark.parametrize("criterion", ["grad_sqnorm", "grad_abs"])
+def test_score_gradient_only_criteria(case, criterion):
+    """The gradient-only criteria of the ablation (section 4.7, Table 2) against the oracle,
+    same bound as the LRM score (fp64 sums, one f32 rounding); the selection they drive is
+    the oracle's on the same f32 scores."""
+    name, pr, s, res, ref = case
+    R = lr.score(s.P, s.G, None, None, s.tok, criterion=criterion)
+    torch.cuda.synchronize()
+    R = R.cpu().numpy().astype(np.float64)
+    R_or = oracle.score_gradient_only(pr.G, pr.routing.tok, pr.cfg.dtype, criterion)
+    err = np.abs(R - R_or)
+    assert np.all(err <= 1e-6 * R_or + 1e-35), f"{name}/{criterion}: max rel {np.max(err / np.maximum(R_or, 1e-30))}"
+    sel, _ = lr.select(s.P, lr.score(s.P, s.G, None, None, s.tok, criterion=criterion), want_keep=False)
+    torch.cuda.synchronize()
+    check_selection(sel.cpu().numpy().astype(np.int64), R_or, pr.routing.seg_off, pr.quota)
+
+
+def test_random_criterion_is_select_on_given_draws(case):
+    """The random-selection baseline of the ablation: uniform draws passed to lrmoe_select keep
+    exactly the oracle's per-expert top-q of the same draws."""
+    name, pr, s, res, ref = case
+    u = np.random.default_rng(7).random(s.P.N).astype(np.float32)
+    sel, keep = lr.select(s.P, torch.from_numpy(u).to(DEV))
+    torch.cuda.synchronize()
+    sel_or, _, _ = oracle.select(u, pr.routing.seg_off, pr.quota)
+    assert np.array_equal(sel.cpu().numpy().astype(np.int64), sel_or)
+
+
 def test_select(case):
     name, pr, s, res, ref = case
     sel = res["sel"].cpu().numpy().astype(np.int64)

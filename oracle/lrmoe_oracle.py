@@ -43,7 +43,7 @@ import numpy as np
 __all__ = [
     "InfeasibleQuota", "widen", "round_bf16", "score", "score_gradient_only", "select", "compact",
     "swiglu_expert_backward", "linear_expert_backward", "scatter_tokens", "scatter_slots",
-    "backward",
+    "backward", "ceil_quotas", "backward_bytes", "plan_quotas",
 ]
 
 
@@ -289,3 +289,62 @@ def backward(*, G, Phi, alpha, tok, slot, seg_off, quota, dtype, T, W2, X=None, 
         dW, dPhi = linear_expert_backward(cseg_off, c["Dlt"], c["PhiC"], widen(W2, dtype))
         out.update(dW2=dW, dPhi=dPhi, out=scatter_tokens(dPhi, c["ctok"], T))
     return out
+
+
+# ---------------------------------------------------------------------------- quota admission
+
+def ceil_quotas(counts, rho) -> np.ndarray:
+    """Retention quotas of one candidate ratio: q_e = min(n_e, ceil(rho * n_e)), rho taken
+    as an exact fraction (a string like "0.6", a Fraction, or an int)."""
+    from fractions import Fraction
+    import math
+    r = Fraction(rho)
+    return np.array([min(int(n), math.ceil(r * int(n))) for n in counts], dtype=np.int64)
+
+
+def backward_bytes(*, T, E, D, F, swiglu, dtype, N, K_tot, packed=False) -> int:
+    """Device bytes of the buffers one physical-compaction backward holds besides its inputs
+    (G, Phi, X, H, W1, W2, alpha, tok, slot) and its scratch: the memory that the retention
+    quotas decide, the estimate Algorithm 1's admission compares with the available HBM.
+    Listed buffer by buffer (e = bytes of the storage dtype; w = D for SwiGLU experts, F for
+    an FC2-only expert):
+      scores R f32 [N], keep flags u8 [N]; sel, ctok, cslot int32 [K_tot];
+      Dlt [K_tot x D] e; packed saved rows PhiC [K_tot x F] e (SwiGLU: XC [K_tot x D],
+      HC [K_tot x 2F] too); SwiGLU dH [K_tot x 2F] e; input gradients [K_tot x w] e;
+      weight gradients f32: dW2 [E x F x D] (SwiGLU: dW1 [E x D x 2F]); scatter output
+      f32 [T x w]."""
+    e = 2 if dtype == "bf16" else 4
+    w = D if swiglu else F
+    b = 4 * N + N
+    b += 3 * 4 * K_tot
+    b += K_tot * D * e
+    if packed:
+        b += K_tot * F * e
+        if swiglu:
+            b += K_tot * D * e + K_tot * 2 * F * e
+    if swiglu:
+        b += K_tot * 2 * F * e
+    b += K_tot * w * e
+    b += 4 * E * F * D
+    if swiglu:
+        b += 4 * E * D * 2 * F
+    b += 4 * T * w
+    return int(b)
+
+
+def plan_quotas(counts, rhos, hbm_avail, *, T, D, F, swiglu, dtype, packed=False):
+    """Algorithm 1's forward-time admission on one GPU (no replica plan and no
+    communication window to check): try the candidate ratios in decreasing order (equal
+    ratios in the order given), form their quotas, and admit the first whose
+    ``backward_bytes`` fit ``hbm_avail``. Returns (index of the admitted candidate,
+    quotas, bytes). None fits: Algorithm 1 returns Infeasible - raised as InfeasibleQuota."""
+    from fractions import Fraction
+    counts = [int(n) for n in counts]
+    order = sorted(range(len(rhos)), key=lambda i: (-Fraction(rhos[i]), i))
+    for i in order:
+        q = ceil_quotas(counts, rhos[i])
+        b = backward_bytes(T=T, E=len(counts), D=D, F=F, swiglu=swiglu, dtype=dtype, N=sum(counts),
+                           K_tot=int(q.sum()), packed=packed)
+        if b <= hbm_avail:
+            return i, q, b
+    raise InfeasibleQuota("no candidate retention ratio fits the available memory")

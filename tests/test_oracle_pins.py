@@ -177,6 +177,78 @@ def check_gradient_only_against_lrm(o, seed=5):
         o.score_gradient_only(Gb, tok, "bf16", "random")
 
 
+def check_ceil_quotas_definition(o, seed=6):
+    """q_e is the least integer >= rho * n_e, capped at n_e, for exact fractional rho."""
+    from fractions import Fraction
+    rng = _rng(seed)
+    counts = [0, 1, 2, 3, 5, 7, 10, 99, 1000] + [int(x) for x in rng.integers(0, 100000, size=20)]
+    for rho in ("0", "1", "0.6", "0.25", "0.75", "0.333", "0.999999", Fraction(2, 3), Fraction(1, 7)):
+        q = o.ceil_quotas(counts, rho)
+        r = Fraction(rho)
+        for n, k in zip(counts, q.tolist()):
+            assert 0 <= k <= n
+            assert k == n or (k >= r * n and k - 1 < r * n), (rho, n, k)
+        if r == 1:
+            assert q.tolist() == counts
+        if r == 0:
+            assert not any(q.tolist())
+
+
+def _buffer_bytes_of_outputs(o, p, packed):
+    """Bytes of the buffers the oracle's own backward returns, from their shapes and the
+    dtype each one is stored in on the device."""
+    e = 2 if p.cfg.dtype == "bf16" else 4
+    r = p.routing
+    out = o.backward(G=p.G, Phi=p.Phi, alpha=r.alpha, tok=r.tok, slot=r.slot, seg_off=r.seg_off, quota=p.quota,
+                     dtype=p.cfg.dtype, T=p.cfg.T, W2=p.W2, X=p.X, H=p.H, W1=p.W1)
+    size = lambda a: int(np.prod(np.asarray(a).shape))  # noqa: E731
+    b = 4 * size(out["R"]) + 1 * size(out["R"])          # scores, keep flags
+    b += 4 * (size(out["sel"]) + size(out["ctok"]) + size(out["cslot"]))
+    b += e * size(out["Dlt"])
+    if packed:
+        b += e * size(out["PhiC"])
+        if p.cfg.swiglu:
+            b += e * (size(out["XC"]) + size(out["HC"]))
+    if p.cfg.swiglu:
+        b += e * (size(out["dH"]) + size(out["dXC"])) + 4 * (size(out["dW1"]) + size(out["dW2"]))
+    else:
+        b += e * size(out["dPhi"]) + 4 * size(out["dW2"])
+    return b + 4 * size(out["out"])
+
+
+def check_backward_bytes_from_shapes(o):
+    """The admission's memory estimate equals the bytes of the buffers the backward really
+    produces (SwiGLU and FC2-only, bf16 and f32, packed or read in place)."""
+    for sw, dt, counts in ((True, "bf16", (5, 0, 7)), (False, "f32", (4, 6, 1)), (True, "f32", (3, 3, 3))):
+        cfg = synth.custom(T=7, K=3, E=3, D=16, F=8, counts=counts, swiglu=sw, dtype=dt, seed=21)
+        p = synth.make_problem(cfg, rho="0.6")
+        for packed in (False, True):
+            est = o.backward_bytes(T=cfg.T, E=cfg.E, D=cfg.D, F=cfg.F, swiglu=sw, dtype=dt,
+                                   N=int(p.routing.seg_off[-1]), K_tot=int(p.quota.sum()), packed=packed)
+            assert est == _buffer_bytes_of_outputs(o, p, packed), (sw, dt, packed)
+
+
+def check_plan_quotas_brute_force(o, seed=8):
+    """Admission picks the largest candidate ratio (ties: the earlier one) whose estimate fits,
+    checked against every candidate; with no candidate fitting it reports Infeasible."""
+    from fractions import Fraction
+    rng = _rng(seed)
+    dims = dict(T=300, D=64, F=48, swiglu=True, dtype="bf16")
+    counts = [int(x) for x in rng.integers(0, 200, size=6)]
+    rhos = ["0.5", "1", "0.75", "0.25", "0.75", "0.9", "0"]
+    est = [o.backward_bytes(E=len(counts), N=sum(counts), K_tot=int(o.ceil_quotas(counts, r).sum()), **dims)
+           for r in rhos]
+    for budget in sorted(set(est)) + [min(est) - 1, max(est) + 1]:
+        ok = [i for i in range(len(rhos)) if est[i] <= budget]
+        if not ok:
+            with pytest.raises(o.InfeasibleQuota):
+                o.plan_quotas(counts, rhos, budget, **dims)
+            continue
+        best = max(ok, key=lambda i: (Fraction(rhos[i]), -i))
+        i, q, b = o.plan_quotas(counts, rhos, budget, **dims)
+        assert (i, b) == (best, est[best]) and q.tolist() == o.ceil_quotas(counts, rhos[best]).tolist()
+
+
 def check_select_exhaustive(o, seed=1, ties=False):
     """Proposition 7.1: per expert, the retained set maximises the retained score sum
     among all subsets of size q_e (and the dropped set minimises Eq. 13; Eq. 16 links
@@ -373,6 +445,9 @@ ALL_CHECKS = {
     "score_is_omission_change": check_score_is_omission_change,
     "gradient_only_brute_force": check_gradient_only_brute_force,
     "gradient_only_against_lrm": check_gradient_only_against_lrm,
+    "ceil_quotas_definition": check_ceil_quotas_definition,
+    "backward_bytes_from_shapes": check_backward_bytes_from_shapes,
+    "plan_quotas_brute_force": check_plan_quotas_brute_force,
     "select_exhaustive_distinct": lambda o: check_select_exhaustive(o, ties=False),
     "select_exhaustive_ties": lambda o: check_select_exhaustive(o, seed=11, ties=True),
     "select_per_expert": check_select_per_expert,
@@ -452,6 +527,28 @@ def _gradient_only_by_pair_row(G, tok, dtype, criterion, chunk=16384):
     return oracle.score_gradient_only(G, np.arange(n) % np.asarray(G).shape[0], dtype, criterion)
 
 
+def _ceil_quotas_floor(counts, rho):
+    from fractions import Fraction
+    import math
+    r = Fraction(rho)
+    return np.array([min(int(n), math.floor(r * int(n))) for n in counts], dtype=np.int64)
+
+
+def _backward_bytes_no_dh(*, T, E, D, F, swiglu, dtype, N, K_tot, packed=False):
+    e = 2 if dtype == "bf16" else 4
+    return oracle.backward_bytes(T=T, E=E, D=D, F=F, swiglu=swiglu, dtype=dtype, N=N, K_tot=K_tot,
+                                 packed=packed) - (K_tot * 2 * F * e if swiglu else 0)
+
+
+def _plan_in_given_order(counts, rhos, hbm_avail, **kw):
+    for i, r in enumerate(rhos):
+        q = oracle.ceil_quotas(counts, r)
+        b = oracle.backward_bytes(E=len(counts), N=sum(int(n) for n in counts), K_tot=int(q.sum()), **kw)
+        if b <= hbm_avail:
+            return i, q, b
+    raise oracle.InfeasibleQuota("none")
+
+
 def _select_smallest(R, seg_off, quota):
     sel, c, tau = oracle.select(-np.asarray(R), seg_off, quota)
     return sel, c, tau
@@ -527,6 +624,9 @@ PLANTED = [
      ["gradient_only_brute_force", "gradient_only_against_lrm"]),
     ("gradient_only_ignores_token", dict(score_gradient_only=_gradient_only_by_pair_row),
      ["gradient_only_brute_force", "gradient_only_against_lrm"]),
+    ("quota_rounds_down", dict(ceil_quotas=_ceil_quotas_floor), ["ceil_quotas_definition"]),
+    ("bytes_without_dh", dict(backward_bytes=_backward_bytes_no_dh), ["backward_bytes_from_shapes"]),
+    ("plan_in_given_order", dict(plan_quotas=_plan_in_given_order), ["plan_quotas_brute_force"]),
     ("select_keeps_smallest", dict(select=_select_smallest),
      ["select_exhaustive_distinct", "fig4_worked_example", "select_per_expert"]),
     ("select_layer_wide", dict(select=_select_layer_wide), ["select_per_expert"]),

@@ -107,6 +107,30 @@ lrmoe_status lrmoe_validate(const lrmoe_problem* p, int64_t* K_tot, int64_t* cse
  * and compact mode (one buffer serves all of them; calls on one stream may share it). */
 lrmoe_status lrmoe_workspace_size(const lrmoe_problem* p, lrmoe_compact_mode mode, size_t* bytes);
 
+/* Host-only. Device bytes of the buffers one physical-compaction backward holds at p's
+ * quotas, besides its inputs (G, Phi, X, H, W1, W2, alpha, tok, slot) and the workspace:
+ *   R f32 [N], keep u8 [N]; sel, ctok, cslot int32 [K_tot]; Dlt [K_tot x D];
+ *   with packed != 0 the packed saved rows PhiC [K_tot x F] (SwiGLU: also XC [K_tot x D]
+ *   and HC [K_tot x 2F]); SwiGLU: dH [K_tot x 2F]; dIn [K_tot x w]; f32 weight gradients
+ *   dW2 [E x F x D] (SwiGLU: dW1 [E x D x 2F]); the scatter output f32 [T x w]
+ * (storage dtype where not marked; w = D for SwiGLU experts, F for FC2-only ones). This is
+ * the memory the retention quotas decide. */
+lrmoe_status lrmoe_backward_bytes(const lrmoe_problem* p, int32_t packed, size_t* bytes);
+
+/* Host-only. Quota admission on one GPU: Algorithm 1's forward-time admission (section
+ * 3.3) with a single GPU, so no replica plan and no communication window to check. The
+ * n_rho candidate ratios rho_i = rho_num[i] / rho_den[i] (0 <= rho_i <= 1, host arrays)
+ * are tried in decreasing order (equal ratios in index order); candidate i gives quotas
+ * q_e = min(n_e, ceil(rho_i n_e)) (exact integer arithmetic) and its estimate
+ * lrmoe_backward_bytes at those quotas. The first candidate whose estimate is at most
+ * hbm_avail is admitted: *chosen = i, quota_out [E] (host) = its quotas, *bytes = its
+ * estimate. p->quota is not read (may be NULL). If no candidate fits, the result is
+ * LRMOE_ERR_INFEASIBLE_QUOTA (Algorithm 1's "return Infeasible") with *chosen = -1. A ratio
+ * outside [0,1], a denominator <= 0 or n_rho < 1 is LRMOE_ERR_INVALID_ARG. */
+lrmoe_status lrmoe_plan_quotas(const lrmoe_problem* p, const int32_t* rho_num, const int32_t* rho_den,
+                               int32_t n_rho, int32_t packed, size_t hbm_avail, int32_t* chosen,
+                               int32_t* quota_out, size_t* bytes);
+
 /* Step 1 - LRM score (section 3.2, Proposition 3.1, Eq. 3; Algorithm 1's scoring step):
  *   R[j] = alpha[j]^2 * ||G[tok[j]]||^2 * ||Phi[j]||^2   for every pair j < N.
  * G [T x D] upstream gradient before the routing weight (appendix 7.1, Eq. 4-5),

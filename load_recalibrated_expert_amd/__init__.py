@@ -104,6 +104,34 @@ class Problem:
         return self.cseg_off_d if mode == COMPACT_PHYSICAL else self.seg_off_d
 
 
+def backward_bytes(p: Problem, packed=False) -> int:
+    """Device bytes of the buffers one physical-compaction backward holds at p's quotas
+    (host-only; the list is in the header, lrmoe_backward_bytes)."""
+    n = ctypes.c_size_t(0)
+    _lib.check(library().lrmoe_backward_bytes(ctypes.byref(p.c), int(bool(packed)), ctypes.byref(n)),
+               "lrmoe_backward_bytes")
+    return int(n.value)
+
+
+def plan_quotas(E, T, K, D, F, swiglu, dtype, seg_off, rhos, hbm_avail, packed=False):
+    """Quota admission on one GPU (host-only): the largest candidate ratio in ``rhos``
+    (exact decimals such as "0.6", or Fractions) whose backward buffers fit ``hbm_avail``
+    bytes. Returns (index into rhos, quotas [E] int32, bytes); raises InfeasibleQuotaError
+    when none fits (Algorithm 1's "return Infeasible")."""
+    from fractions import Fraction
+    fr = [Fraction(r) for r in rhos]
+    num = np.array([f.numerator for f in fr], dtype=np.int32)
+    den = np.array([f.denominator for f in fr], dtype=np.int32)
+    c, keep = _lib.make_problem_struct(E, T, K, D, F, swiglu, dtype, seg_off, np.zeros(E, dtype=np.int32))
+    chosen, nb = ctypes.c_int32(-1), ctypes.c_size_t(0)
+    q = np.zeros(E, dtype=np.int32)
+    I32 = ctypes.POINTER(ctypes.c_int32)
+    _lib.check(library().lrmoe_plan_quotas(ctypes.byref(c), num.ctypes.data_as(I32), den.ctypes.data_as(I32),
+                                           len(fr), int(bool(packed)), int(hbm_avail), ctypes.byref(chosen),
+                                           q.ctypes.data_as(I32), ctypes.byref(nb)), "lrmoe_plan_quotas")
+    return int(chosen.value), q, int(nb.value)
+
+
 CRITERIA = {"lrm": 0, "grad_sqnorm": 1, "grad_abs": 2}
 
 

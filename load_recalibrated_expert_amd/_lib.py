@@ -21,7 +21,8 @@ COMPACT_PHYSICAL, COMPACT_ZERO_MASKED = 0, 1
 SCATTER_TOKEN, SCATTER_SLOT = 0, 1
 
 EXPORTS = ("lrmoe_status_string", "lrmoe_version", "lrmoe_validate", "lrmoe_workspace_size",
-           "lrmoe_score", "lrmoe_score_criterion", "lrmoe_select", "lrmoe_compact", "lrmoe_grouped_gemm_bwd", "lrmoe_scatter")
+           "lrmoe_backward_bytes", "lrmoe_plan_quotas", "lrmoe_score", "lrmoe_score_criterion", "lrmoe_select",
+           "lrmoe_compact", "lrmoe_grouped_gemm_bwd", "lrmoe_scatter")
 
 
 class LrmoeError(RuntimeError):
@@ -61,6 +62,9 @@ def load() -> ctypes.CDLL:
     sigs = {
         "lrmoe_validate": [P, ctypes.POINTER(i64), ctypes.POINTER(i64)],
         "lrmoe_workspace_size": [P, ctypes.c_int, ctypes.POINTER(sz)],
+        "lrmoe_backward_bytes": [P, i32, ctypes.POINTER(sz)],
+        "lrmoe_plan_quotas": [P, ctypes.POINTER(i32), ctypes.POINTER(i32), i32, i32, sz, ctypes.POINTER(i32),
+                              ctypes.POINTER(i32), ctypes.POINTER(sz)],
         "lrmoe_score": [P, vp, vp, vp, vp, vp, vp, sz, vp],
         "lrmoe_score_criterion": [P, i32, vp, vp, vp, vp, vp, vp, sz, vp],
         "lrmoe_select": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],

@@ -48,6 +48,25 @@ size_t ws_need(const lrmoe_problem* p, lrmoe_compact_mode mode) {
   return std::max<size_t>(b, 256);
 }
 
+// Buffers of one physical-compaction backward at K_tot retained pairs (the list is in the
+// header, with lrmoe_backward_bytes).
+size_t backward_buffer_bytes(const lrmoe_problem* p, int64_t K_tot, bool packed) {
+  const size_t e = p->dtype == LRMOE_BF16 ? 2 : 4, K = (size_t)K_tot, N = (size_t)p->N;
+  const size_t D = (size_t)p->D, F = (size_t)p->F, E = (size_t)p->E, T = (size_t)p->T;
+  const bool sw = p->swiglu != 0;
+  const size_t w = sw ? D : F;
+  size_t b = N * sizeof(float) + N;            // R, keep
+  b += K * 3 * sizeof(int32_t);                // sel, ctok, cslot
+  b += K * D * e;                              // Dlt
+  if (packed) b += K * F * e + (sw ? K * D * e + K * 2 * F * e : 0);  // PhiC (XC, HC)
+  if (sw) b += K * 2 * F * e;                  // dH
+  b += K * w * e;                              // dIn
+  b += E * F * D * sizeof(float);              // dW2
+  if (sw) b += E * D * 2 * F * sizeof(float);  // dW1
+  b += T * w * sizeof(float);                  // scatter output
+  return b;
+}
+
 #define LRMOE_TRY(x)                      \
   do {                                    \
     const lrmoe_status st_ = (x);         \
@@ -79,6 +98,52 @@ lrmoe_status lrmoe_validate(const lrmoe_problem* p, int64_t* K_tot, int64_t* cse
   if (K_tot) *K_tot = k;
   if (cseg_off) std::copy(cseg.begin(), cseg.end(), cseg_off);
   return LRMOE_OK;
+}
+
+lrmoe_status lrmoe_backward_bytes(const lrmoe_problem* p, int32_t packed, size_t* bytes) {
+  if (!bytes) return LRMOE_ERR_INVALID_ARG;
+  int64_t K_tot = 0;
+  LRMOE_TRY(check_problem(p, &K_tot, nullptr));
+  *bytes = backward_buffer_bytes(p, K_tot, packed != 0);
+  return LRMOE_OK;
+}
+
+lrmoe_status lrmoe_plan_quotas(const lrmoe_problem* p, const int32_t* rho_num, const int32_t* rho_den,
+                               int32_t n_rho, int32_t packed, size_t hbm_avail, int32_t* chosen,
+                               int32_t* quota_out, size_t* bytes) {
+  if (!p || !rho_num || !rho_den || n_rho < 1 || !chosen || !quota_out || !bytes) return LRMOE_ERR_INVALID_ARG;
+  *chosen = -1;
+  for (int i = 0; i < n_rho; ++i)
+    if (rho_den[i] <= 0 || rho_num[i] < 0 || rho_num[i] > rho_den[i]) return LRMOE_ERR_INVALID_ARG;
+  if (p->E < 1 || p->E > 65535 || !p->seg_off) return LRMOE_ERR_INVALID_ARG;
+  // the problem is checked with all-zero quotas (always feasible) for everything but them
+  std::vector<int32_t> q(p->E, 0);
+  lrmoe_problem pq = *p;
+  pq.quota = q.data();
+  LRMOE_TRY(check_problem(&pq, nullptr, nullptr));
+  std::vector<int> order(n_rho);
+  for (int i = 0; i < n_rho; ++i) order[i] = i;
+  // decreasing ratio, equal ratios in index order: a/b > c/d  <=>  a*d > c*b (positive b, d)
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    return (int64_t)rho_num[a] * rho_den[b] > (int64_t)rho_num[b] * rho_den[a];
+  });
+  for (int i : order) {
+    int64_t K_tot = 0;
+    for (int e = 0; e < p->E; ++e) {
+      const int64_t n = p->seg_off[e + 1] - p->seg_off[e];
+      const int64_t c = (n * rho_num[i] + rho_den[i] - 1) / rho_den[i];  // ceil(rho n), n >= 0
+      q[e] = (int32_t)std::min(n, c);
+      K_tot += q[e];
+    }
+    const size_t b = backward_buffer_bytes(p, K_tot, packed != 0);
+    if (b <= hbm_avail) {
+      *chosen = i;
+      std::copy(q.begin(), q.end(), quota_out);
+      *bytes = b;
+      return LRMOE_OK;
+    }
+  }
+  return LRMOE_ERR_INFEASIBLE_QUOTA;
 }
 
 lrmoe_status lrmoe_workspace_size(const lrmoe_problem* p, lrmoe_compact_mode mode, size_t* bytes) {

@@ -1,0 +1,92 @@
+"""Quota admission on one GPU (host-only C ABI: lrmoe_backward_bytes, lrmoe_plan_quotas)
+against the oracle's admission (Algorithm 1's forward-time admission with a single GPU).
+Integer results, so they must agree exactly. No GPU needed."""
+import ctypes
+
+import numpy as np
+import pytest
+
+import load_recalibrated_expert_amd as lr
+import oracle
+import synth
+from load_recalibrated_expert_amd import _lib
+
+RHOS = ["1", "0.8", "0.6", "0.5", "0.25", "0.1", "0"]
+
+
+@pytest.fixture(scope="module", params=["qwen3_30b_a3b_share", "extreme_skew", "tiny"])
+def workload(request):
+    cfg = synth.CONFIGS[request.param]
+    return cfg, np.diff(synth.make_routing(cfg).seg_off).astype(np.int64)
+
+
+def _dims(cfg):
+    return dict(T=cfg.T, D=cfg.D, F=cfg.F, swiglu=bool(cfg.swiglu), dtype=cfg.dtype)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_backward_bytes_matches_oracle(workload, packed):
+    cfg, counts = workload
+    seg = np.concatenate([[0], np.cumsum(counts)])
+    for rho in RHOS:
+        q = oracle.ceil_quotas(counts, rho).astype(np.int32)
+        c, keep = _lib.make_problem_struct(cfg.E, cfg.T, cfg.K, cfg.D, cfg.F, cfg.swiglu,
+                                           _lib.BF16 if cfg.dtype == "bf16" else _lib.F32, seg, q)
+        n = ctypes.c_size_t(0)
+        assert _lib.load().lrmoe_backward_bytes(ctypes.byref(c), int(packed), ctypes.byref(n)) == _lib.OK
+        ref = oracle.backward_bytes(E=cfg.E, N=int(seg[-1]), K_tot=int(q.sum()), packed=packed, **_dims(cfg))
+        assert n.value == ref, (cfg.name, rho, packed)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_plan_quotas_matches_oracle(workload, packed):
+    cfg, counts = workload
+    seg = np.concatenate([[0], np.cumsum(counts)])
+    dt = _lib.BF16 if cfg.dtype == "bf16" else _lib.F32
+    est = [oracle.backward_bytes(E=cfg.E, N=int(seg[-1]), K_tot=int(oracle.ceil_quotas(counts, r).sum()),
+                                 packed=packed, **_dims(cfg)) for r in RHOS]
+    for budget in sorted(set(est)) + [max(est) + 1, min(est) - 1]:
+        try:
+            ref = oracle.plan_quotas(counts, RHOS, budget, packed=packed, **_dims(cfg))
+        except oracle.InfeasibleQuota:
+            with pytest.raises(_lib.InfeasibleQuotaError):
+                lr.plan_quotas(cfg.E, cfg.T, cfg.K, cfg.D, cfg.F, cfg.swiglu, dt, seg, RHOS, budget, packed=packed)
+            continue
+        i, q, b = lr.plan_quotas(cfg.E, cfg.T, cfg.K, cfg.D, cfg.F, cfg.swiglu, dt, seg, RHOS, budget, packed=packed)
+        assert (i, b) == (ref[0], ref[2])
+        assert q.tolist() == ref[1].tolist()
+
+
+def test_plan_quotas_order_ties_and_rounding():
+    """Candidates given out of order and with a duplicate; quotas use the exact ceiling
+    (0.6 * 5 = 3, where a floating-point product exceeds 3)."""
+    counts = np.array([5, 10, 0, 7], dtype=np.int64)
+    seg = np.concatenate([[0], np.cumsum(counts)])
+    rhos = ["0.3", "0.6", "0.9", "0.6"]
+    dims = dict(T=22, D=64, F=32, swiglu=True, dtype="bf16")
+    big = 1 << 40
+    i, q, b = lr.plan_quotas(4, 22, 1, 64, 32, 1, _lib.BF16, seg, rhos, big)
+    assert i == 2 and q.tolist() == [5, 9, 0, 7]
+    b06 = oracle.backward_bytes(E=4, N=22, K_tot=int(oracle.ceil_quotas(counts, "0.6").sum()), **dims)
+    i, q, b = lr.plan_quotas(4, 22, 1, 64, 32, 1, _lib.BF16, seg, rhos, b06)
+    assert i == 1 and q.tolist() == [3, 6, 0, 5] and b == b06
+
+
+def test_plan_quotas_rejects_bad_ratios():
+    seg = np.array([0, 3, 5], dtype=np.int64)
+    c, keep = _lib.make_problem_struct(2, 5, 1, 64, 32, 1, _lib.BF16, seg, np.zeros(2, dtype=np.int32))
+    I32 = ctypes.POINTER(ctypes.c_int32)
+    out_i, out_b = ctypes.c_int32(7), ctypes.c_size_t(0)
+    q = np.zeros(2, dtype=np.int32)
+    for num, den in (([1], [0]), ([3], [2]), ([-1], [2])):
+        n, d = np.array(num, dtype=np.int32), np.array(den, dtype=np.int32)
+        st = _lib.load().lrmoe_plan_quotas(ctypes.byref(c), n.ctypes.data_as(I32), d.ctypes.data_as(I32), 1, 0,
+                                           1 << 40, ctypes.byref(out_i), q.ctypes.data_as(I32), ctypes.byref(out_b))
+        assert st == _lib.ERR_INVALID_ARG
+    n, d = np.array([1], dtype=np.int32), np.array([2], dtype=np.int32)
+    st = _lib.load().lrmoe_plan_quotas(ctypes.byref(c), n.ctypes.data_as(I32), d.ctypes.data_as(I32), 0, 0,
+                                       1 << 40, ctypes.byref(out_i), q.ctypes.data_as(I32), ctypes.byref(out_b))
+    assert st == _lib.ERR_INVALID_ARG
+    st = _lib.load().lrmoe_plan_quotas(ctypes.byref(c), n.ctypes.data_as(I32), d.ctypes.data_as(I32), 1, 0,
+                                       0, ctypes.byref(out_i), q.ctypes.data_as(I32), ctypes.byref(out_b))
+    assert st == _lib.ERR_INFEASIBLE_QUOTA and out_i.value == -1

@@ -44,6 +44,7 @@ __all__ = [
     "InfeasibleQuota", "widen", "round_bf16", "score", "score_gradient_only", "select", "compact",
     "swiglu_expert_backward", "linear_expert_backward", "scatter_tokens", "scatter_slots",
     "backward", "ceil_quotas", "backward_bytes", "plan_quotas",
+    "swiglu", "expert_forward_fc1", "expert_forward_fc2",
 ]
 
 
@@ -348,3 +349,47 @@ def plan_quotas(counts, rhos, hbm_avail, *, T, D, F, swiglu, dtype, packed=False
         if b <= hbm_avail:
             return i, q, b
     raise InfeasibleQuota("no candidate retention ratio fits the available memory")
+
+
+# ---------------------------------------------------------------------------- forward and context save
+
+def swiglu(h, F: int) -> np.ndarray:
+    """phi = silu(gate) * up for rows h = [gate | up] (float64), silu(x) = x / (1 + e^-x)."""
+    h = np.asarray(h, dtype=np.float64)
+    gate, up = h[:, :F], h[:, F:]
+    return gate / (1.0 + np.exp(-gate)) * up
+
+
+def expert_forward_fc1(X, tok, seg_off, W1, dtype: str):
+    """First half of the expert forward that produces the backward's saved context
+    (Algorithm 1's FullForwardAndSaveContext; section 3.1: the forward keeps every routed
+    pair). Pair j of expert e (expert-major, j in [seg_off[e], seg_off[e+1])) computes
+    h_j = x_{tok[j]} W1[e] ([gate | up], 2F wide) and phi_j = silu(gate_j) * up_j.
+    Returns float64 (H [N, 2F], Phi [N, F]); the stored context is their bf16 (or f32)
+    rounding."""
+    X = widen(X, dtype)
+    W1 = widen(W1, dtype)
+    seg_off = np.asarray(seg_off, dtype=np.int64)
+    tok = np.asarray(tok, dtype=np.int64)
+    F = W1.shape[2] // 2
+    N = int(seg_off[-1])
+    H = np.zeros((N, 2 * F), dtype=np.float64)
+    for e in range(len(seg_off) - 1):
+        r = slice(seg_off[e], seg_off[e + 1])
+        H[r] = X[tok[r]] @ W1[e]
+    return H, swiglu(H, F)
+
+
+def expert_forward_fc2(Phi, alpha, seg_off, W2, dtype: str) -> np.ndarray:
+    """Second half: y_j = alpha_j * phi_j W2[e] for the stored phi rows (the FC2 input is
+    the saved tensor). Returns float64 [N, D]; the layer output is the token sum of these
+    rows (scatter_tokens)."""
+    P = widen(Phi, dtype)
+    W2 = widen(W2, dtype)
+    seg_off = np.asarray(seg_off, dtype=np.int64)
+    a = np.asarray(alpha, dtype=np.float64)
+    Y = np.zeros((P.shape[0], W2.shape[2]), dtype=np.float64)
+    for e in range(len(seg_off) - 1):
+        r = slice(seg_off[e], seg_off[e + 1])
+        Y[r] = a[r, None] * (P[r] @ W2[e])
+    return Y

@@ -249,6 +249,50 @@ def check_plan_quotas_brute_force(o, seed=8):
         assert (i, b) == (best, est[best]) and q.tolist() == o.ceil_quotas(counts, rhos[best]).tolist()
 
 
+def check_swiglu_closed_forms(o):
+    """silu(x) = x sigma(x): sigma(0) = 1/2, sigma(ln 3) = 3/4, sigma(-ln 3) = 1/4, and the odd
+    part silu(x) - silu(-x) = x for any x; the up half multiplies."""
+    ln3 = math.log(3.0)
+    h = np.array([[0.0, ln3, -ln3, 2.0, 5.0, -1.5, 3.0, 7.0]])  # F = 4: gate | up
+    phi = o.swiglu(h, 4)[0]
+    ref = [0.0 * 5.0, 0.75 * ln3 * -1.5, -0.25 * ln3 * 3.0]  # silu(gate_k) * up_k
+    for k in range(3):
+        assert abs(phi[k] - ref[k]) <= 1e-15 * max(1.0, abs(ref[k])), k
+    x = np.linspace(-9.0, 9.0, 37)
+    hp = np.stack([x, np.ones_like(x)], axis=1)
+    hm = np.stack([-x, np.ones_like(x)], axis=1)
+    assert np.allclose(o.swiglu(hp, 1)[:, 0] - o.swiglu(hm, 1)[:, 0], x, rtol=0, atol=1e-14)
+
+
+def check_forward_exact(o, seed=9):
+    """Exact rational brute force of both forward GEMMs on dyadic bf16 inputs: pair j of
+    expert e multiplies its token's x by W1[e] (gather through tok, weights stored [in x out])
+    and its stored phi by W2[e], scaled by its routing weight."""
+    from fractions import Fraction
+    rng = _rng(seed)
+    T, E, D, F = 4, 2, 3, 2
+    tok = np.array([2, 0, 3, 1, 2], dtype=np.int32)
+    seg = np.array([0, 2, 5], dtype=np.int64)
+    X = (rng.integers(-8, 9, size=(T, D)) / 4.0).astype(np.float32)
+    W1 = (rng.integers(-8, 9, size=(E, D, 2 * F)) / 8.0).astype(np.float32)
+    W2 = (rng.integers(-8, 9, size=(E, F, D)) / 8.0).astype(np.float32)
+    P = (rng.integers(-8, 9, size=(5, F)) / 2.0).astype(np.float32)
+    alpha = np.array([0.5, 0.25, 1.0, 0.125, 2.0], dtype=np.float32)
+    b = synth.f32_to_bf16_bits
+    H, Phi = o.expert_forward_fc1(b(X), tok, seg, b(W1), "bf16")
+    Y = o.expert_forward_fc2(b(P), alpha, seg, b(W2), "bf16")
+    for j in range(5):
+        e = 0 if j < 2 else 1
+        for c in range(2 * F):
+            ref = sum(Fraction(float(X[tok[j], d])) * Fraction(float(W1[e, d, c])) for d in range(D))
+            assert Fraction(float(H[j, c])) == ref, (j, c)
+        for d in range(D):
+            ref = Fraction(float(alpha[j])) * sum(Fraction(float(P[j, f])) * Fraction(float(W2[e, f, d]))
+                                                  for f in range(F))
+            assert Fraction(float(Y[j, d])) == ref, (j, d)
+    assert np.array_equal(Phi, o.swiglu(H, F))
+
+
 def check_select_exhaustive(o, seed=1, ties=False):
     """Proposition 7.1: per expert, the retained set maximises the retained score sum
     among all subsets of size q_e (and the dropped set minimises Eq. 13; Eq. 16 links
@@ -448,6 +492,8 @@ ALL_CHECKS = {
     "ceil_quotas_definition": check_ceil_quotas_definition,
     "backward_bytes_from_shapes": check_backward_bytes_from_shapes,
     "plan_quotas_brute_force": check_plan_quotas_brute_force,
+    "swiglu_closed_forms": check_swiglu_closed_forms,
+    "forward_exact": check_forward_exact,
     "select_exhaustive_distinct": lambda o: check_select_exhaustive(o, ties=False),
     "select_exhaustive_ties": lambda o: check_select_exhaustive(o, seed=11, ties=True),
     "select_per_expert": check_select_per_expert,
@@ -549,6 +595,19 @@ def _plan_in_given_order(counts, rhos, hbm_avail, **kw):
     raise oracle.InfeasibleQuota("none")
 
 
+def _swiglu_sigmoid_of_minus(h, F):
+    h = np.asarray(h, dtype=np.float64)
+    return h[:, :F] / (1.0 + np.exp(h[:, :F])) * h[:, F:]
+
+
+def _fc1_no_gather(X, tok, seg_off, W1, dtype):
+    return oracle.expert_forward_fc1(X, np.arange(len(tok)) % np.asarray(X).shape[0], seg_off, W1, dtype)
+
+
+def _fc2_alpha_dropped(Phi, alpha, seg_off, W2, dtype):
+    return oracle.expert_forward_fc2(Phi, np.ones_like(np.asarray(alpha)), seg_off, W2, dtype)
+
+
 def _select_smallest(R, seg_off, quota):
     sel, c, tau = oracle.select(-np.asarray(R), seg_off, quota)
     return sel, c, tau
@@ -627,6 +686,9 @@ PLANTED = [
     ("quota_rounds_down", dict(ceil_quotas=_ceil_quotas_floor), ["ceil_quotas_definition"]),
     ("bytes_without_dh", dict(backward_bytes=_backward_bytes_no_dh), ["backward_bytes_from_shapes"]),
     ("plan_in_given_order", dict(plan_quotas=_plan_in_given_order), ["plan_quotas_brute_force"]),
+    ("silu_with_sigmoid_of_minus_x", dict(swiglu=_swiglu_sigmoid_of_minus), ["swiglu_closed_forms", "forward_exact"]),
+    ("fc1_ignores_token_gather", dict(expert_forward_fc1=_fc1_no_gather), ["forward_exact"]),
+    ("fc2_drops_routing_weight", dict(expert_forward_fc2=_fc2_alpha_dropped), ["forward_exact"]),
     ("select_keeps_smallest", dict(select=_select_smallest),
      ["select_exhaustive_distinct", "fig4_worked_example", "select_per_expert"]),
     ("select_layer_wide", dict(select=_select_layer_wide), ["select_per_expert"]),

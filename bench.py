@@ -46,6 +46,9 @@ def parse():
                          "of known size, used to scale hardware byte counters)")
     ap.add_argument("--cpu-sample-frac", type=float, default=1.0,
                     help="fraction of the pairs (smallest experts first) the oracle runs on")
+    ap.add_argument("--forward", action="store_true",
+                    help="also time the forward that saves the backward's context (FC1 + SwiGLU + FC2 over all "
+                         "pairs, then the token combine); reported as an extra object, not the headline")
     ap.add_argument("--criterion", default="lrm", choices=["lrm", "grad_sqnorm", "grad_abs", "random"],
                     help="selection criterion: the LRM score (default) or an alternative of the ablation; "
                          "'random' selects on uniform draws made once on the host (no score kernel)")
@@ -304,6 +307,41 @@ def main():
             "ms_per_step": mwall / args.steps * 1e3, "retained_pairs_per_s": P.K_tot * args.steps / mwall,
             "grouped_gemm_ms": mper["grouped_gemm_bwd"], "gemm_rows": P.N, "compact_rows": P.K_tot,
             "gemm_flops": mfl, "speedup_of_compaction": (mwall / args.steps * 1e3) / ms,
+        }
+    if args.forward and cfg.swiglu and dt == "bf16":
+        fo, fev = {}, []
+        def fwd_step(timing=None):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)] if timing is not None else None
+            if ev:
+                ev[0].record()
+            f = lr.expert_forward(P, ins["X"], ins["tok"], ins["alpha"], ins["W1"], ins["W2"], out=fo)
+            fo.update(f)
+            if ev:
+                ev[1].record()
+            fo["y"] = lr.scatter(P, f["Y"], ins["tok"], ins["slot"], n_rows=P.N, out=fo.get("y"))
+            if ev:
+                ev[2].record()
+                timing.append(ev)
+        for _ in range(args.warmup):
+            fwd_step()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(args.steps):
+            fwd_step()
+        torch.cuda.synchronize()
+        fwall = time.perf_counter() - t
+        for _ in range(args.steps):
+            fwd_step(fev)
+        torch.cuda.synchronize()
+        gemm_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in fev]))
+        comb_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in fev]))
+        ffl = 6.0 * P.N * cfg.D * cfg.F  # FC1 2*N*D*2F + FC2 2*N*F*D
+        result["forward"] = {
+            "ms_per_step": fwall / args.steps * 1e3, "pairs_per_s": P.N * args.steps / fwall,
+            "expert_forward_ms": gemm_ms, "TFLOP/s": ffl / (gemm_ms * 1e-3) / 1e12,
+            "mfma_frac": ffl / (gemm_ms * 1e-3) / 1e12 / peak, "flops": ffl, "combine_ms": comb_ms,
+            "note": "FC1 with the SwiGLU forward fused, FC2 scaled by the routing weight, over all N pairs; "
+                    "then the token combine (scatter)",
         }
     if not args.no_cpu_baseline and args.criterion == "lrm":  # the oracle's backward scores with LRM
         cb = cpu_baseline(pr, args.cpu_sample_frac)

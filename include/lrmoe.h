@@ -223,6 +223,23 @@ lrmoe_status lrmoe_grouped_gemm_bwd(const lrmoe_problem* p, lrmoe_compact_mode m
                                     int32_t accumulate, void* ws, size_t ws_bytes, lrmoe_stream_t stream,
                                     lrmoe_event_t din_ready);
 
+/* The forward that produces the backward's saved context (Algorithm 1's
+ * FullForwardAndSaveContext; section 3.1: the forward keeps every routed pair). For every
+ * pair j < N, expert-major (expert e: j in [seg_off[e], seg_off[e+1])), with t = tok[j]:
+ *   H[j]   = X[t] W1[e]                    [gate | up], storage dtype [N x 2F], out
+ *   Phi[j] = silu(gate) * up               from the fp32 sums, storage dtype [N x F], out
+ *   Y[j]   = alpha[j] * (Phi[j] W2[e])     the stored Phi; storage dtype [N x D], out
+ * bf16 MFMA with fp32 accumulation, one rounding per stored value. The layer output is
+ * the token sum of the Y rows: lrmoe_scatter (TOKEN mode) with rows = Y, ctok = tok and
+ * cslot = the pairs' slots. H and Phi are the saved activations lrmoe_score, lrmoe_compact
+ * and lrmoe_grouped_gemm_bwd read. seg_off_d [E+1] int64 is the device copy of
+ * p->seg_off. SwiGLU bf16 problems only (else LRMOE_ERR_UNSUPPORTED); X must be under
+ * 2 GiB, as must each expert's W1 and W2 slice (32-bit offsets), else
+ * LRMOE_ERR_UNSUPPORTED. p's quotas are checked but not used. No workspace. */
+lrmoe_status lrmoe_expert_forward(const lrmoe_problem* p, const int64_t* seg_off_d, const void* X,
+                                  const int32_t* tok, const float* alpha, const void* W1, const void* W2,
+                                  void* H, void* Phi, void* Y, lrmoe_stream_t stream);
+
 /* Step 5 - inverse mapping (section 3.1; Algorithm 1's ScatterWithZeros).
  * rows [n_rows x width] of dtype rows_dtype; row c belongs to pair (ctok[c], cslot[c]),
  * ctok in [0,T), cslot in [0,K), each (token, slot) at most once. Rows with an

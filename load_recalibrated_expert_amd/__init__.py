@@ -223,6 +223,21 @@ def grouped_gemm_bwd(p: Problem, Dlt, PhiC, W2, XC=None, HC=None, W1=None, mode=
     return res
 
 
+def expert_forward(p: Problem, X, tok, alpha, W1, W2, out=None, stream=None):
+    """The forward that saves the backward's context: H = X[tok] W1 ([gate | up]),
+    Phi = silu(gate) * up, Y = alpha * Phi W2 (rows of the N pairs, expert-major).
+    The layer output is ``scatter(p, Y, tok, slot, n_rows=p.N)``."""
+    dt = torch.bfloat16
+    o = out or {}
+    H = o.get("H") if o.get("H") is not None else torch.empty(max(p.N, 1), 2 * p.F, dtype=dt, device=p.device)
+    Phi = o.get("Phi") if o.get("Phi") is not None else torch.empty(max(p.N, 1), p.F, dtype=dt, device=p.device)
+    Y = o.get("Y") if o.get("Y") is not None else torch.empty(max(p.N, 1), p.D, dtype=dt, device=p.device)
+    _lib.check(library().lrmoe_expert_forward(ctypes.byref(p.c), _ptr(p.seg_off_d), _ptr(X), _ptr(tok), _ptr(alpha),
+                                              _ptr(W1), _ptr(W2), _ptr(H), _ptr(Phi), _ptr(Y), _stream(stream)),
+               "lrmoe_expert_forward")
+    return {"H": H[:p.N], "Phi": Phi[:p.N], "Y": Y[:p.N]}
+
+
 def scatter(p: Problem, rows_t, ctok, cslot, n_rows=None, mode=SCATTER_TOKEN, out=None, ws=None, stream=None):
     """``ws`` defaults to the problem's workspace; a scatter running concurrently with
     another call of the same problem (on another stream) needs its own."""

@@ -22,7 +22,7 @@ SCATTER_TOKEN, SCATTER_SLOT = 0, 1
 
 EXPORTS = ("lrmoe_status_string", "lrmoe_version", "lrmoe_validate", "lrmoe_workspace_size",
            "lrmoe_backward_bytes", "lrmoe_plan_quotas", "lrmoe_score", "lrmoe_score_criterion", "lrmoe_select",
-           "lrmoe_compact", "lrmoe_grouped_gemm_bwd", "lrmoe_scatter")
+           "lrmoe_compact", "lrmoe_grouped_gemm_bwd", "lrmoe_scatter", "lrmoe_expert_forward")
 
 
 class LrmoeError(RuntimeError):
@@ -73,6 +73,7 @@ def load() -> ctypes.CDLL:
         "lrmoe_grouped_gemm_bwd": [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
                                    sz, vp, vp],
         "lrmoe_scatter": [P, ctypes.c_int, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp],
+        "lrmoe_expert_forward": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)

@@ -118,6 +118,9 @@ lrmoe_status launch_compact(const lrmoe_problem* p, int64_t rows, bool masked, c
                             void* ws, hipStream_t s);
 size_t compact_ws_bytes(const lrmoe_problem* p);
 
+lrmoe_status launch_expert_forward(const lrmoe_problem* p, const int64_t* seg_off_d, const void* X,
+                                   const int32_t* tok, const float* alpha, const void* W1, const void* W2, void* H,
+                                   void* Phi, void* Y, hipStream_t s);
 size_t gemm_ws_bytes(const lrmoe_problem* p, const int64_t* row_off_h);
 lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_off_h,
                                      const int64_t* row_off_d, const void* Dlt, const void* PhiC,

@@ -130,6 +130,23 @@ struct DmaK {
       off[j] = row < rows_valid ? (uint32_t)((row * ld + col) * 2) : kOOB;
     }
   }
+  // Tile row r is row rows[r] of the matrix at p (its rows are gathered; a mapped row outside
+  // [0, nrows) reads as zeros). The rows stay fixed along K, so the map is read once here.
+  // The byte offsets are 32-bit: the host keeps nrows * ld * 2 under 2 GiB.
+  __device__ __forceinline__ void init_rows(const uint16_t* p, int64_t ld, int rows_valid, const int32_t* rows,
+                                            int64_t nrows) {
+    r = make_rsrc(p);
+    const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int logical = (l & 7) ^ ((l >> 3) & 7);
+    col = (logical & 3) * 8;
+    wbase = w * NL * 64;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int row = (logical >> 2) * HALF + (w * NL + j) * 8 + (l >> 3);
+      const int64_t src = row < rows_valid ? (int64_t)rows[row] : -1;
+      off[j] = (src >= 0 && src < nrows) ? (uint32_t)((src * ld + col) * 2) : kOOB;
+    }
+  }
   __device__ __forceinline__ void issue_one(int j, const uint4* stage, int k0, int kend, uint32_t) const {
     const bool kok = k0 + col < kend;
     dma16(r, stage + wbase + j * 64, (kok && off[j] != kOOB) ? off[j] + (uint32_t)k0 * 2u : kOOB);
@@ -159,6 +176,25 @@ struct DmaT {
       const int c = (((pc >> 2) ^ (k & 3)) << 2) | (pc & 3);  // logical 16-byte chunk
       row[j] = k;
       off[j] = c * 8 < mn_valid ? (uint32_t)((k * ld + c * 8) * 2) : kOOB;
+    }
+  }
+  // SwiGLU pairing of a [K x 2F] weight: tile columns 0..127 are the gate columns j0..j0+127
+  // and tile columns 128..255 the matching up columns F+j0..F+j0+127; columns at or past F
+  // in either half read as zeros.
+  __device__ __forceinline__ void init_paired(const uint16_t* p, int64_t ld, int j0, int F) {
+    r = make_rsrc(p);
+    const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    wbase = w * DMA_PER_WAVE * 64;
+#pragma unroll
+    for (int j = 0; j < DMA_PER_WAVE; ++j) {
+      const int k = (w * DMA_PER_WAVE + j) * 2 + (l >> 5);
+      const int pc = l & 31;
+      const int c = (((pc >> 2) ^ (k & 3)) << 2) | (pc & 3);  // logical 16-byte chunk
+      const int t = c * 8;                                     // tile column
+      const int f = t < 128 ? j0 + t : j0 + t - 128;           // column within its half
+      const int64_t src = t < 128 ? f : (int64_t)F + f;
+      row[j] = k;
+      off[j] = f < F ? (uint32_t)((k * ld + src) * 2) : kOOB;
     }
   }
   __device__ __forceinline__ void issue_one(int j, const uint4* stage, int k0, int kend, uint32_t kstep) const {
@@ -303,7 +339,7 @@ __device__ __forceinline__ void mfma(f32x16_t& acc, const bf16x8_t& n_frag, cons
 // fences keep that order): during the first step the direct loads of stage kt+S-1 and the
 // fragments of the second step; during the second step the fragments of stage kt+1's first
 // step, so MFMAs start right after the next barrier.
-template <class C, bool TN, class LA, class LB>
+template <class C, bool TNA, bool TNB, class LA, class LB>
 __device__ __forceinline__ void gemm_mainloop(StageBufs<C>& sm, LA& la, LB& lb, int kend, uint32_t kstep_a,
                                               uint32_t kstep_b, f32x16_t (&acc)[NB][MB], int wm, int wn, int lane) {
   constexpr int NM = NB * MB, STAGES = C::STAGES, NLA = LA::NL, NLB = LB::NL;
@@ -333,9 +369,9 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs<C>& sm, LA& la, LB& lb, 
   __syncthreads();
   bf16x8_t fa[2][MB], fb[2][NB];
 #pragma unroll
-  for (int i = 0; i < MB; ++i) fa[0][i] = load_frag<TN, HA>(sm.a[0], wm * 32 * MB + i * 32, 0, lane);
+  for (int i = 0; i < MB; ++i) fa[0][i] = load_frag<TNA, HA>(sm.a[0], wm * 32 * MB + i * 32, 0, lane);
 #pragma unroll
-  for (int i = 0; i < NB; ++i) fb[0][i] = load_frag<TN, HB>(sm.b[0], wn * 32 * NB + i * 32, 0, lane);
+  for (int i = 0; i < NB; ++i) fb[0][i] = load_frag<TNB, HB>(sm.b[0], wn * 32 * NB + i * 32, 0, lane);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt % STAGES, nxt = (kt + 1) % STAGES, ldst = (kt + STAGES - 1) % STAGES;
     const int k_ld = (kt + STAGES - 1) * BK;
@@ -350,16 +386,16 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs<C>& sm, LA& la, LB& lb, 
       __builtin_amdgcn_sched_barrier(0);
       if (i < NLA) la.issue_one(i, sm.a[ldst], k_ld, kend, kstep_a);
       else if (i < NLA + NLB) lb.issue_one(i - NLA, sm.b[ldst], k_ld, kend, kstep_b);
-      if (i < MB) fa[1][i] = load_frag<TN, HA>(sm.a[cur], wm * 32 * MB + i * 32, 1, lane);
-      else if (i < MB + NB) fb[1][i - MB] = load_frag<TN, HB>(sm.b[cur], wn * 32 * NB + (i - MB) * 32, 1, lane);
+      if (i < MB) fa[1][i] = load_frag<TNA, HA>(sm.a[cur], wm * 32 * MB + i * 32, 1, lane);
+      else if (i < MB + NB) fb[1][i - MB] = load_frag<TNB, HB>(sm.b[cur], wn * 32 * NB + (i - MB) * 32, 1, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       mfma(acc[i / MB][i % MB], fb[1][i / MB], fa[1][i % MB]);
       __builtin_amdgcn_sched_barrier(0);
-      if (i < MB) fa[0][i] = load_frag<TN, HA>(sm.a[nxt], wm * 32 * MB + i * 32, 0, lane);
-      else if (i < MB + NB) fb[0][i - MB] = load_frag<TN, HB>(sm.b[nxt], wn * 32 * NB + (i - MB) * 32, 0, lane);
+      if (i < MB) fa[0][i] = load_frag<TNA, HA>(sm.a[nxt], wm * 32 * MB + i * 32, 0, lane);
+      else if (i < MB + NB) fb[0][i - MB] = load_frag<TNB, HB>(sm.b[nxt], wn * 32 * NB + (i - MB) * 32, 0, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
     la.advance(kt + STAGES);
@@ -586,7 +622,7 @@ __global__ __launch_bounds__(CfgD::NTHR) void dgrad_kernel(DgradArgs g) {
   DmaK<C::NWAVE, C::BN> lb;
   la.init(g.A + row0 * g.lda, g.lda, rows_valid);
   lb.init(g.W + (int64_t)e * g.w_estride + (int64_t)n0 * g.ldw, g.ldw, n_valid);
-  gemm_mainloop<C, false>(lds, la, lb, g.K, 0, 0, acc, wm, wn, lane);
+  gemm_mainloop<C, false, false>(lds, la, lb, g.K, 0, 0, acc, wm, wn, lane);
 
   if (EPI == EPI_SWIGLU) {
     epilogue_swiglu<C>(lds, acc, wm, wn, lane, g, row0, rows_valid, n0, n_valid);
@@ -596,6 +632,142 @@ __global__ __launch_bounds__(CfgD::NTHR) void dgrad_kernel(DgradArgs g) {
       if (tr < rows_valid && tc < n_valid) *(uint4*)(out + (row0 + tr) * g.ldo + n0 + tc) = pack_bf16x8(v);
     });
   }
+}
+
+// ---------------------------------------------------------------- forward with context save
+//
+// The expert forward that produces the backward's saved context (Algorithm 1's
+// FullForwardAndSaveContext; section 3.1 keeps every routed pair in the forward). Pair j of
+// expert e, over all N pairs in expert-major order:
+//   FC1  h_j = x_{tok[j]} W1[e]          X rows gathered through tok, W1[e] read [D x 2F]
+//   SwiGLU phi_j = silu(gate_j) * up_j   fused in the FC1 epilogue; H and Phi saved in bf16
+//   FC2  y_j = alpha_j * phi_j W2[e]     the stored phi, W2[e] read [F x D]; Y rows in bf16
+// The layer output is the token sum of the Y rows (the scatter step).
+
+struct FwdArgs {
+  const uint16_t* X;    // [T x D] token rows
+  int64_t T;
+  const int32_t* tok;   // [N] token of each pair
+  const float* alpha;   // [N] routing weights
+  const uint16_t* W1;   // [E x D x 2F]
+  const uint16_t* W2;   // [E x F x D]
+  uint16_t* H;          // [N x 2F] out
+  uint16_t* Phi;        // [N x F] out (FC1 launch) / in (FC2 launch)
+  uint16_t* Y;          // [N x D] out
+  const int64_t* row_off;
+  int E, D, F;
+  int ntn;              // N tiles per M tile: ceil(F / 128) (FC1), ceil(D / 256) (FC2)
+};
+
+// Expert, first row and rows of M tile `local / ntn` (uniform per block); false past the end.
+__device__ __forceinline__ bool fwd_tile(const FwdArgs& g, int b, int& e, int64_t& row0, int& rows_valid, int& nt) {
+  int local = b;
+  for (e = 0; e < g.E; ++e) {
+    const int64_t r0 = g.row_off[e], m = g.row_off[e + 1] - r0;
+    const int cnt = (int)((m + BM - 1) / BM) * g.ntn;
+    if (local < cnt) {
+      const int mt = local / g.ntn;
+      nt = local % g.ntn;
+      row0 = r0 + (int64_t)mt * BM;
+      rows_valid = (int)min<int64_t>(BM, m - (int64_t)mt * BM);
+      return true;
+    }
+    local -= cnt;
+  }
+  return false;
+}
+
+// FC1 tile: 256 pair rows x [128 gate | 128 up] columns j0 = 128 nt; the SwiGLU forward in the
+// epilogue, staged through LDS like epilogue_staged. A thread takes 8 gate columns of a row
+// with the matching 8 up columns and writes both to H and phi = silu(gate) * up (from the
+// fp32 sums, rounded once) to Phi.
+__global__ __launch_bounds__(NTHR) void fwd_fc1_kernel(FwdArgs g) {
+  __shared__ StageBufs<CfgW> lds;
+  int e, rows_valid, nt;
+  int64_t row0;
+  if (!fwd_tile(g, xcd_remap(blockIdx.x, gridDim.x), e, row0, rows_valid, nt)) return;  // uniform per block
+  const int j0 = nt * 128, F = g.F;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN;
+  f32x16_t acc[NB][MB];
+  zero_acc(acc);
+  DmaK<NWAVE, BM> la;
+  la.init_rows(g.X, g.D, rows_valid, g.tok + row0, g.T);
+  DmaT lb;
+  lb.init_paired(g.W1 + (int64_t)e * g.D * 2 * F, 2 * F, j0, F);
+  gemm_mainloop<CfgW, false, true>(lds, la, lb, g.D, 0, (uint32_t)(2 * F * 2), acc, wm, wn, lane);
+
+  constexpr int P = BN / 4;  // float4 per staged row
+  float4* st = reinterpret_cast<float4*>(&lds);
+  const int64_t ldh = 2 * (int64_t)F;
+#pragma unroll
+  for (int half = 0; half < WM; ++half) {
+    __syncthreads();
+    if (wm == half) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = mb * 32 + (lane & 31);
+            const int c = (wn * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5)) >> 2;
+            st[r * P + (c ^ (r & 15))] =
+                make_float4(acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
+          }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < (BM / WM) * 16 / NTHR; ++i) {
+      const int id = threadIdx.x + NTHR * i;
+      const int r = id / 16, c8 = id % 16;
+      const int tr = half * (BM / WM) + r, f = j0 + c8 * 8;
+      if (tr < rows_valid && f < F) {
+        const float4 g0 = st[r * P + ((2 * c8) ^ (r & 15))], g1 = st[r * P + ((2 * c8 + 1) ^ (r & 15))];
+        const float4 u0 = st[r * P + ((32 + 2 * c8) ^ (r & 15))], u1 = st[r * P + ((32 + 2 * c8 + 1) ^ (r & 15))];
+        const float gt[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+        const float ut[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+        float ph[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          // silu from the hardware base-2 exponential and reciprocal: x / (1 + 2^(-x log2 e))
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gt[k] * -1.44269504088896341f));
+          ph[k] = gt[k] * sg * ut[k];
+        }
+        const int64_t row = row0 + tr;
+        *(uint4*)(g.H + row * ldh + f) = pack_bf16x8(gt);
+        *(uint4*)(g.H + row * ldh + F + f) = pack_bf16x8(ut);
+        *(uint4*)(g.Phi + row * F + f) = pack_bf16x8(ph);
+      }
+    }
+  }
+}
+
+// FC2 tile: 256 pair rows x 256 output columns n0 = 256 nt; rows scaled by their routing
+// weight in the epilogue.
+__global__ __launch_bounds__(NTHR) void fwd_fc2_kernel(FwdArgs g) {
+  __shared__ StageBufs<CfgW> lds;
+  int e, rows_valid, nt;
+  int64_t row0;
+  if (!fwd_tile(g, xcd_remap(blockIdx.x, gridDim.x), e, row0, rows_valid, nt)) return;  // uniform per block
+  const int n0 = nt * BN, n_valid = min(BN, g.D - n0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN;
+  f32x16_t acc[NB][MB];
+  zero_acc(acc);
+  DmaK<NWAVE, BM> la;
+  la.init(g.Phi + row0 * g.F, g.F, rows_valid);
+  DmaT lb;
+  lb.init(g.W2 + (int64_t)e * g.F * g.D + n0, g.D, n_valid);
+  gemm_mainloop<CfgW, false, true>(lds, la, lb, g.F, 0, (uint32_t)(g.D * 2), acc, wm, wn, lane);
+  uint16_t* __restrict__ y = g.Y;
+  const float* __restrict__ alpha = g.alpha;
+  const int D = g.D;
+  epilogue_staged<CfgW>(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
+    if (tr < rows_valid && tc < n_valid) {
+      const float a = alpha[row0 + tr];
+      const float w[8] = {a * v[0], a * v[1], a * v[2], a * v[3], a * v[4], a * v[5], a * v[6], a * v[7]};
+      *(uint4*)(y + (row0 + tr) * D + n0 + tc) = pack_bf16x8(w);
+    }
+  });
 }
 
 // ---------------------------------------------------------------- weight-gradient kernels
@@ -718,11 +890,11 @@ __global__ __launch_bounds__(NTHR) void wgrad_kernel(WgradArgs g) {
   if ((G0 || G1) && (ty == 0 ? G0 : G1)) {
     DmaTG la;
     la.init(T.A + m0, T.lda, m_valid, T.a_rows + r0 + k_begin, klen, T.a_nrows);
-    gemm_mainloop<CfgW, true>(lds, la, lb, klen, 0, (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
+    gemm_mainloop<CfgW, true, true>(lds, la, lb, klen, 0, (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
   } else {
     DmaT la;
     la.init(T.A + (r0 + k_begin) * T.lda + m0, T.lda, m_valid);
-    gemm_mainloop<CfgW, true>(lds, la, lb, klen, (uint32_t)(T.lda * 2), (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
+    gemm_mainloop<CfgW, true, true>(lds, la, lb, klen, (uint32_t)(T.lda * 2), (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
   }
 
   if (s > 1) {
@@ -967,6 +1139,33 @@ int64_t wgrad_xcd_ranges(const lrmoe_problem* p, const int64_t* row_off_h, int (
 }
 
 }  // namespace
+
+lrmoe_status launch_expert_forward(const lrmoe_problem* p, const int64_t* seg_off_d, const void* X,
+                                   const int32_t* tok, const float* alpha, const void* W1, const void* W2, void* H,
+                                   void* Phi, void* Y, hipStream_t s) {
+  int64_t mtiles = 0;
+  for (int e = 0; e < p->E; ++e) mtiles += ceil_div(p->seg_off[e + 1] - p->seg_off[e], BM);
+  if (mtiles == 0) return LRMOE_OK;
+  FwdArgs g{};
+  g.X = (const uint16_t*)X;
+  g.T = p->T;
+  g.tok = tok;
+  g.alpha = alpha;
+  g.W1 = (const uint16_t*)W1;
+  g.W2 = (const uint16_t*)W2;
+  g.H = (uint16_t*)H;
+  g.Phi = (uint16_t*)Phi;
+  g.Y = (uint16_t*)Y;
+  g.row_off = seg_off_d;
+  g.E = p->E;
+  g.D = p->D;
+  g.F = p->F;
+  g.ntn = (int)ceil_div(p->F, 128);
+  fwd_fc1_kernel<<<(unsigned)(mtiles * g.ntn), NTHR, 0, s>>>(g);
+  g.ntn = (int)ceil_div(p->D, BN);
+  fwd_fc2_kernel<<<(unsigned)(mtiles * g.ntn), NTHR, 0, s>>>(g);
+  return launch_status();
+}
 
 size_t gemm_ws_bytes(const lrmoe_problem* p, const int64_t* row_off_h) {
   if (p->dtype != LRMOE_BF16) return 0;

@@ -175,6 +175,19 @@ lrmoe_status lrmoe_score_criterion(const lrmoe_problem* p, lrmoe_criterion crite
                                (hipStream_t)stream);
 }
 
+lrmoe_status lrmoe_expert_forward(const lrmoe_problem* p, const int64_t* seg_off_d, const void* X,
+                                  const int32_t* tok, const float* alpha, const void* W1, const void* W2,
+                                  void* H, void* Phi, void* Y, lrmoe_stream_t stream) {
+  LRMOE_TRY(check_problem(p, nullptr, nullptr));
+  if (p->dtype != LRMOE_BF16 || p->swiglu != 1) return LRMOE_ERR_UNSUPPORTED;
+  if (p->N == 0) return LRMOE_OK;
+  if (!seg_off_d || !X || !tok || !alpha || !W1 || !W2 || !H || !Phi || !Y) return LRMOE_ERR_INVALID_ARG;
+  const int64_t lim = (int64_t)1 << 31;
+  if ((int64_t)p->T * p->D * 2 >= lim || (int64_t)p->D * 2 * p->F * 2 >= lim || (int64_t)p->F * p->D * 2 >= lim)
+    return LRMOE_ERR_UNSUPPORTED;
+  return launch_expert_forward(p, seg_off_d, X, tok, alpha, W1, W2, H, Phi, Y, (hipStream_t)stream);
+}
+
 lrmoe_status lrmoe_select(const lrmoe_problem* p, const float* R, const int64_t* seg_off_d,
                           const int32_t* quota_d, const int64_t* cseg_off_d, int32_t* sel, uint8_t* keep,
                           void* ws, size_t ws_bytes, lrmoe_stream_t stream) {

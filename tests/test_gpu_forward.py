@@ -97,3 +97,37 @@ def test_forward_rejects_unsupported():
     s = Staged(pr)
     with pytest.raises(lr.LrmoeError):
         lr.expert_forward(s.P, s.X, s.tok, s.alpha, s.W1, s.W2)
+
+
+@pytest.mark.parametrize("name", ["qwen3_30b_a3b_share", "glm45_106b_a12b_share"])
+def test_forward_full_size_sampled(name):
+    """Full-size workload, the launch bench.py --forward times: 96 sampled pairs (the first
+    and last of every expert plus random ones) checked row by row against the oracle."""
+    log(f"forward full size {name}: generating")
+    pr = synth.make_problem(name)
+    s = Staged(pr)
+    out = lr.expert_forward(s.P, s.X, s.tok, s.alpha, s.W1, s.W2)
+    torch.cuda.synchronize()
+    r = pr.routing
+    seg = r.seg_off
+    rng = np.random.default_rng(5)
+    pick = set(rng.integers(0, int(seg[-1]), size=64).tolist())
+    for e in range(pr.cfg.E):
+        if seg[e + 1] > seg[e]:
+            pick.update((int(seg[e]), int(seg[e + 1]) - 1))
+    pick = np.array(sorted(pick), dtype=np.int64)
+    e_of = np.searchsorted(seg, pick, side="right") - 1
+    log(f"forward full size {name}: checking {len(pick)} pairs")
+    H = as_f64(out["H"][torch.from_numpy(pick).to(DEV)])
+    Phi_bits = bits(out["Phi"][torch.from_numpy(pick).to(DEV)])
+    Y = as_f64(out["Y"][torch.from_numpy(pick).to(DEV)])
+    X = oracle.widen(pr.X, "bf16")
+    F = pr.cfg.F
+    H_ref = np.stack([X[r.tok[j]] @ oracle.widen(pr.W1[e], "bf16") for j, e in zip(pick, e_of)])
+    _close_rows(H, H_ref)
+    _close_rows(oracle.widen(Phi_bits, "bf16"), oracle.swiglu(H_ref, F))
+    Y_ref = np.stack([float(r.alpha[j]) * (oracle.widen(Phi_bits[i], "bf16") @ oracle.widen(pr.W2[e], "bf16"))
+                      for i, (j, e) in enumerate(zip(pick, e_of))])
+    _close_rows(Y, Y_ref)
+    del s, out
+    torch.cuda.empty_cache()

@@ -140,6 +140,25 @@ def test_score_criterion_host_checks():
     assert f(ctypes.byref(p), 0, fake, None, None, fake, fake, fake, 1 << 20, None) == _lib.ERR_INVALID_ARG
 
 
+def test_expert_forward_host_checks():
+    """lrmoe_expert_forward: SwiGLU bf16 only, every pointer required when there are pairs,
+    matrices too large for 32-bit offsets refused - all on the host, before any launch."""
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    f = lib.lrmoe_expert_forward
+    p, keep = _problem(dtype=_lib.F32)
+    assert f(ctypes.byref(p), *([fake] * 9), None) == _lib.ERR_UNSUPPORTED
+    p, keep = _problem(swiglu=0)
+    assert f(ctypes.byref(p), *([fake] * 9), None) == _lib.ERR_UNSUPPORTED
+    p, keep = _problem()
+    for i in range(9):
+        args = [fake] * 9
+        args[i] = None
+        assert f(ctypes.byref(p), *args, None) == _lib.ERR_INVALID_ARG, i
+    big, keep2 = _problem(T=600000, D=2048, counts=(5, 0, 7))
+    assert f(ctypes.byref(big), *([fake] * 9), None) == _lib.ERR_UNSUPPORTED  # X is 2.3 GiB
+
+
 def _gemm(p, phi_rows=None, x_rows=None, swiglu=True):
     """lrmoe_grouped_gemm_bwd with fake device pointers (only host checks can pass)."""
     fake = ctypes.c_void_p(0x1000)

@@ -62,6 +62,13 @@ SMALL = {
     # rows wider than any register-held compaction (D = 4160 > 512 16-byte chunks)
     "widest_rows": dict(cfg=synth.custom("widest_rows", T=60, K=2, E=2, D=4160, F=64, counts=(70, 40),
                                          seed=21), rho="0.5"),
+    # one expert and top-1 routing: every token holds exactly one pair
+    "one_expert_top1": dict(cfg=synth.custom("one_expert_top1", T=700, K=1, E=1, D=192, F=96, counts=(700,),
+                                             seed=23), rho="0.6"),
+    # more experts than the weight-gradient plan block has threads (1100 > 512), most of
+    # them holding a handful of pairs and every fifteenth none
+    "experts_1100": dict(cfg=synth.custom("experts_1100", T=2000, K=4, E=1100, D=128, F=64,
+                                          counts=tuple((7 * e) % 15 for e in range(1100)), seed=24), rho="0.5"),
 }
 
 

@@ -4,7 +4,8 @@ The weight-gradient GEMM reads the expert input X in place, through the packed r
 token map, with 32-bit byte offsets; the library accepts that while T * D * 2 < 2^31 and
 rejects larger X (unsupported). Here T = 2^20 - 1 and D = 1024, so X and G are
 2^31 - 2048 bytes each and the gathered rows of the last tokens sit just under the limit.
-The token-order scatter writes a [T x D] fp32 output of 4 GiB, past 32-bit byte offsets.
+The forward's FC1 launch gathers X the same way. The token-order scatter writes a
+[T x D] fp32 output of 4 GiB, past 32-bit byte offsets.
 
 Only a few thousand pairs are routed. Their tokens' rows of G and X are drawn from the
 seeded generator; every other row is zero and enters no result. The oracle runs on the
@@ -61,13 +62,14 @@ def limit():
     log("address limit: oracle on the routed tokens")
     ref = oracle.backward(G=G_r, Phi=Phi, alpha=r.alpha, tok=tok_r, slot=r.slot, seg_off=r.seg_off, quota=quota,
                           dtype="bf16", T=Tr, W2=W2, X=X_r, H=H, W1=W1)
-    yield dict(r=r, toks=toks, toks_d=toks_d, quota=quota, res=res, ref=ref, E=E)
+    yield dict(r=r, toks=toks, toks_d=toks_d, quota=quota, res=res, ref=ref, E=E, P=P, X=X, X_r=X_r, tok_r=tok_r,
+               W1=W1, W2=W2)
     del res, G, X
     torch.cuda.empty_cache()
 
 
 def test_limit_inputs_reach_the_limit(limit):
-    # the last tokens are routed, so the in-place gather reads within 2 KiB of the limit
+    # the last tokens are routed, so the in-place gather reads within 1 MiB of the limit
     assert (int(limit["toks"][-1]) + 1) * D * 2 > (1 << 31) - (1 << 20)
     assert T * D * 2 < (1 << 31)
 
@@ -115,3 +117,22 @@ def test_limit_scatter(limit):
     for t0 in range(0, T, 1 << 17):
         nonzero += int((out[t0:t0 + (1 << 17)] != 0).any(dim=1).sum())
     assert nonzero == int(np.count_nonzero(np.abs(ref["out"]).sum(axis=1)))
+
+
+def _close_rows(got, ref, rel=2.0 ** -8, floor=1e-4):
+    rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
+    assert np.all(np.abs(got - ref) <= rel * np.abs(ref) + floor * rms)
+
+
+def test_limit_forward(limit):
+    """The forward that saves the context, gathering X rows up to the last routed token:
+    per element within one bf16 rounding of the oracle (as in the forward parity cases)."""
+    r, P = limit["r"], limit["P"]
+    out = lr.expert_forward(P, limit["X"], torch.from_numpy(r.tok).to(DEV), torch.from_numpy(r.alpha).to(DEV),
+                            to_dev(limit["W1"], "bf16"), to_dev(limit["W2"], "bf16"))
+    torch.cuda.synchronize()
+    H_or, Phi_or = oracle.expert_forward_fc1(limit["X_r"], limit["tok_r"], r.seg_off, limit["W1"], "bf16")
+    _close_rows(as_f64(out["H"]), H_or)
+    _close_rows(as_f64(out["Phi"]), Phi_or)
+    Y_or = oracle.expert_forward_fc2(bits(out["Phi"]), r.alpha, r.seg_off, limit["W2"], "bf16")
+    _close_rows(as_f64(out["Y"]), Y_or)

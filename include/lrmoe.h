@@ -14,6 +14,14 @@
  *   lrmoe_grouped_gemm_bwd variable-size grouped GEMMs        (section 3.4)
  *   lrmoe_scatter          inverse mapping to token order     (section 3.1)
  *
+ * Beside the path:
+ *
+ *   lrmoe_score_criterion  the ablation's gradient-only scores (section 4.7, Table 2)
+ *   lrmoe_expert_forward   the forward that saves the backward's context
+ *                          (Algorithm 1, FullForwardAndSaveContext)
+ *   lrmoe_backward_bytes,  host-only: the device bytes a backward holds, and quota
+ *   lrmoe_plan_quotas      admission on one GPU (Algorithm 1's admission, section 3.3)
+ *
  * Conventions shared by every entry point
  * ---------------------------------------
  * - Pairs are stored expert-major: expert e owns pair rows [seg_off[e], seg_off[e+1]).

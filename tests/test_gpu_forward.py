@@ -19,9 +19,9 @@ import load_recalibrated_expert_amd as lr
 import oracle
 import synth
 
-pytestmark = pytest.mark.gpu
+from gpu_util import DEV, Staged, as_f64, bits, log, rel_fro
 
-from gpu_util import DEV, Staged, as_f64, bits, log, rel_fro, to_dev  # noqa: E402
+pytestmark = pytest.mark.gpu
 
 CASES = {
     "ragged": synth.custom("fwd_ragged", T=600, K=4, E=6, D=512, F=384, counts=(700, 0, 513, 300, 257, 1), seed=31),

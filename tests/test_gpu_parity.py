@@ -22,12 +22,9 @@ import load_recalibrated_expert_amd as lr
 import oracle
 import synth
 
+from gpu_util import DEV, Staged, as_f64, bits, check_selection, log, rel_fro
+
 pytestmark = pytest.mark.gpu
-
-if not torch.cuda.is_available():  # pragma: no cover - collected on CPU, skipped by marker there
-    pass
-
-from gpu_util import DEV, Staged, as_f64, bits, check_selection, log, rel_fro, to_dev  # noqa: E402
 
 SMALL = {
     "swiglu_ragged": dict(cfg=synth.custom("swiglu_ragged", T=600, K=4, E=6, D=512, F=384,

@@ -142,7 +142,34 @@ def cpu_baseline(pr, frac):
     return {"value": kt / dt, "unit": "pairs/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{len(chosen)} smallest of {cfg.E} experts: {tot} pairs, {kt} retained, full T={cfg.T} token "
                       f"rows; all five steps in fp64 ({dt:.1f} s)",
-            "seconds": dt, "retained_pairs": kt, "_out": out}
+            "seconds": dt, "retained_pairs": kt, "experts": len(chosen), "_out": out}
+
+
+def parity(np, bufs, ref, swiglu):
+    """Agreement of the last timed step's outputs with the oracle run of the CPU baseline
+    when that run covered the whole workload (same inputs), next to the bounds the parity
+    tests hold them to."""
+    def f64(t):
+        return t.detach().double().cpu().numpy()
+
+    def rel(a, b):
+        d = float(np.linalg.norm(b))
+        return float(np.linalg.norm(a - b)) / (d if d > 0 else 1.0)
+
+    R = f64(bufs["R"])
+    g = bufs["g"]
+    dW = [rel(a, b) for a, b in zip(f64(g["dW2"]), ref["dW2"])]
+    if swiglu:
+        dW += [rel(a, b) for a, b in zip(f64(g["dW1"]), ref["dW1"])]
+    return {
+        "against": "the cpu_baseline oracle run (whole workload, same inputs)",
+        "score_max_rel": float(np.max(np.abs(R - ref["R"]) / np.maximum(ref["R"], 1e-30))),
+        "selection_identical": bool(np.array_equal(bufs["sel"].cpu().numpy().astype(np.int64), ref["sel"])),
+        "weight_grad_max_rel_fro": max(dW),
+        "input_grad_rel_fro": rel(f64(g["dIn"]), ref["dXC" if swiglu else "dPhi"]),
+        "scatter_rel_fro": rel(f64(bufs["out"]), ref["out"]),
+        "bounds": {"score_max_rel": 1e-6, "rel_fro": 5e-3},
+    }
 
 
 def main():
@@ -266,9 +293,9 @@ def main():
         per = {n: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in timing])) for i, n in enumerate(names)}
         if overlap:
             per["scatter"] = float(np.mean([ev[6].elapsed_time(ev[7]) for ev in timing]))
-        return wall, per
+        return wall, per, bufs
 
-    wall, per = measure(lr.COMPACT_PHYSICAL)
+    wall, per, phys_bufs = measure(lr.COMPACT_PHYSICAL)
     ms = wall / args.steps * 1e3
     value = P.K_tot * args.steps / wall
     bytes_ = algorithmic_bytes(cfg, P.N, P.K_tot, packed=args.packed, criterion=args.criterion)
@@ -301,7 +328,7 @@ def main():
         "kernels": kernels,
     }
     if not args.no_masked:
-        mwall, mper = measure(lr.COMPACT_ZERO_MASKED)
+        mwall, mper, _ = measure(lr.COMPACT_ZERO_MASKED)
         mfl = gemm_flops(cfg, P.N)
         result["masked_baseline"] = {
             "ms_per_step": mwall / args.steps * 1e3, "retained_pairs_per_s": P.K_tot * args.steps / mwall,
@@ -345,8 +372,10 @@ def main():
         }
     if not args.no_cpu_baseline and args.criterion == "lrm":  # the oracle's backward scores with LRM
         cb = cpu_baseline(pr, args.cpu_sample_frac)
-        cb.pop("_out", None)
+        ref = cb.pop("_out", None)
         result["cpu_baseline"] = {k: cb[k] for k in ("value", "unit", "cores", "kind", "sample")}
+        if cb["experts"] == cfg.E:
+            result["parity"] = parity(np, phys_bufs, ref, cfg.swiglu)
     print(json.dumps(result), flush=True)
 
 

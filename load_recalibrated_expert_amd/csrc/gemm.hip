@@ -38,28 +38,35 @@ typedef int v4i_t __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr int BM = 256, BK = 32;
-// Block tile configuration: every wavefront owns a 128 x 64 sub-tile held as 2 x 4 MFMA
-// accumulators (128 registers), on a 2 x WN grid of wavefronts, two wavefronts per SIMD.
-// Both GEMM kinds use one block of 8 wavefronts per CU, 256 x 256 tiles and four 32 KB
-// stages. (Two blocks of 4 wavefronts per CU with 256 x 128 tiles and three 24 KB stages
-// each, so that one block's epilogue overlaps the other's MFMAs, ran the data gradients 7%
-// slower: with one stage less, each direct load has a single K step to land.)
+// Block tile configuration: a 256 x BN output tile per block on a 2 x WN grid of
+// wavefronts; each wavefront owns a 128 x (BN / WN) sub-tile held as MB x NB MFMA
+// accumulators of 32 x 32. Eight wavefronts (two per SIMD) hold 128 x 64 sub-tiles in 128
+// VGPRs each; four wavefronts (one per SIMD) hold 128 x 128 sub-tiles in 256 accumulation
+// registers, which reads a third fewer LDS bytes per MFMA. K advances 32 per stage through
+// STAGES LDS stages of 32 KB. (Two blocks of 4 wavefronts per CU with 256 x 128 tiles and
+// three 24 KB stages each, so that one block's epilogue overlaps the other's MFMAs, ran the
+// data gradients 7% slower: with one stage less, each direct load has a single K step to land.)
 template <int NWAVE_, int BN_, int STAGES_>
 struct TileCfg {
   static constexpr int NWAVE = NWAVE_, NTHR = NWAVE_ * 64, BN = BN_, STAGES = STAGES_;
   static constexpr int WM = 2, WN = NWAVE_ / 2;  // wave grid over the tile (M x N)
-  static constexpr int MB = 4, NB = 2;           // 32-wide MFMA blocks per wavefront
+  static constexpr int MB = BM / WM / 32, NB = BN_ / WN / 32;  // 32-wide MFMA blocks per wavefront
+  static constexpr int NL = BM * BK * 2 / 1024 / NWAVE_;  // 1 KB direct loads per wave per 256-row operand
   static constexpr int A_U4 = BM * BK * 2 / 16, B_U4 = BN_ * BK * 2 / 16;  // uint4 per stage
   static_assert(WN * NB * 32 == BN_ && WM * MB * 32 == BM, "wave tiles cover the block tile");
 };
-using CfgW = TileCfg<8, 256, 4>;  // weight gradients
+using CfgW = TileCfg<8, 256, 4>;  // weight gradients and the forward
 using CfgD = TileCfg<8, 256, 4>;  // data gradients
-// the weight-gradient configuration, also used by the host side and the small kernels
-constexpr int BN = CfgW::BN, STAGES = CfgW::STAGES, NWAVE = CfgW::NWAVE, NTHR = CfgW::NTHR;
-constexpr int WN = CfgW::WN, WM = CfgW::WM, NB = CfgW::NB, MB = CfgW::MB;
-constexpr int DMA_PER_WAVE = BM * BK * 2 / 1024 / NWAVE;  // 1 KB direct loads per operand per stage
+// the weight-gradient configuration, also used by the host side
+constexpr int BN = CfgW::BN, STAGES = CfgW::STAGES;
+// threads of the small kernels (plan, split-K reduction, f32 path)
+constexpr int kAuxThr = 512;
 constexpr int64_t kKcMax = 12288;          // max packed rows per weight-gradient chunk
 constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past num_records: the load returns 0
+
+// Kernel attributes of a block of C::NWAVE wavefronts: with one wavefront per SIMD the
+// wavefront may hold 512 registers (256 of them accumulation registers).
+#define LRMOE_GEMM_ATTR(C) __launch_bounds__(C::NTHR) __attribute__((amdgpu_waves_per_eu(C::NWAVE / 4, C::NWAVE / 4)))
 
 __device__ __forceinline__ int xcd_remap(int b, int n) {
   const int x = b & 7, i = b >> 3;
@@ -156,22 +163,23 @@ struct DmaK {
   __device__ __forceinline__ void advance(int) {}
 };
 
-// Direct-to-LDS loader of a row-major-in-K operand. A 1 KB direct load fills 2 K rows;
-// wave w issues loads j covering rows 2 (w*DMA_PER_WAVE + j) + l/32, and lane l fetches the
-// chunk that belongs in 16-byte slot l % 32 of its row.
+// Direct-to-LDS loader of a row-major-in-K operand, NL_ 1 KB loads per wavefront per stage.
+// A 1 KB direct load fills 2 K rows; wave w issues loads j covering rows 2 (w*NL + j) + l/32,
+// and lane l fetches the chunk that belongs in 16-byte slot l % 32 of its row.
+template <int NL_>
 struct DmaT {
-  static constexpr int NL = DMA_PER_WAVE;
+  static constexpr int NL = NL_;
   rsrc_t r;
-  uint32_t off[DMA_PER_WAVE];
-  int row[DMA_PER_WAVE];
+  uint32_t off[NL];
+  int row[NL];
   int wbase;
   __device__ __forceinline__ void init(const uint16_t* p, int64_t ld, int mn_valid) {
     r = make_rsrc(p);
     const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    wbase = w * DMA_PER_WAVE * 64;
+    wbase = w * NL * 64;
 #pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; ++j) {
-      const int k = (w * DMA_PER_WAVE + j) * 2 + (l >> 5);
+    for (int j = 0; j < NL; ++j) {
+      const int k = (w * NL + j) * 2 + (l >> 5);
       const int pc = l & 31;
       const int c = (((pc >> 2) ^ (k & 3)) << 2) | (pc & 3);  // logical 16-byte chunk
       row[j] = k;
@@ -184,10 +192,10 @@ struct DmaT {
   __device__ __forceinline__ void init_paired(const uint16_t* p, int64_t ld, int j0, int F) {
     r = make_rsrc(p);
     const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    wbase = w * DMA_PER_WAVE * 64;
+    wbase = w * NL * 64;
 #pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; ++j) {
-      const int k = (w * DMA_PER_WAVE + j) * 2 + (l >> 5);
+    for (int j = 0; j < NL; ++j) {
+      const int k = (w * NL + j) * 2 + (l >> 5);
       const int pc = l & 31;
       const int c = (((pc >> 2) ^ (k & 3)) << 2) | (pc & 3);  // logical 16-byte chunk
       const int t = c * 8;                                     // tile column
@@ -210,25 +218,25 @@ typedef __attribute__((address_space(4))) const int32_t const_i32_t;
 // The same operand with gathered K rows: K row k of the item is row idx[k] of the matrix
 // (saved activations read in place instead of packed). A lane's 16-byte chunk sits at
 // row * pitch + its column offset, so the buffer resource spans the whole matrix (under
-// 2 GiB; the host checks). Rows outside [0, nrows) read as zeros. A wavefront needs 4 row
-// indices per stage, rows 4w + 2j + h for its loads j = 0, 1 and halves h = 0, 1. It reads
+// 2 GiB; the host checks). Rows outside [0, nrows) read as zeros. A wavefront needs 2 NL row
+// indices per stage, rows 2 (w NL + j) + h for its loads j < NL and halves h = 0, 1. It reads
 // them with scalar loads (the index array is constant during the kernel), issued at the top
 // of the loop iteration whose end turns them into the load offsets of a later stage. Scalar
 // loads are not counted by the vector-memory counter whose fixed counts the K loop waits
 // on, and the wait for them falls together with the loop's wait for its own LDS reads.
 // Reads are clamped to [0, klen) so they never leave the item's part of the index array.
+template <int NL_>
 struct DmaTG {
-  static constexpr int NL = DMA_PER_WAVE;
+  static constexpr int NL = NL_;
   rsrc_t r;                        // the matrix
   const_i32_t* idx;                // the item's row indices
-  uint32_t coff[DMA_PER_WAVE];     // column offset in bytes, or kOOB past the tile's columns
-  int row[DMA_PER_WAVE];           // K row within a stage
+  uint32_t coff[NL];               // column offset in bytes, or kOOB past the tile's columns
+  int row[NL];                     // K row within a stage
   int wbase, w, h;
   uint32_t pitch, nrows;
   int klen;
-  int32_t e[4];                    // indices of rows 4w .. 4w+3 of the stage being prepared
-  uint32_t off[DMA_PER_WAVE];      // byte offsets of the stage to issue next (kOOB: zeros)
-  static_assert(DMA_PER_WAVE == 2, "index layout assumes two direct loads per wavefront");
+  int32_t e[2 * NL];               // indices of rows 2 w NL .. 2 w NL + 2 NL - 1 of the stage being prepared
+  uint32_t off[NL];                // byte offsets of the stage to issue next (kOOB: zeros)
   __device__ __forceinline__ void init(const uint16_t* p, int64_t ld, int mn_valid, const int32_t* idx_, int klen_,
                                        int64_t nrows_) {
     r = make_rsrc(p);
@@ -239,10 +247,10 @@ struct DmaTG {
     const int lane = threadIdx.x & 63;
     w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     h = lane >> 5;
-    wbase = w * DMA_PER_WAVE * 64;
+    wbase = w * NL * 64;
 #pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; ++j) {
-      const int k = (w * DMA_PER_WAVE + j) * 2 + h;
+    for (int j = 0; j < NL; ++j) {
+      const int k = (w * NL + j) * 2 + h;
       const int pc = lane & 31;
       const int c = (((pc >> 2) ^ (k & 3)) << 2) | (pc & 3);
       row[j] = k;
@@ -252,23 +260,22 @@ struct DmaTG {
   }
   __device__ __forceinline__ void load_indices(int s) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) e[i] = idx[min(s * BK + 4 * w + i, klen - 1)];
+    for (int i = 0; i < 2 * NL; ++i) e[i] = idx[min(s * BK + 2 * NL * w + i, klen - 1)];
   }
   __device__ __forceinline__ void start() {
     load_indices(0);
     advance(0);
   }
-  // at the top of loop iteration kt, whose end prepares stage kt + STAGES
-  __device__ __forceinline__ void fetch(int kt) { load_indices(kt + STAGES); }
-  // stage s's load offsets from its indices (loaded by load_indices(s)), computed ahead (at
-  // the end of the previous loop iteration, where the wavefront waits anyway) so that issuing
-  // the loads costs no arithmetic
+  // the indices of stage s (scalar loads; advance(s) turns them into load offsets)
+  __device__ __forceinline__ void fetch(int s) { load_indices(s); }
+  // stage s's load offsets from its indices (loaded by fetch(s)), computed ahead, where the
+  // wavefront waits anyway, so that issuing the loads costs no arithmetic
   __device__ __forceinline__ void advance(int s) {
-    const int32_t mrow[DMA_PER_WAVE] = {h ? e[1] : e[0], h ? e[3] : e[2]};
 #pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; ++j) {
-      const bool ok = s * BK + row[j] < klen && (uint32_t)mrow[j] < nrows && coff[j] != kOOB;
-      off[j] = ok ? (uint32_t)mrow[j] * pitch + coff[j] : kOOB;
+    for (int j = 0; j < NL; ++j) {
+      const int32_t mrow = h ? e[2 * j + 1] : e[2 * j];
+      const bool ok = s * BK + row[j] < klen && (uint32_t)mrow < nrows && coff[j] != kOOB;
+      off[j] = ok ? (uint32_t)mrow * pitch + coff[j] : kOOB;
     }
   }
   __device__ __forceinline__ void issue_one(int j, const uint4* stage, int, int, uint32_t) const {
@@ -317,11 +324,15 @@ __device__ __forceinline__ bf16x8_t load_frag(const uint4* __restrict__ stage, i
   }
 }
 
-__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[NB][MB]) {
+template <class C>
+using acc_t = f32x16_t[C::NB][C::MB];
+
+template <class C>
+__device__ __forceinline__ void zero_acc(acc_t<C>& acc) {
 #pragma unroll
-  for (int i = 0; i < NB; ++i)
+  for (int i = 0; i < C::NB; ++i)
 #pragma unroll
-    for (int j = 0; j < MB; ++j)
+    for (int j = 0; j < C::MB; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 }
@@ -331,19 +342,24 @@ __device__ __forceinline__ void mfma(f32x16_t& acc, const bf16x8_t& n_frag, cons
 }
 
 // The K loop shared by every bf16 GEMM. S = C::STAGES LDS stages of 32 K values per operand
-// (four for the weight gradients, three for the data gradients) are filled by direct loads
-// issued S-1 stages ahead. At the top of stage kt each wave waits for its own loads of stage
-// kt+1, and one barrier then makes stage kt+1 visible and frees stage kt-1's buffer, into
-// which stage kt+S-1 is loaded. A stage is two K16 steps of NB x MB MFMAs. The wavefront
-// issues in order, so every memory instruction sits right behind an MFMA (hard scheduling
-// fences keep that order): during the first step the direct loads of stage kt+S-1 and the
-// fragments of the second step; during the second step the fragments of stage kt+1's first
-// step, so MFMAs start right after the next barrier.
+// are filled by direct loads issued S-1 stages ahead. At the top of stage kt each wave waits
+// for its own loads of stage kt+1, and one barrier then makes stage kt+1 visible and frees
+// stage kt-1's buffer, into which stage kt+S-1 is loaded. A stage is two K16 steps of
+// NB x MB MFMAs. The wavefront issues in order, so every memory instruction sits right
+// behind an MFMA (hard scheduling fences keep that order): during the first step the
+// direct loads of stage kt+S-1 and the fragments of the second step; during the
+// second step the fragments of stage kt+1's first step, so MFMAs start right after the next
+// barrier. With 16 MFMAs per step the fragment reads take the first slots and the direct
+// loads the following ones; with 8 they share the first slots.
 template <class C, bool TNA, bool TNB, class LA, class LB>
 __device__ __forceinline__ void gemm_mainloop(StageBufs<C>& sm, LA& la, LB& lb, int kend, uint32_t kstep_a,
-                                              uint32_t kstep_b, f32x16_t (&acc)[NB][MB], int wm, int wn, int lane) {
+                                              uint32_t kstep_b, acc_t<C>& acc, int wm, int wn, int lane) {
+  constexpr int MB = C::MB, NB = C::NB;
   constexpr int NM = NB * MB, STAGES = C::STAGES, NLA = LA::NL, NLB = LB::NL;
   constexpr int HA = BM / 2, HB = C::BN / 2;  // K-contiguous stage halves
+  // first MFMA slot of the direct loads: behind the fragment reads when the step has room
+  // for both, else from the first slot on, beside them
+  constexpr int kDma0 = NM >= MB + NB + NLA + NLB ? MB + NB : 0;
   static_assert(NLA + NLB <= NM, "one direct load per MFMA slot of the first K16 step");
   const int nk = (kend + BK - 1) / BK;
   if (nk <= 0) return;
@@ -356,8 +372,8 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs<C>& sm, LA& la, LB& lb, 
       if (j < NLA) la.issue_one(j, sm.a[s], s * BK, kend, kstep_a);
       if (j < NLB) lb.issue_one(j, sm.b[s], s * BK, kend, kstep_b);
     }
-    la.fetch(s + 1 - STAGES);  // the indices of stage s + 1
-    lb.fetch(s + 1 - STAGES);
+    la.fetch(s + 1);  // the indices of stage s + 1
+    lb.fetch(s + 1);
     la.advance(s + 1);
     lb.advance(s + 1);
   }
@@ -378,14 +394,15 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs<C>& sm, LA& la, LB& lb, 
     // stage kt+1 landed: the loads of stages kt+2..kt+STAGES-2 may still be in flight
     __builtin_amdgcn_s_waitcnt(0x0F70 | (kLoop & 0xF) | ((kLoop >> 4) << 14));
     __syncthreads();
-    la.fetch(kt);
-    lb.fetch(kt);
+    la.fetch(kt + STAGES);
+    lb.fetch(kt + STAGES);
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       mfma(acc[i / MB][i % MB], fb[0][i / MB], fa[0][i % MB]);
       __builtin_amdgcn_sched_barrier(0);
-      if (i < NLA) la.issue_one(i, sm.a[ldst], k_ld, kend, kstep_a);
-      else if (i < NLA + NLB) lb.issue_one(i - NLA, sm.b[ldst], k_ld, kend, kstep_b);
+      if (i >= kDma0 && i < kDma0 + NLA) la.issue_one(i - kDma0, sm.a[ldst], k_ld, kend, kstep_a);
+      else if (i >= kDma0 + NLA && i < kDma0 + NLA + NLB)
+        lb.issue_one(i - kDma0 - NLA, sm.b[ldst], k_ld, kend, kstep_b);
       if (i < MB) fa[1][i] = load_frag<TNA, HA>(sm.a[cur], wm * 32 * MB + i * 32, 1, lane);
       else if (i < MB + NB) fb[1][i - MB] = load_frag<TNB, HB>(sm.b[cur], wn * 32 * NB + (i - MB) * 32, 1, lane);
       __builtin_amdgcn_sched_barrier(0);
@@ -409,32 +426,36 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs<C>& sm, LA& la, LB& lb, 
 // Writes the accumulators out through LDS so that every output row is handled by
 // consecutive threads with 16-byte accesses. The 256 x BN fp32 tile is staged in two halves
 // of 128 rows (the wavefronts with wm = 0, then wm = 1), each filling the stage buffers
-// (128 x 256 x 4 = 128 KB, or 128 x 128 x 4 = 64 KB of 72 KB). A staged row holds BN/4 chunks
-// of 4 floats; chunk c of row r sits in slot c ^ (r & 15), so the accumulator writes (32 rows
-// per instruction) and the row reads both spread over the banks.
+// (128 x 256 x 4 = 128 KB, all four stages). A staged row holds BN/4 chunks of 4 floats;
+// chunk c of row r sits in slot c ^ (r & 15), so the accumulator writes (32 rows per
+// instruction) and the row reads both spread over the banks.
+template <class C>
+__device__ __forceinline__ void stage_half(float4* st, const acc_t<C>& acc, int wn, int lane) {
+  constexpr int P = C::BN / 4;
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = mb * 32 + (lane & 31);
+        const int c = (wn * 32 * C::NB + nb * 32 + 8 * q + 4 * (lane >> 5)) >> 2;
+        st[r * P + (c ^ (r & 15))] =
+            make_float4(acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
+      }
+}
+
 // BODY(row, col, v[8]) receives 8 consecutive columns of one tile row.
 template <class C, class Body>
-__device__ __forceinline__ void epilogue_staged(StageBufs<C>& sm, const f32x16_t (&acc)[NB][MB], int wm, int wn,
-                                                int lane, Body body) {
+__device__ __forceinline__ void epilogue_staged(StageBufs<C>& sm, const acc_t<C>& acc, int wm, int wn, int lane,
+                                                Body body) {
   constexpr int P = C::BN / 4, NT = C::NTHR;
   static_assert((BM / 2) * C::BN * 4 <= (int)sizeof(StageBufs<C>), "a staged half fits the stage buffers");
   float4* st = reinterpret_cast<float4*>(&sm);
 #pragma unroll
   for (int half = 0; half < C::WM; ++half) {
     __syncthreads();
-    if (wm == half) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = mb * 32 + (lane & 31);
-            const int c = (wn * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5)) >> 2;
-            st[r * P + (c ^ (r & 15))] =
-                make_float4(acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
-          }
-    }
+    if (wm == half) stage_half<C>(st, acc, wn, lane);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < (BM / C::WM) * (C::BN / 8) / NT; ++i) {
@@ -476,27 +497,31 @@ struct DgradArgs {
 
 // SwiGLU backward epilogue of the FC2 data gradient: the tile's dPhi (the accumulators) gives
 // dH = [dPhi * up * silu'(gate), dPhi * silu(gate)] with gate, up read from the saved rows.
-// Staged through LDS in two halves like epilogue_staged. A thread handles 8 rows per half:
-// it loads their 8 row indices together, then their [gate | up] chunks in batches (all 8 in
-// the second half; 4 and 4 in the first, where the other half's accumulators still occupy
-// registers), and stores a batch's dH only after computing all of it, so a half costs two
-// or three memory round trips instead of three per row. Loads always read a valid address
-// (row 0 for a row outside the tile or outside HC) and invalid rows are zeroed at use, so
-// the compiler neither branches around the loads nor waits between them.
+// Staged through LDS in two halves like epilogue_staged. A thread handles kIt rows per half:
+// it loads their row indices together, then their [gate | up] chunks in batches, and stores
+// a batch's dH only after computing all of it, so a half costs a few memory round trips
+// instead of three per row. The first batch is loaded before the half is staged. With eight
+// wavefronts (accumulators in ordinary registers) the first half runs two batches of 4 one
+// after the other, since the other half's accumulators are still live, and the second half
+// one batch of 8; with four wavefronts (accumulators in accumulation registers) batches of 4
+// run with the next batch's loads in flight. Loads always read a valid address (row 0 for a
+// row outside the tile or outside HC) and invalid rows are zeroed at use, so the compiler
+// neither branches around the loads nor waits between them.
 template <int B>
 struct HcBatch {
   uint4 gw[B], uw[B];
   uint32_t okm;
 };
 
-template <class C>
-__device__ __forceinline__ void epilogue_swiglu(StageBufs<C>& sm, const f32x16_t (&acc)[NB][MB], int wm, int wn,
-                                                int lane, const DgradArgs& g, int64_t row0, int rows_valid, int n0,
-                                                int n_valid) {
-  constexpr int WM = C::WM, BN = C::BN, NTHR = C::NTHR, P = BN / 4;
-  constexpr int kIt = (BM / WM) * (BN / 8) / NTHR;  // rows per thread per half (8)
-  constexpr int kRowStep = NTHR / (BN / 8);          // 16
-  static_assert(kIt == 8, "batches of 4 + 4 and 8 rows");
+template <class C, int B, bool AHEAD>
+__device__ __forceinline__ void swiglu_half(StageBufs<C>& sm, const acc_t<C>& acc, int wm, int wn, int lane,
+                                            const DgradArgs& g, int64_t row0, int rows_valid, int n0, int n_valid,
+                                            int half) {
+  constexpr int BN = C::BN, NTHR = C::NTHR, P = BN / 4;
+  constexpr int kIt = (BM / C::WM) * (BN / 8) / NTHR;  // rows per thread per half
+  constexpr int kRowStep = NTHR / (BN / 8);
+  constexpr int kNb = kIt / B;
+  static_assert(kNb * B == kIt, "whole batches");
   const int tr0 = threadIdx.x / (BN / 8), tc = (threadIdx.x % (BN / 8)) * 8;
   const int64_t ld = 2 * (int64_t)g.F;
   const int F = g.F;
@@ -504,13 +529,20 @@ __device__ __forceinline__ void epilogue_swiglu(StageBufs<C>& sm, const f32x16_t
   const uint16_t* __restrict__ hc = g.HC;
   uint16_t* __restrict__ dh = g.out;
   float4* st = reinterpret_cast<float4*>(&sm);
-  auto issue = [&](auto& bt, const int64_t (&hrow)[kIt], int half, int i0) {
-    constexpr int NBt = sizeof(bt.gw) / sizeof(uint4);
+  int64_t hrow[kIt];
+  if (g.hc_rows != nullptr) {
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) hrow[i] = g.hc_rows[row0 + min(half * (BM / C::WM) + tr0 + kRowStep * i, rows_valid - 1)];
+  } else {
+#pragma unroll
+    for (int i = 0; i < kIt; ++i) hrow[i] = row0 + half * (BM / C::WM) + tr0 + kRowStep * i;
+  }
+  auto issue = [&](HcBatch<B>& bt, int i0) {
     bt.okm = 0;
 #pragma unroll
-    for (int b = 0; b < NBt; ++b) {
+    for (int b = 0; b < B; ++b) {
       const int i = i0 + b;
-      const int tr = half * (BM / WM) + tr0 + kRowStep * i;
+      const int tr = half * (BM / C::WM) + tr0 + kRowStep * i;
       const bool ok = tr < rows_valid && col_ok && hrow[i] >= 0 && hrow[i] < g.hc_nrows;
       bt.okm |= ok ? 1u << b : 0u;
       const int64_t hb = ok ? hrow[i] * ld + n0 + tc : 0;
@@ -518,10 +550,9 @@ __device__ __forceinline__ void epilogue_swiglu(StageBufs<C>& sm, const f32x16_t
       bt.uw[b] = *(const uint4*)(hc + hb + F);
     }
   };
-  auto finish = [&](auto& bt, int half, int i0) {
-    constexpr int NBt = sizeof(bt.gw) / sizeof(uint4);
+  auto finish = [&](HcBatch<B>& bt, int i0) {
 #pragma unroll
-    for (int b = 0; b < NBt; ++b) {
+    for (int b = 0; b < B; ++b) {
       const int r = tr0 + kRowStep * (i0 + b), c8 = tc / 8;
       const float4 lo = st[r * P + ((2 * c8) ^ (r & 15))];
       const float4 hi = st[r * P + ((2 * c8 + 1) ^ (r & 15))];
@@ -544,8 +575,8 @@ __device__ __forceinline__ void epilogue_swiglu(StageBufs<C>& sm, const f32x16_t
       bt.uw[b] = pack_bf16x8(du);
     }
 #pragma unroll
-    for (int b = 0; b < NBt; ++b) {
-      const int tr = half * (BM / WM) + tr0 + kRowStep * (i0 + b);
+    for (int b = 0; b < B; ++b) {
+      const int tr = half * (BM / C::WM) + tr0 + kRowStep * (i0 + b);
       if (tr < rows_valid && col_ok) {
         const int64_t rowb = (row0 + tr) * ld + n0 + tc;
         *(uint4*)(dh + rowb) = bt.gw[b];
@@ -553,49 +584,36 @@ __device__ __forceinline__ void epilogue_swiglu(StageBufs<C>& sm, const f32x16_t
       }
     }
   };
+  HcBatch<B> bt[kNb > 1 ? 2 : 1];
+  issue(bt[0], 0);
+  __syncthreads();
+  if (wm == half) stage_half<C>(st, acc, wn, lane);
+  __syncthreads();
 #pragma unroll
-  for (int half = 0; half < WM; ++half) {
-    int64_t hrow[kIt];
-    if (g.hc_rows != nullptr) {
-#pragma unroll
-      for (int i = 0; i < kIt; ++i)
-        hrow[i] = g.hc_rows[row0 + min(half * (BM / WM) + tr0 + kRowStep * i, rows_valid - 1)];
-    } else {
-#pragma unroll
-      for (int i = 0; i < kIt; ++i) hrow[i] = row0 + half * (BM / WM) + tr0 + kRowStep * i;
-    }
-    HcBatch<kIt / 2> b0, b1;
-    HcBatch<kIt> ball;
-    if (half == 0) issue(b0, hrow, half, 0);
-    else issue(ball, hrow, half, 0);
-    __syncthreads();
-    if (wm == half) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = mb * 32 + (lane & 31);
-            const int c = (wn * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5)) >> 2;
-            st[r * P + (c ^ (r & 15))] =
-                make_float4(acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
-          }
-    }
-    __syncthreads();
-    if (half == 0) {
-      finish(b0, half, 0);
-      issue(b1, hrow, half, kIt / 2);
-      finish(b1, half, kIt / 2);
-    } else {
-      finish(ball, half, 0);
-    }
+  for (int i = 0; i < kNb; ++i) {
+    if (AHEAD && i + 1 < kNb) issue(bt[(i + 1) & 1], (i + 1) * B);
+    finish(bt[i & 1], i * B);
+    if (!AHEAD && i + 1 < kNb) issue(bt[(i + 1) & 1], (i + 1) * B);
+  }
+}
+
+template <class C>
+__device__ __forceinline__ void epilogue_swiglu(StageBufs<C>& sm, const acc_t<C>& acc, int wm, int wn, int lane,
+                                                const DgradArgs& g, int64_t row0, int rows_valid, int n0,
+                                                int n_valid) {
+  static_assert(C::WM == 2, "two halves");
+  if constexpr (C::NWAVE == 8) {
+    swiglu_half<C, 4, false>(sm, acc, wm, wn, lane, g, row0, rows_valid, n0, n_valid, 0);
+    swiglu_half<C, 8, false>(sm, acc, wm, wn, lane, g, row0, rows_valid, n0, n_valid, 1);
+  } else {
+    swiglu_half<C, 4, true>(sm, acc, wm, wn, lane, g, row0, rows_valid, n0, n_valid, 0);
+    swiglu_half<C, 4, true>(sm, acc, wm, wn, lane, g, row0, rows_valid, n0, n_valid, 1);
   }
 }
 
 // One output tile per block.
 template <int EPI>
-__global__ __launch_bounds__(CfgD::NTHR) void dgrad_kernel(DgradArgs g) {
+__global__ LRMOE_GEMM_ATTR(CfgD) void dgrad_kernel(DgradArgs g) {
   using C = CfgD;
   __shared__ StageBufs<C> lds;
   const int b = xcd_remap(blockIdx.x, gridDim.x);
@@ -616,8 +634,8 @@ __global__ __launch_bounds__(CfgD::NTHR) void dgrad_kernel(DgradArgs g) {
   const int n_valid = min(C::BN, g.N - n0);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
-  f32x16_t acc[NB][MB];
-  zero_acc(acc);
+  acc_t<C> acc;
+  zero_acc<C>(acc);
   DmaK<C::NWAVE, BM> la;
   DmaK<C::NWAVE, C::BN> lb;
   la.init(g.A + row0 * g.lda, g.lda, rows_valid);
@@ -681,46 +699,35 @@ __device__ __forceinline__ bool fwd_tile(const FwdArgs& g, int b, int& e, int64_
 // epilogue, staged through LDS like epilogue_staged. A thread takes 8 gate columns of a row
 // with the matching 8 up columns and writes both to H and phi = silu(gate) * up (from the
 // fp32 sums, rounded once) to Phi.
-__global__ __launch_bounds__(NTHR) void fwd_fc1_kernel(FwdArgs g) {
-  __shared__ StageBufs<CfgW> lds;
+__global__ LRMOE_GEMM_ATTR(CfgW) void fwd_fc1_kernel(FwdArgs g) {
+  using C = CfgW;
+  __shared__ StageBufs<C> lds;
   int e, rows_valid, nt;
   int64_t row0;
   if (!fwd_tile(g, xcd_remap(blockIdx.x, gridDim.x), e, row0, rows_valid, nt)) return;  // uniform per block
   const int j0 = nt * 128, F = g.F;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN;
-  f32x16_t acc[NB][MB];
-  zero_acc(acc);
-  DmaK<NWAVE, BM> la;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  acc_t<C> acc;
+  zero_acc<C>(acc);
+  DmaK<C::NWAVE, BM> la;
   la.init_rows(g.X, g.D, rows_valid, g.tok + row0, g.T);
-  DmaT lb;
+  DmaT<C::NL> lb;
   lb.init_paired(g.W1 + (int64_t)e * g.D * 2 * F, 2 * F, j0, F);
-  gemm_mainloop<CfgW, false, true>(lds, la, lb, g.D, 0, (uint32_t)(2 * F * 2), acc, wm, wn, lane);
+  gemm_mainloop<C, false, true>(lds, la, lb, g.D, 0, (uint32_t)(2 * F * 2), acc, wm, wn, lane);
 
-  constexpr int P = BN / 4;  // float4 per staged row
+  constexpr int P = C::BN / 4;  // float4 per staged row
   float4* st = reinterpret_cast<float4*>(&lds);
   const int64_t ldh = 2 * (int64_t)F;
 #pragma unroll
-  for (int half = 0; half < WM; ++half) {
+  for (int half = 0; half < C::WM; ++half) {
     __syncthreads();
-    if (wm == half) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int r = mb * 32 + (lane & 31);
-            const int c = (wn * 32 * NB + nb * 32 + 8 * q + 4 * (lane >> 5)) >> 2;
-            st[r * P + (c ^ (r & 15))] =
-                make_float4(acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1], acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]);
-          }
-    }
+    if (wm == half) stage_half<C>(st, acc, wn, lane);
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < (BM / WM) * 16 / NTHR; ++i) {
-      const int id = threadIdx.x + NTHR * i;
+    for (int i = 0; i < (BM / C::WM) * 16 / C::NTHR; ++i) {
+      const int id = threadIdx.x + C::NTHR * i;
       const int r = id / 16, c8 = id % 16;
-      const int tr = half * (BM / WM) + r, f = j0 + c8 * 8;
+      const int tr = half * (BM / C::WM) + r, f = j0 + c8 * 8;
       if (tr < rows_valid && f < F) {
         const float4 g0 = st[r * P + ((2 * c8) ^ (r & 15))], g1 = st[r * P + ((2 * c8 + 1) ^ (r & 15))];
         const float4 u0 = st[r * P + ((32 + 2 * c8) ^ (r & 15))], u1 = st[r * P + ((32 + 2 * c8 + 1) ^ (r & 15))];
@@ -744,24 +751,25 @@ __global__ __launch_bounds__(NTHR) void fwd_fc1_kernel(FwdArgs g) {
 
 // FC2 tile: 256 pair rows x 256 output columns n0 = 256 nt; rows scaled by their routing
 // weight in the epilogue.
-__global__ __launch_bounds__(NTHR) void fwd_fc2_kernel(FwdArgs g) {
-  __shared__ StageBufs<CfgW> lds;
+__global__ LRMOE_GEMM_ATTR(CfgW) void fwd_fc2_kernel(FwdArgs g) {
+  using C = CfgW;
+  __shared__ StageBufs<C> lds;
   int e, rows_valid, nt;
   int64_t row0;
   if (!fwd_tile(g, xcd_remap(blockIdx.x, gridDim.x), e, row0, rows_valid, nt)) return;  // uniform per block
-  const int n0 = nt * BN, n_valid = min(BN, g.D - n0);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN;
-  f32x16_t acc[NB][MB];
-  zero_acc(acc);
-  DmaK<NWAVE, BM> la;
+  const int n0 = nt * C::BN, n_valid = min(C::BN, g.D - n0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  acc_t<C> acc;
+  zero_acc<C>(acc);
+  DmaK<C::NWAVE, BM> la;
   la.init(g.Phi + row0 * g.F, g.F, rows_valid);
-  DmaT lb;
+  DmaT<C::NL> lb;
   lb.init(g.W2 + (int64_t)e * g.F * g.D + n0, g.D, n_valid);
-  gemm_mainloop<CfgW, false, true>(lds, la, lb, g.F, 0, (uint32_t)(g.D * 2), acc, wm, wn, lane);
+  gemm_mainloop<C, false, true>(lds, la, lb, g.F, 0, (uint32_t)(g.D * 2), acc, wm, wn, lane);
   uint16_t* __restrict__ y = g.Y;
   const float* __restrict__ alpha = g.alpha;
   const int D = g.D;
-  epilogue_staged<CfgW>(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
+  epilogue_staged<C>(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
     if (tr < rows_valid && tc < n_valid) {
       const float a = alpha[row0 + tr];
       const float w[8] = {a * v[0], a * v[1], a * v[2], a * v[3], a * v[4], a * v[5], a * v[6], a * v[7]};
@@ -816,17 +824,17 @@ __host__ __device__ inline void expert_split(int64_t m, int& s, int& kc) {
 }
 
 // One block: order experts by decreasing chunk length (ties: lower id) and lay out items.
-__global__ __launch_bounds__(NTHR) void wgrad_plan_kernel(WgradArgs g) {
+__global__ __launch_bounds__(kAuxThr) void wgrad_plan_kernel(WgradArgs g) {
   const int E = g.E;
   const int tiles = g.t[0].tiles + (g.ntypes > 1 ? g.t[1].tiles : 0);
-  for (int e = threadIdx.x; e < E; e += NTHR) {
+  for (int e = threadIdx.x; e < E; e += kAuxThr) {
     int s, kc;
     expert_split(g.row_off[e + 1] - g.row_off[e], s, kc);
     g.plan_s[e] = s;
     g.plan_kc[e] = kc;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += NTHR) {
+  for (int e = threadIdx.x; e < E; e += kAuxThr) {
     const int kc = g.plan_kc[e];
     int rank = 0;
     for (int f = 0; f < E; ++f) {
@@ -855,8 +863,9 @@ __global__ __launch_bounds__(NTHR) void wgrad_plan_kernel(WgradArgs g) {
 // G0, G1: the A operand of weight-gradient type 0 (FC2: Phi) / type 1 (FC1: X) is gathered
 // through its row map (a compile-time choice, so neither loader carries the other's code).
 template <bool G0, bool G1>
-__global__ __launch_bounds__(NTHR) void wgrad_kernel(WgradArgs g) {
-  __shared__ StageBufs<CfgW> lds;
+__global__ LRMOE_GEMM_ATTR(CfgW) void wgrad_kernel(WgradArgs g) {
+  using C = CfgW;
+  __shared__ StageBufs<C> lds;
   // hardware sends block i to XCD i % 8; the grid holds 8 x (largest range) blocks
   const int x = blockIdx.x & 7;
   const int b = g.xlo[x] + (int)(blockIdx.x >> 3);
@@ -882,24 +891,24 @@ __global__ __launch_bounds__(NTHR) void wgrad_kernel(WgradArgs g) {
   const int m0 = mt * BM, n0 = nt * BN;
   const int m_valid = min(BM, T.M - m0), n_valid = min(BN, T.N - n0);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / WN, wn = wave % WN;
-  f32x16_t acc[NB][MB];
-  zero_acc(acc);
-  DmaT lb;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  acc_t<C> acc;
+  zero_acc<C>(acc);
+  DmaT<C::NL> lb;
   lb.init(T.B + (r0 + k_begin) * T.ldb + n0, T.ldb, n_valid);
   if ((G0 || G1) && (ty == 0 ? G0 : G1)) {
-    DmaTG la;
+    DmaTG<C::NL> la;
     la.init(T.A + m0, T.lda, m_valid, T.a_rows + r0 + k_begin, klen, T.a_nrows);
-    gemm_mainloop<CfgW, true, true>(lds, la, lb, klen, 0, (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
+    gemm_mainloop<C, true, true>(lds, la, lb, klen, 0, (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
   } else {
-    DmaT la;
+    DmaT<C::NL> la;
     la.init(T.A + (r0 + k_begin) * T.lda + m0, T.lda, m_valid);
-    gemm_mainloop<CfgW, true, true>(lds, la, lb, klen, (uint32_t)(T.lda * 2), (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
+    gemm_mainloop<C, true, true>(lds, la, lb, klen, (uint32_t)(T.lda * 2), (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
   }
 
   if (s > 1) {
     float* __restrict__ p = g.partials + (g.plan_pbase[e] + (int64_t)chunk * tiles + rem) * (int64_t)(BM * BN);
-    epilogue_staged<CfgW>(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
+    epilogue_staged<C>(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
       float4* q4 = (float4*)(p + tr * BN + tc);
       q4[0] = make_float4(v[0], v[1], v[2], v[3]);
       q4[1] = make_float4(v[4], v[5], v[6], v[7]);
@@ -907,7 +916,7 @@ __global__ __launch_bounds__(NTHR) void wgrad_kernel(WgradArgs g) {
   } else {
     float* __restrict__ o = T.out + (int64_t)e * T.M * T.N;
     const bool accum = g.accumulate != 0;
-    epilogue_staged<CfgW>(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
+    epilogue_staged<C>(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
       if (tr < m_valid && tc < n_valid) {
         float4* q4 = (float4*)(o + (int64_t)(m0 + tr) * T.N + n0 + tc);
         float4 a = make_float4(v[0], v[1], v[2], v[3]), b = make_float4(v[4], v[5], v[6], v[7]);
@@ -928,9 +937,9 @@ __global__ __launch_bounds__(NTHR) void wgrad_kernel(WgradArgs g) {
 // cover the partials' read latency; a thread keeps its four float4 loads of a chunk in
 // flight together.
 constexpr int kRedParts = 8;
-constexpr int kRedPer = BM / kRedParts * (BN / 4) / NTHR;  // float4 per thread (4)
+constexpr int kRedPer = BM / kRedParts * (BN / 4) / kAuxThr;  // float4 per thread (4)
 
-__global__ __launch_bounds__(NTHR) void wgrad_reduce_kernel(WgradArgs g) {
+__global__ __launch_bounds__(kAuxThr) void wgrad_reduce_kernel(WgradArgs g) {
   const int tiles = g.t[0].tiles + (g.ntypes > 1 ? g.t[1].tiles : 0);
   const int part = blockIdx.x % kRedParts;
   int b = blockIdx.x / kRedParts, e = 0;
@@ -956,7 +965,7 @@ __global__ __launch_bounds__(NTHR) void wgrad_reduce_kernel(WgradArgs g) {
   float4 sum[kRedPer];
 #pragma unroll
   for (int u = 0; u < kRedPer; ++u) {
-    const int idx = part * (BM / kRedParts) * (BN / 4) + threadIdx.x + u * NTHR;
+    const int idx = part * (BM / kRedParts) * (BN / 4) + threadIdx.x + u * kAuxThr;
     r[u] = idx / (BN / 4);
     c[u] = (idx % (BN / 4)) * 4;
     ok[u] = r[u] < m_valid && c[u] < n_valid;
@@ -1005,7 +1014,7 @@ __device__ __forceinline__ int find_expert(const int64_t* row_off, int E, int64_
 
 // out[r][n] = sum_k A[r][k] * W[e(r)][n][k]; SwiGLU epilogue or plain store.
 template <int EPI>
-__global__ __launch_bounds__(NTHR) void f32_dgrad_kernel(const float* __restrict__ A, int64_t lda,
+__global__ __launch_bounds__(kAuxThr) void f32_dgrad_kernel(const float* __restrict__ A, int64_t lda,
                                                          const float* __restrict__ W, int64_t ldw,
                                                          int64_t w_estride, int N, int K,
                                                          const int64_t* __restrict__ row_off, int E,
@@ -1013,7 +1022,7 @@ __global__ __launch_bounds__(NTHR) void f32_dgrad_kernel(const float* __restrict
                                                          const int32_t* __restrict__ hc_rows, int64_t hc_nrows,
                                                          float* __restrict__ out, int64_t ldo, int F) {
   const int64_t r = blockIdx.x;
-  const int n = blockIdx.y * NTHR + threadIdx.x;
+  const int n = blockIdx.y * kAuxThr + threadIdx.x;
   if (n >= N) return;
   const int e = find_expert(row_off, E, r);
   const float* a = A + r * lda;
@@ -1034,13 +1043,13 @@ __global__ __launch_bounds__(NTHR) void f32_dgrad_kernel(const float* __restrict
 
 // out[e][i][j] (+)= sum over rows r of expert e of A[ar(r)][i] * B[r][j], with ar(r) =
 // a_rows[r] (rows outside [0, a_nrows) read as zeros) or r when a_rows is nullptr
-__global__ __launch_bounds__(NTHR) void f32_wgrad_kernel(const float* __restrict__ A, int64_t lda,
+__global__ __launch_bounds__(kAuxThr) void f32_wgrad_kernel(const float* __restrict__ A, int64_t lda,
                                                          const int32_t* __restrict__ a_rows, int64_t a_nrows,
                                                          const float* __restrict__ B, int64_t ldb, int M, int N,
                                                          const int64_t* __restrict__ row_off,
                                                          float* __restrict__ out, int accumulate) {
   const int e = blockIdx.z, i = blockIdx.y;
-  const int j = blockIdx.x * NTHR + threadIdx.x;
+  const int j = blockIdx.x * kAuxThr + threadIdx.x;
   if (j >= N) return;
   float acc = 0.0f;
   for (int64_t r = row_off[e]; r < row_off[e + 1]; ++r) {
@@ -1161,9 +1170,9 @@ lrmoe_status launch_expert_forward(const lrmoe_problem* p, const int64_t* seg_of
   g.D = p->D;
   g.F = p->F;
   g.ntn = (int)ceil_div(p->F, 128);
-  fwd_fc1_kernel<<<(unsigned)(mtiles * g.ntn), NTHR, 0, s>>>(g);
+  fwd_fc1_kernel<<<(unsigned)(mtiles * g.ntn), CfgW::NTHR, 0, s>>>(g);
   g.ntn = (int)ceil_div(p->D, BN);
-  fwd_fc2_kernel<<<(unsigned)(mtiles * g.ntn), NTHR, 0, s>>>(g);
+  fwd_fc2_kernel<<<(unsigned)(mtiles * g.ntn), CfgW::NTHR, 0, s>>>(g);
   return launch_status();
 }
 
@@ -1194,27 +1203,27 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
     const float* dl = (const float*)Dlt;
     if (p->swiglu) {
       if (rows > 0) {
-        f32_dgrad_kernel<EPI_SWIGLU><<<dim3((unsigned)rows, (unsigned)ceil_div(F, NTHR)), NTHR, 0, s>>>(
+        f32_dgrad_kernel<EPI_SWIGLU><<<dim3((unsigned)rows, (unsigned)ceil_div(F, kAuxThr)), kAuxThr, 0, s>>>(
             dl, D, (const float*)W2, D, (int64_t)F * D, F, D, row_off_d, E, (const float*)HC, hc_rows, hc_nrows,
             (float*)dH, 2 * F, F);
-        f32_dgrad_kernel<EPI_STORE><<<dim3((unsigned)rows, (unsigned)ceil_div(D, NTHR)), NTHR, 0, s>>>(
+        f32_dgrad_kernel<EPI_STORE><<<dim3((unsigned)rows, (unsigned)ceil_div(D, kAuxThr)), kAuxThr, 0, s>>>(
             (const float*)dH, 2 * F, (const float*)W1, 2 * F, (int64_t)D * 2 * F, D, 2 * F, row_off_d, E, nullptr,
             nullptr, 0, (float*)dIn, D, F);
       }
       if (mark_din() != LRMOE_OK) return LRMOE_ERR_HIP;
       if (E > 0) {
-        f32_wgrad_kernel<<<dim3((unsigned)ceil_div(D, NTHR), F, E), NTHR, 0, s>>>(
+        f32_wgrad_kernel<<<dim3((unsigned)ceil_div(D, kAuxThr), F, E), kAuxThr, 0, s>>>(
             (const float*)PhiC, F, phi_rows, phi_nrows, dl, D, F, D, row_off_d, dW2, accumulate);
-        f32_wgrad_kernel<<<dim3((unsigned)ceil_div(2 * F, NTHR), D, E), NTHR, 0, s>>>(
+        f32_wgrad_kernel<<<dim3((unsigned)ceil_div(2 * F, kAuxThr), D, E), kAuxThr, 0, s>>>(
             (const float*)XC, D, x_rows, x_nrows, (const float*)dH, 2 * F, D, 2 * F, row_off_d, dW1, accumulate);
       }
     } else {
       if (rows > 0)
-        f32_dgrad_kernel<EPI_STORE><<<dim3((unsigned)rows, (unsigned)ceil_div(F, NTHR)), NTHR, 0, s>>>(
+        f32_dgrad_kernel<EPI_STORE><<<dim3((unsigned)rows, (unsigned)ceil_div(F, kAuxThr)), kAuxThr, 0, s>>>(
             dl, D, (const float*)W2, D, (int64_t)F * D, F, D, row_off_d, E, nullptr, nullptr, 0, (float*)dIn, F, F);
       if (mark_din() != LRMOE_OK) return LRMOE_ERR_HIP;
       if (E > 0)
-        f32_wgrad_kernel<<<dim3((unsigned)ceil_div(D, NTHR), F, E), NTHR, 0, s>>>(
+        f32_wgrad_kernel<<<dim3((unsigned)ceil_div(D, kAuxThr), F, E), kAuxThr, 0, s>>>(
             (const float*)PhiC, F, phi_rows, phi_nrows, dl, D, F, D, row_off_d, dW2, accumulate);
     }
     return launch_status();
@@ -1285,16 +1294,16 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
   w.accumulate = accumulate;
   if (E > 0) {
     const int64_t per_xcd = wgrad_xcd_ranges(p, row_off_h, w.xlo);
-    wgrad_plan_kernel<<<1, NTHR, 0, s>>>(w);
+    wgrad_plan_kernel<<<1, kAuxThr, 0, s>>>(w);
     const unsigned grid = (unsigned)(8 * per_xcd);
     const bool g0 = phi_rows != nullptr, g1 = x_rows != nullptr;
     if (per_xcd > 0) {
-      if (g0 && g1) wgrad_kernel<true, true><<<grid, NTHR, 0, s>>>(w);
-      else if (g0) wgrad_kernel<true, false><<<grid, NTHR, 0, s>>>(w);
-      else if (g1) wgrad_kernel<false, true><<<grid, NTHR, 0, s>>>(w);
-      else wgrad_kernel<false, false><<<grid, NTHR, 0, s>>>(w);
+      if (g0 && g1) wgrad_kernel<true, true><<<grid, CfgW::NTHR, 0, s>>>(w);
+      else if (g0) wgrad_kernel<true, false><<<grid, CfgW::NTHR, 0, s>>>(w);
+      else if (g1) wgrad_kernel<false, true><<<grid, CfgW::NTHR, 0, s>>>(w);
+      else wgrad_kernel<false, false><<<grid, CfgW::NTHR, 0, s>>>(w);
     }
-    if (L.nreduce > 0) wgrad_reduce_kernel<<<(unsigned)(L.nreduce * kRedParts), NTHR, 0, s>>>(w);
+    if (L.nreduce > 0) wgrad_reduce_kernel<<<(unsigned)(L.nreduce * kRedParts), kAuxThr, 0, s>>>(w);
   }
   return launch_status();
 }

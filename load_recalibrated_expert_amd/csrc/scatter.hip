@@ -1,6 +1,7 @@
-// Step 5: inverse mapping (LRMoE paper, section 3.1: returned input-gradient contributions
-// are scatter-added at their original token and routing-slot positions in zero-initialised
-// dense buffers; Algorithm 1's ScatterWithZeros).
+// Step 5: inverse mapping (LRMoE paper, section 3.1 and Algorithm 1's ScatterWithZeros).
+// Every packed input-gradient row goes back to the (token, slot) position its pair came
+// from; positions whose pair was dropped stay zero, and the token-order output adds up the
+// rows of each token.
 //
 // Each packed row belongs to one (token, slot) position and each position holds at most one
 // pair, so a [T x K] map from position to packed row is built first (fill -1, then one

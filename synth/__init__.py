@@ -20,9 +20,10 @@ What it draws, and from which passage of the pages the shapes come:
   32,768 tokens per GPU, 128 experts with top-8 routing, so 16 local experts
   under EP8, hidden 2048 and expert intermediate 768 (Qwen3-30B-A3B shaped),
   and a GLM4.5-106B-A12B-shaped variant with hidden 4096 and intermediate 1408.
-* Retention quotas ``q_e = min(n_e, ceil(rho * n_e))``: the pages fix quotas
-  before the layer call (section 3.1, "quotas remain fixed for the invocation")
-  but do not give the planner's rounding; this is the plain reading.
+* Retention quotas ``q_e = min(n_e, ceil(rho * n_e))``: the LRMoE paper sets the
+  quotas once, before the layer call, and the backward does not revise them
+  (section 3.1); it does not give the planner's rounding, so this is the plain
+  reading.
 
 Random numbers come from numpy's counter-based Philox generator, one stream per
 (seed, tensor id, row chunk), so generation is deterministic and can run on

@@ -10,6 +10,7 @@ import torch
 
 import load_recalibrated_expert_amd as lr
 import synth
+from parity_ref import check_selection, on_gpu_selection, reference_selection  # noqa: F401
 
 DEV = torch.device("cuda:0")
 
@@ -67,23 +68,3 @@ class Staged:
 def rel_fro(a, b) -> float:
     d = float(np.linalg.norm(b))
     return float(np.linalg.norm(np.asarray(a) - np.asarray(b))) / (d if d > 0 else 1.0)
-
-
-def check_selection(sel_gpu: np.ndarray, R_or: np.ndarray, seg_off, quota, band=1e-5):
-    """sel must equal the oracle's selection on the f32-rounded scores, except for pairs
-    whose scores lie within `band` (relative) of the expert's threshold."""
-    import oracle
-
-    sel_or, cseg, tau = oracle.select(R_or.astype(np.float32), seg_off, quota)
-    assert len(sel_gpu) == len(sel_or)
-    for e in range(len(quota)):
-        a = sel_gpu[cseg[e]:cseg[e + 1]]
-        b = sel_or[cseg[e]:cseg[e + 1]]
-        assert np.all((a >= seg_off[e]) & (a < seg_off[e + 1])), f"expert {e}: index outside its segment"
-        assert np.all(np.diff(a) > 0), f"expert {e}: not strictly ascending"
-        if np.array_equal(a, b):
-            continue
-        diff = np.setxor1d(a, b)
-        t = tau[e]
-        assert np.all(np.abs(R_or[diff] - t) <= band * t), f"expert {e}: selection differs outside the band"
-    return sel_or, cseg, tau

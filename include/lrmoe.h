@@ -112,17 +112,25 @@ const char* lrmoe_version(void);
 lrmoe_status lrmoe_validate(const lrmoe_problem* p, int64_t* K_tot, int64_t* cseg_off);
 
 /* Host-only. Bytes of scratch that every entry point below needs for this problem
- * and compact mode (one buffer serves all of them; calls on one stream may share it). */
+ * and compact mode (one buffer serves all of them; calls on one stream may share it).
+ * It is the largest of: the score's fp64 token norms [T]; the selection's histograms and
+ * chunk counts; the (token, slot) -> packed row map int32 [T x K] of compaction and
+ * scatter; the grouped GEMM's weight-gradient plan plus its split-K partials, one
+ * 256 x 256 fp32 tile per (chunk, weight-gradient tile) of every expert whose rows (the
+ * retained rows q_e, or n_e when zero-masked) exceed 12288 and are cut into chunks of at
+ * most 12288. The partials dominate at large quotas, so the size depends on them. */
 lrmoe_status lrmoe_workspace_size(const lrmoe_problem* p, lrmoe_compact_mode mode, size_t* bytes);
 
-/* Host-only. Device bytes of the buffers one physical-compaction backward holds at p's
- * quotas, besides its inputs (G, Phi, X, H, W1, W2, alpha, tok, slot) and the workspace:
+/* Host-only. Device bytes one physical-compaction backward holds at p's quotas, besides
+ * its inputs (G, Phi, X, H, W1, W2, alpha, tok, slot): its workspace (lrmoe_workspace_size
+ * for LRMOE_COMPACT_PHYSICAL at these quotas) plus the buffers
  *   R f32 [N], keep u8 [N]; sel, ctok, cslot int32 [K_tot]; Dlt [K_tot x D];
  *   with packed != 0 the packed saved rows PhiC [K_tot x F] (SwiGLU: also XC [K_tot x D]
  *   and HC [K_tot x 2F]); SwiGLU: dH [K_tot x 2F]; dIn [K_tot x w]; f32 weight gradients
  *   dW2 [E x F x D] (SwiGLU: dW1 [E x D x 2F]); the scatter output f32 [T x w]
  * (storage dtype where not marked; w = D for SwiGLU experts, F for FC2-only ones). This is
- * the memory the retention quotas decide. */
+ * the memory the retention quotas decide: the estimate quota admission compares with the
+ * available HBM. */
 lrmoe_status lrmoe_backward_bytes(const lrmoe_problem* p, int32_t packed, size_t* bytes);
 
 /* Host-only. Quota admission on one GPU: Algorithm 1's forward-time admission (section

@@ -90,10 +90,11 @@ class Problem:
                    "lrmoe_workspace_size")
         return int(n.value)
 
-    def workspace(self) -> torch.Tensor:
-        """One scratch buffer large enough for every call in either compact mode."""
-        if self._ws is None:
-            n = max(self.workspace_size(COMPACT_PHYSICAL), self.workspace_size(COMPACT_ZERO_MASKED))
+    def workspace(self, mode=COMPACT_PHYSICAL) -> torch.Tensor:
+        """The problem's scratch buffer, large enough for every call in ``mode`` (it grows
+        once when a zero-masked call needs more than the physical ones)."""
+        n = self.workspace_size(mode)
+        if self._ws is None or self._ws.numel() < n:
             self._ws = torch.empty(n, dtype=torch.uint8, device=self.device)
         return self._ws
 
@@ -105,8 +106,9 @@ class Problem:
 
 
 def backward_bytes(p: Problem, packed=False) -> int:
-    """Device bytes of the buffers one physical-compaction backward holds at p's quotas
-    (host-only; the list is in the header, lrmoe_backward_bytes)."""
+    """Device bytes one physical-compaction backward holds at p's quotas besides its
+    inputs: its buffers and its workspace (host-only; the list is in the header,
+    lrmoe_backward_bytes)."""
     n = ctypes.c_size_t(0)
     _lib.check(library().lrmoe_backward_bytes(ctypes.byref(p.c), int(bool(packed)), ctypes.byref(n)),
                "lrmoe_backward_bytes")
@@ -115,8 +117,8 @@ def backward_bytes(p: Problem, packed=False) -> int:
 
 def plan_quotas(E, T, K, D, F, swiglu, dtype, seg_off, rhos, hbm_avail, packed=False):
     """Quota admission on one GPU (host-only): the largest candidate ratio in ``rhos``
-    (exact decimals such as "0.6", or Fractions) whose backward buffers fit ``hbm_avail``
-    bytes. Returns (index into rhos, quotas [E] int32, bytes); raises InfeasibleQuotaError
+    (exact decimals such as "0.6", or Fractions) whose backward (buffers and workspace)
+    fits ``hbm_avail`` bytes. Returns (index into rhos, quotas [E] int32, bytes); raises InfeasibleQuotaError
     when none fits (Algorithm 1's "return Infeasible")."""
     from fractions import Fraction
     fr = [Fraction(r) for r in rhos]
@@ -210,7 +212,7 @@ def grouped_gemm_bwd(p: Problem, Dlt, PhiC, W2, XC=None, HC=None, W1=None, mode=
         o.setdefault("dIn", torch.empty(max(rows, 1), p.D, dtype=dt, device=dev))
     else:
         o.setdefault("dIn", torch.empty(max(rows, 1), p.F, dtype=dt, device=dev))
-    ws = p.workspace()
+    ws = p.workspace(mode)
     _lib.check(library().lrmoe_grouped_gemm_bwd(
         ctypes.byref(p.c), mode, _ptr(p.row_off_d(mode)), _ptr(Dlt), _ptr(PhiC), _ptr(XC), _ptr(HC), _ptr(hc_rows),
         _ptr(phi_rows), _ptr(x_rows), _ptr(W2),

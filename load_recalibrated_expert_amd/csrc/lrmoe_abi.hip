@@ -49,7 +49,7 @@ size_t ws_need(const lrmoe_problem* p, lrmoe_compact_mode mode) {
 }
 
 // Buffers of one physical-compaction backward at K_tot retained pairs (the list is in the
-// header, with lrmoe_backward_bytes).
+// header, with lrmoe_backward_bytes); the workspace is added by backward_estimate.
 size_t backward_buffer_bytes(const lrmoe_problem* p, int64_t K_tot, bool packed) {
   const size_t e = p->dtype == LRMOE_BF16 ? 2 : 4, K = (size_t)K_tot, N = (size_t)p->N;
   const size_t D = (size_t)p->D, F = (size_t)p->F, E = (size_t)p->E, T = (size_t)p->T;
@@ -65,6 +65,12 @@ size_t backward_buffer_bytes(const lrmoe_problem* p, int64_t K_tot, bool packed)
   if (sw) b += E * D * 2 * F * sizeof(float);  // dW1
   b += T * w * sizeof(float);                  // scatter output
   return b;
+}
+
+// The admission estimate at p's quotas: the backward's buffers plus the scratch the
+// library asks for at those quotas (physical compaction).
+size_t backward_estimate(const lrmoe_problem* p, int64_t K_tot, bool packed) {
+  return backward_buffer_bytes(p, K_tot, packed) + ws_need(p, LRMOE_COMPACT_PHYSICAL);
 }
 
 #define LRMOE_TRY(x)                      \
@@ -104,7 +110,7 @@ lrmoe_status lrmoe_backward_bytes(const lrmoe_problem* p, int32_t packed, size_t
   if (!bytes) return LRMOE_ERR_INVALID_ARG;
   int64_t K_tot = 0;
   LRMOE_TRY(check_problem(p, &K_tot, nullptr));
-  *bytes = backward_buffer_bytes(p, K_tot, packed != 0);
+  *bytes = backward_estimate(p, K_tot, packed != 0);
   return LRMOE_OK;
 }
 
@@ -135,7 +141,7 @@ lrmoe_status lrmoe_plan_quotas(const lrmoe_problem* p, const int32_t* rho_num, c
       q[e] = (int32_t)std::min(n, c);
       K_tot += q[e];
     }
-    const size_t b = backward_buffer_bytes(p, K_tot, packed != 0);
+    const size_t b = backward_estimate(&pq, K_tot, packed != 0);  // pq.quota points at q
     if (b <= hbm_avail) {
       *chosen = i;
       std::copy(q.begin(), q.end(), quota_out);

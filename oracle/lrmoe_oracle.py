@@ -303,12 +303,13 @@ def ceil_quotas(counts, rho) -> np.ndarray:
     return np.array([min(int(n), math.ceil(r * int(n))) for n in counts], dtype=np.int64)
 
 
-def backward_bytes(*, T, E, D, F, swiglu, dtype, N, K_tot, packed=False) -> int:
-    """Device bytes of the buffers one physical-compaction backward holds besides its inputs
-    (G, Phi, X, H, W1, W2, alpha, tok, slot) and its scratch: the memory that the retention
-    quotas decide, the estimate Algorithm 1's admission compares with the available HBM.
-    Listed buffer by buffer (e = bytes of the storage dtype; w = D for SwiGLU experts, F for
-    an FC2-only expert):
+def backward_bytes(*, T, E, D, F, swiglu, dtype, N, K_tot, packed=False, workspace=0) -> int:
+    """Device bytes one physical-compaction backward holds besides its inputs (G, Phi, X, H,
+    W1, W2, alpha, tok, slot): the memory that the retention quotas decide, the estimate
+    Algorithm 1's admission compares with the available HBM. It is ``workspace`` (the
+    scratch the backward's implementation asks for at these quotas: the pages fix no
+    scratch layout, so the caller supplies it) plus the buffers, listed one by one (e =
+    bytes of the storage dtype; w = D for SwiGLU experts, F for an FC2-only expert):
       scores R f32 [N], keep flags u8 [N]; sel, ctok, cslot int32 [K_tot];
       Dlt [K_tot x D] e; packed saved rows PhiC [K_tot x F] e (SwiGLU: XC [K_tot x D],
       HC [K_tot x 2F] too); SwiGLU dH [K_tot x 2F] e; input gradients [K_tot x w] e;
@@ -330,22 +331,24 @@ def backward_bytes(*, T, E, D, F, swiglu, dtype, N, K_tot, packed=False) -> int:
     if swiglu:
         b += 4 * E * D * 2 * F
     b += 4 * T * w
-    return int(b)
+    return int(b + workspace)
 
 
-def plan_quotas(counts, rhos, hbm_avail, *, T, D, F, swiglu, dtype, packed=False):
+def plan_quotas(counts, rhos, hbm_avail, *, T, D, F, swiglu, dtype, packed=False, workspace=None):
     """Algorithm 1's forward-time admission on one GPU (no replica plan and no
     communication window to check): try the candidate ratios in decreasing order (equal
     ratios in the order given), form their quotas, and admit the first whose
-    ``backward_bytes`` fit ``hbm_avail``. Returns (index of the admitted candidate,
-    quotas, bytes). None fits: Algorithm 1 returns Infeasible - raised as InfeasibleQuota."""
+    ``backward_bytes`` fit ``hbm_avail``. ``workspace(quotas)`` gives the implementation's
+    scratch bytes at a candidate's quotas (None: no scratch). Returns (index of the
+    admitted candidate, quotas, bytes). None fits: Algorithm 1 returns Infeasible - raised
+    as InfeasibleQuota."""
     from fractions import Fraction
     counts = [int(n) for n in counts]
     order = sorted(range(len(rhos)), key=lambda i: (-Fraction(rhos[i]), i))
     for i in order:
         q = ceil_quotas(counts, rhos[i])
         b = backward_bytes(T=T, E=len(counts), D=D, F=F, swiglu=swiglu, dtype=dtype, N=sum(counts),
-                           K_tot=int(q.sum()), packed=packed)
+                           K_tot=int(q.sum()), packed=packed, workspace=0 if workspace is None else workspace(q))
         if b <= hbm_avail:
             return i, q, b
     raise InfeasibleQuota("no candidate retention ratio fits the available memory")

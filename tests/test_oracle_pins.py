@@ -228,25 +228,45 @@ def check_backward_bytes_from_shapes(o):
             assert est == _buffer_bytes_of_outputs(o, p, packed), (sw, dt, packed)
 
 
+def _scratch_of(q):
+    """A quota-dependent scratch size standing in for an implementation's workspace: it
+    grows with the largest quota in steps, as split reductions do, and is not monotone in
+    the total."""
+    q = [int(x) for x in q]
+    return 4096 * (1 + max(q) // 37) + 96 * (q[0] % 5)
+
+
 def check_plan_quotas_brute_force(o, seed=8):
     """Admission picks the largest candidate ratio (ties: the earlier one) whose estimate fits,
-    checked against every candidate; with no candidate fitting it reports Infeasible."""
+    checked against every candidate; with no candidate fitting it reports Infeasible. The
+    estimate is the buffers plus the workspace at the candidate's own quotas, run without
+    and with a quota-dependent workspace."""
     from fractions import Fraction
     rng = _rng(seed)
     dims = dict(T=300, D=64, F=48, swiglu=True, dtype="bf16")
     counts = [int(x) for x in rng.integers(0, 200, size=6)]
     rhos = ["0.5", "1", "0.75", "0.25", "0.75", "0.9", "0"]
-    est = [o.backward_bytes(E=len(counts), N=sum(counts), K_tot=int(o.ceil_quotas(counts, r).sum()), **dims)
-           for r in rhos]
-    for budget in sorted(set(est)) + [min(est) - 1, max(est) + 1]:
-        ok = [i for i in range(len(rhos)) if est[i] <= budget]
-        if not ok:
-            with pytest.raises(o.InfeasibleQuota):
-                o.plan_quotas(counts, rhos, budget, **dims)
-            continue
-        best = max(ok, key=lambda i: (Fraction(rhos[i]), -i))
-        i, q, b = o.plan_quotas(counts, rhos, budget, **dims)
-        assert (i, b) == (best, est[best]) and q.tolist() == o.ceil_quotas(counts, rhos[best]).tolist()
+    for ws in (None, _scratch_of):
+        est = []
+        for r in rhos:
+            q = o.ceil_quotas(counts, r)
+            b = o.backward_bytes(E=len(counts), N=sum(counts), K_tot=int(q.sum()), **dims)
+            est.append(b + (0 if ws is None else ws(q)))
+        for budget in sorted(set(est)) + [min(est) - 1, max(est) + 1]:
+            ok = [i for i in range(len(rhos)) if est[i] <= budget]
+            if not ok:
+                with pytest.raises(o.InfeasibleQuota):
+                    o.plan_quotas(counts, rhos, budget, workspace=ws, **dims)
+                continue
+            best = max(ok, key=lambda i: (Fraction(rhos[i]), -i))
+            i, q, b = o.plan_quotas(counts, rhos, budget, workspace=ws, **dims)
+            assert (i, b) == (best, est[best]) and q.tolist() == o.ceil_quotas(counts, rhos[best]).tolist()
+
+
+def check_backward_bytes_adds_workspace(o):
+    """The workspace enters the estimate once, as given."""
+    kw = dict(T=50, E=3, D=32, F=16, swiglu=True, dtype="bf16", N=90, K_tot=40)
+    assert o.backward_bytes(workspace=12345, **kw) == o.backward_bytes(**kw) + 12345
 
 
 def check_swiglu_closed_forms(o):
@@ -492,6 +512,7 @@ ALL_CHECKS = {
     "ceil_quotas_definition": check_ceil_quotas_definition,
     "backward_bytes_from_shapes": check_backward_bytes_from_shapes,
     "plan_quotas_brute_force": check_plan_quotas_brute_force,
+    "backward_bytes_adds_workspace": check_backward_bytes_adds_workspace,
     "swiglu_closed_forms": check_swiglu_closed_forms,
     "forward_exact": check_forward_exact,
     "select_exhaustive_distinct": lambda o: check_select_exhaustive(o, ties=False),
@@ -580,19 +601,28 @@ def _ceil_quotas_floor(counts, rho):
     return np.array([min(int(n), math.floor(r * int(n))) for n in counts], dtype=np.int64)
 
 
-def _backward_bytes_no_dh(*, T, E, D, F, swiglu, dtype, N, K_tot, packed=False):
+def _backward_bytes_no_dh(*, T, E, D, F, swiglu, dtype, N, K_tot, packed=False, workspace=0):
     e = 2 if dtype == "bf16" else 4
     return oracle.backward_bytes(T=T, E=E, D=D, F=F, swiglu=swiglu, dtype=dtype, N=N, K_tot=K_tot,
-                                 packed=packed) - (K_tot * 2 * F * e if swiglu else 0)
+                                 packed=packed, workspace=workspace) - (K_tot * 2 * F * e if swiglu else 0)
 
 
-def _plan_in_given_order(counts, rhos, hbm_avail, **kw):
+def _plan_in_given_order(counts, rhos, hbm_avail, workspace=None, **kw):
     for i, r in enumerate(rhos):
         q = oracle.ceil_quotas(counts, r)
-        b = oracle.backward_bytes(E=len(counts), N=sum(int(n) for n in counts), K_tot=int(q.sum()), **kw)
+        b = oracle.backward_bytes(E=len(counts), N=sum(int(n) for n in counts), K_tot=int(q.sum()),
+                                  workspace=0 if workspace is None else workspace(q), **kw)
         if b <= hbm_avail:
             return i, q, b
     raise oracle.InfeasibleQuota("none")
+
+
+def _plan_without_workspace(counts, rhos, hbm_avail, workspace=None, **kw):
+    return oracle.plan_quotas(counts, rhos, hbm_avail, **kw)
+
+
+def _backward_bytes_ignores_workspace(*, workspace=0, **kw):
+    return oracle.backward_bytes(**kw)
 
 
 def _swiglu_sigmoid_of_minus(h, F):
@@ -686,6 +716,9 @@ PLANTED = [
     ("quota_rounds_down", dict(ceil_quotas=_ceil_quotas_floor), ["ceil_quotas_definition"]),
     ("bytes_without_dh", dict(backward_bytes=_backward_bytes_no_dh), ["backward_bytes_from_shapes"]),
     ("plan_in_given_order", dict(plan_quotas=_plan_in_given_order), ["plan_quotas_brute_force"]),
+    ("plan_without_workspace", dict(plan_quotas=_plan_without_workspace), ["plan_quotas_brute_force"]),
+    ("bytes_ignore_workspace", dict(backward_bytes=_backward_bytes_ignores_workspace),
+     ["backward_bytes_adds_workspace"]),
     ("silu_with_sigmoid_of_minus_x", dict(swiglu=_swiglu_sigmoid_of_minus), ["swiglu_closed_forms", "forward_exact"]),
     ("fc1_ignores_token_gather", dict(expert_forward_fc1=_fc1_no_gather), ["forward_exact"]),
     ("fc2_drops_routing_weight", dict(expert_forward_fc2=_fc2_alpha_dropped), ["forward_exact"]),

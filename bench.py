@@ -265,13 +265,19 @@ def main():
                          criterion=args.criterion)
             bufs["R"] = R
         rec(1)
-        sel, keep = lr.select(P, R, sel=bufs.get("sel"), keep=bufs.get("keep"))
+        phys = mode == lr.COMPACT_PHYSICAL
+        maps = None
+        if phys:  # the selection writes the (token, slot) map that compaction and the scatter use
+            sel, keep, maps = lr.select(P, R, sel=bufs.get("sel"), keep=bufs.get("keep"), tok=tok, slot=slot,
+                                        maps=bufs.get("maps"))
+            bufs.setdefault("maps", maps)
+        else:
+            sel, keep = lr.select(P, R, sel=bufs.get("sel"), keep=bufs.get("keep"))
         bufs.setdefault("sel", sel)
         bufs.setdefault("keep", keep)
         rec(2)
-        phys = mode == lr.COMPACT_PHYSICAL
         c = lr.compact(P, G, Phi, alpha, tok, slot, sel=sel, keep=keep, X=ins["X"] if args.packed else None,
-                       mode=mode, out=bufs.get("c"), pack_phi=args.packed)
+                       mode=mode, out=bufs.get("c"), pack_phi=args.packed, maps=maps)
         bufs.setdefault("c", c)
         rec(3)
         ctok, cslot = (c["ctok"], c["cslot"]) if phys else (tok, slot)
@@ -292,11 +298,12 @@ def main():
             side.wait_event(bufs["din_ready"])
             rec(6, side)
             lr.scatter(P, g["dIn"], ctok, cslot, n_rows=P.rows(mode), out=bufs["out"], ws=bufs["side_ws"],
-                       stream=side)
+                       pmap=maps["pmap"] if maps else None, stream=side)
             rec(7, side)
             main.wait_stream(side)
         else:
-            out = lr.scatter(P, g["dIn"], ctok, cslot, n_rows=P.rows(mode), out=bufs.get("out"))
+            out = lr.scatter(P, g["dIn"], ctok, cslot, n_rows=P.rows(mode), out=bufs.get("out"),
+                             pmap=maps["pmap"] if maps else None)
             bufs.setdefault("out", out)
         rec(5)
         if ev:

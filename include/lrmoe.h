@@ -122,8 +122,9 @@ lrmoe_status lrmoe_validate(const lrmoe_problem* p, int64_t* K_tot, int64_t* cse
 lrmoe_status lrmoe_workspace_size(const lrmoe_problem* p, lrmoe_compact_mode mode, size_t* bytes);
 
 /* Host-only. Device bytes one physical-compaction backward holds at p's quotas, besides
- * its inputs (G, Phi, X, H, W1, W2, alpha, tok, slot): its workspace (lrmoe_workspace_size
- * for LRMOE_COMPACT_PHYSICAL at these quotas) plus the buffers
+ * its inputs (G, Phi, X, H, W1, W2, alpha, tok, slot): its scratch, the workspace
+ * (lrmoe_workspace_size for LRMOE_COMPACT_PHYSICAL at these quotas) and the (token, slot)
+ * map pmap int32 [T x K] of lrmoe_select, plus the buffers
  *   R f32 [N], keep u8 [N]; sel, ctok, cslot int32 [K_tot]; Dlt [K_tot x D];
  *   with packed != 0 the packed saved rows PhiC [K_tot x F] (SwiGLU: also XC [K_tot x D]
  *   and HC [K_tot x 2F]); SwiGLU: dH [K_tot x 2F]; dIn [K_tot x w]; f32 weight gradients
@@ -172,10 +173,19 @@ lrmoe_status lrmoe_score_criterion(const lrmoe_problem* p, lrmoe_criterion crite
  * seg_off_d [E+1] int64, quota_d [E] int32, cseg_off_d [E+1] int64 are device copies of
  * the problem's offsets, quotas and validated packed offsets.
  * sel [K_tot] int32 out: retained pair indices, segment by segment, ascending.
- * keep [N] uint8 out (may be NULL): 1 if retained, else 0. */
+ * keep [N] uint8 out (may be NULL): 1 if retained, else 0.
+ * pmap [T x K] int32 out (may be NULL; then tok, slot, ctok, cslot may be NULL and ctok,
+ * cslot must be): with tok, slot [N] int32 (the pairs' tokens and routing slots), the
+ * (token, slot) -> packed row map of the retained pairs, pmap[t*K + k] = c, -1 where the
+ * position holds no retained pair; and for every packed row c its token and slot,
+ * ctok[c], cslot[c] [K_tot] int32 (both -1 for a pair whose token is outside [0,T) or
+ * slot outside [0,K): such a pair has no position). Compaction and the scatter take pmap
+ * instead of building it themselves, so a backward builds it once. Each (token, slot)
+ * position must hold at most one pair. */
 lrmoe_status lrmoe_select(const lrmoe_problem* p, const float* R, const int64_t* seg_off_d,
                           const int32_t* quota_d, const int64_t* cseg_off_d, int32_t* sel,
-                          uint8_t* keep, void* ws, size_t ws_bytes, lrmoe_stream_t stream);
+                          uint8_t* keep, const int32_t* tok, const int32_t* slot, int32_t* pmap,
+                          int32_t* ctok, int32_t* cslot, void* ws, size_t ws_bytes, lrmoe_stream_t stream);
 
 /* Step 3 - compaction (section 3.1 "compact runtime", section 3.4 / Figure 4).
  * PHYSICAL, for packed row c < K_tot with j = sel[c], t = tok[j]:
@@ -188,19 +198,24 @@ lrmoe_status lrmoe_select(const lrmoe_problem* p, const float* R, const int64_t*
  *   grouped GEMM can read the saved rows in place through sel and ctok (its row maps),
  *   which saves the copies.
  *   Each (token, slot) position holds at most one pair (a token routes to an expert through
- *   one slot); the gather runs token by token through a [T x K] position map kept in ws, so
- *   a token's G and X rows are read from HBM once for all of its retained pairs. A packed
- *   row whose pair has tok outside [0,T) or slot outside [0,K) is left untouched.
+ *   one slot); the gather runs token by token through a [T x K] position map, so a token's
+ *   G and X rows are read from HBM once for all of its retained pairs. pmap: the map and
+ *   ctok/cslot written by lrmoe_select for this sel (tok, slot and cslot may then be NULL,
+ *   ctok is read, and neither is written; no workspace needed); NULL: the map is built in
+ *   ws and ctok, cslot are written here. A retained pair whose tok is outside [0,T) or slot
+ *   outside [0,K) has no position: its ctok and cslot are -1 and its packed rows are zero
+ *   (Dlt, and PhiC, XC, HC when requested), so it adds nothing to the later steps.
  * ZERO_MASKED, for every pair j < N: Dlt[j] = keep[j] ? alpha[j] * G[tok[j]] : 0 and
  *   XC[j] = X[tok[j]] (swiglu; XC optional, the GEMM can read X through tok); sel is
  *   ignored; PhiC and HC must be NULL (the GEMMs read Phi and H in place); ctok/cslot, if
- *   not NULL, receive copies of tok/slot. ws may be NULL.
- * ws: scratch of at least lrmoe_workspace_size bytes (PHYSICAL), else LRMOE_ERR_WORKSPACE. */
+ *   not NULL, receive copies of tok/slot; pmap must be NULL. ws may be NULL.
+ * ws: scratch of at least lrmoe_workspace_size bytes (PHYSICAL without pmap), else
+ * LRMOE_ERR_WORKSPACE. */
 lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, const int32_t* sel,
                            const uint8_t* keep, const void* G, const void* Phi, const void* X,
                            const void* H, const float* alpha, const int32_t* tok, const int32_t* slot,
                            void* Dlt, void* PhiC, void* XC, void* HC, int32_t* ctok, int32_t* cslot,
-                           void* ws, size_t ws_bytes, lrmoe_stream_t stream);
+                           const int32_t* pmap, void* ws, size_t ws_bytes, lrmoe_stream_t stream);
 
 /* Step 4 - packed expert backward, variable-size grouped GEMMs (section 3.4: the FC2
  * and FC1 data- and weight-gradient GEMMs on the retained rows; section 3.1: the
@@ -262,10 +277,12 @@ lrmoe_status lrmoe_expert_forward(const lrmoe_problem* p, const int64_t* seg_off
  * out-of-range index are ignored.
  * TOKEN: out [T x width] f32 = per-token sums, added in slot order (deterministic).
  * SLOT:  out [T*K x width] f32 = the row of each (t, k), zero where no row maps.
- * out is overwritten. */
+ * out is overwritten. pmap (may be NULL): the (token, slot) -> packed row map lrmoe_select
+ * wrote for these rows (then n_rows must be K_tot, ctok and cslot may be NULL and no
+ * workspace is needed); NULL: the map is built in ws from ctok and cslot. */
 lrmoe_status lrmoe_scatter(const lrmoe_problem* p, lrmoe_scatter_mode mode, int64_t n_rows, int32_t width,
                            int32_t rows_dtype, const void* rows, const int32_t* ctok, const int32_t* cslot,
-                           float* out, void* ws, size_t ws_bytes, lrmoe_stream_t stream);
+                           const int32_t* pmap, float* out, void* ws, size_t ws_bytes, lrmoe_stream_t stream);
 
 #ifdef __cplusplus
 }

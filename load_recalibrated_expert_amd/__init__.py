@@ -154,23 +154,39 @@ def score(p: Problem, G, Phi, alpha, tok, R=None, criterion="lrm", stream=None):
     return R
 
 
-def select(p: Problem, R, sel=None, keep=None, want_keep=True, stream=None):
+def select(p: Problem, R, sel=None, keep=None, want_keep=True, tok=None, slot=None, maps=None, stream=None):
+    """Step 2. Returns (sel, keep). With the pairs' ``tok`` and ``slot`` it also writes the
+    (token, slot) -> packed row map and the packed rows' tokens and slots, and returns
+    (sel, keep, maps) with maps = {"pmap", "ctok", "cslot"} (``maps`` reuses buffers)."""
     sel = sel if sel is not None else torch.empty(max(p.K_tot, 1), dtype=torch.int32, device=p.device)
     if keep is None and want_keep:
         keep = torch.empty(max(p.N, 1), dtype=torch.uint8, device=p.device)
+    m = None
+    if tok is not None:
+        m = dict(maps or {})
+        m.setdefault("pmap", torch.empty(max(p.T * p.K, 1), dtype=torch.int32, device=p.device))
+        m.setdefault("ctok", torch.empty(max(p.K_tot, 1), dtype=torch.int32, device=p.device))
+        m.setdefault("cslot", torch.empty(max(p.K_tot, 1), dtype=torch.int32, device=p.device))
     ws = p.workspace()
     _lib.check(library().lrmoe_select(ctypes.byref(p.c), _ptr(R), _ptr(p.seg_off_d), _ptr(p.quota_d),
-                                      _ptr(p.cseg_off_d), _ptr(sel), _ptr(keep), _ptr(ws), ws.numel(),
-                                      _stream(stream)), "lrmoe_select")
-    return sel[:p.K_tot], (keep[:p.N] if keep is not None else None)
+                                      _ptr(p.cseg_off_d), _ptr(sel), _ptr(keep), _ptr(tok), _ptr(slot),
+                                      _ptr(m["pmap"]) if m else None, _ptr(m["ctok"]) if m else None,
+                                      _ptr(m["cslot"]) if m else None, _ptr(ws), ws.numel(), _stream(stream)),
+               "lrmoe_select")
+    out = (sel[:p.K_tot], (keep[:p.N] if keep is not None else None))
+    if m is None:
+        return out
+    return out + ({"pmap": m["pmap"][:p.T * p.K], "ctok": m["ctok"][:p.K_tot], "cslot": m["cslot"][:p.K_tot]},)
 
 
 def compact(p: Problem, G, Phi, alpha, tok, slot, sel=None, keep=None, X=None, H=None,
-            mode=COMPACT_PHYSICAL, out=None, pack_phi=True, stream=None):
-    """Always writes Dlt (and ctok/cslot). The saved rows are packed only on request:
-    PhiC when ``pack_phi`` (physical mode), XC when X is given, HC when H is given
-    (physical mode). The grouped GEMM can read each of them in place instead, through
-    its row maps (sel for Phi and H, ctok or tok for X)."""
+            mode=COMPACT_PHYSICAL, out=None, pack_phi=True, maps=None, stream=None):
+    """Always writes Dlt; ctok/cslot too unless ``maps`` (the map, ctok and cslot that
+    select wrote for this sel) is given, in which case they are returned as given and the
+    gather runs through that map. The saved rows are packed only on request: PhiC when
+    ``pack_phi`` (physical mode), XC when X is given, HC when H is given (physical mode).
+    The grouped GEMM can read each of them in place instead, through its row maps (sel for
+    Phi and H, ctok or tok for X)."""
     rows = p.rows(mode)
     dt = p.torch_dtype
     o = dict(out or {})
@@ -183,13 +199,17 @@ def compact(p: Problem, G, Phi, alpha, tok, slot, sel=None, keep=None, X=None, H
             o.setdefault("HC", torch.empty(max(rows, 1), 2 * p.F, dtype=dt, device=dev))
     if p.swiglu and X is not None:
         o.setdefault("XC", torch.empty(max(rows, 1), p.D, dtype=dt, device=dev))
-    o.setdefault("ctok", torch.empty(max(rows, 1), dtype=torch.int32, device=dev))
-    o.setdefault("cslot", torch.empty(max(rows, 1), dtype=torch.int32, device=dev))
+    pmap = None
+    if maps is not None:
+        o["ctok"], o["cslot"], pmap = maps["ctok"], maps["cslot"], maps["pmap"]
+    else:
+        o.setdefault("ctok", torch.empty(max(rows, 1), dtype=torch.int32, device=dev))
+        o.setdefault("cslot", torch.empty(max(rows, 1), dtype=torch.int32, device=dev))
     ws = p.workspace()
     _lib.check(library().lrmoe_compact(
         ctypes.byref(p.c), mode, _ptr(sel), _ptr(keep), _ptr(G), _ptr(Phi), _ptr(X), _ptr(H), _ptr(alpha),
         _ptr(tok), _ptr(slot), _ptr(o["Dlt"]), _ptr(o.get("PhiC")), _ptr(o.get("XC")), _ptr(o.get("HC")),
-        _ptr(o["ctok"]), _ptr(o["cslot"]), _ptr(ws), ws.numel(), _stream(stream)), "lrmoe_compact")
+        _ptr(o["ctok"]), _ptr(o["cslot"]), _ptr(pmap), _ptr(ws), ws.numel(), _stream(stream)), "lrmoe_compact")
     return {k: v[:rows] for k, v in o.items()}
 
 
@@ -240,19 +260,23 @@ def expert_forward(p: Problem, X, tok, alpha, W1, W2, out=None, stream=None):
     return {"H": H[:p.N], "Phi": Phi[:p.N], "Y": Y[:p.N]}
 
 
-def scatter(p: Problem, rows_t, ctok, cslot, n_rows=None, mode=SCATTER_TOKEN, out=None, ws=None, stream=None):
-    """``ws`` defaults to the problem's workspace; a scatter running concurrently with
-    another call of the same problem (on another stream) needs its own."""
+def scatter(p: Problem, rows_t, ctok, cslot, n_rows=None, mode=SCATTER_TOKEN, out=None, ws=None, pmap=None,
+            stream=None):
+    """``pmap``: the (token, slot) map select wrote for these packed rows (then no workspace
+    is used). Without it the map is built in ``ws``, which defaults to the problem's
+    workspace; a scatter running concurrently with another call of the same problem (on
+    another stream) then needs its own."""
     n_rows = rows_t.shape[0] if n_rows is None else n_rows
     width = rows_t.shape[1]
     rdt = BF16 if rows_t.dtype == torch.bfloat16 else F32
     if out is None:
         nout = p.T if mode == SCATTER_TOKEN else p.T * p.K
         out = torch.empty(max(nout, 1), width, dtype=torch.float32, device=p.device)
-    ws = p.workspace() if ws is None else ws
+    if pmap is None:
+        ws = p.workspace() if ws is None else ws
     _lib.check(library().lrmoe_scatter(ctypes.byref(p.c), mode, n_rows, width, rdt, _ptr(rows_t), _ptr(ctok),
-                                       _ptr(cslot), _ptr(out), _ptr(ws), ws.numel(), _stream(stream)),
-               "lrmoe_scatter")
+                                       _ptr(cslot), _ptr(pmap), _ptr(out), _ptr(ws), 0 if ws is None else ws.numel(),
+                                       _stream(stream)), "lrmoe_scatter")
     return out
 
 
@@ -270,13 +294,20 @@ def backward(p: Problem, *, G, Phi, alpha, tok, slot, W2, X=None, H=None, W1=Non
     b = bufs if bufs is not None else {}
     main = stream if stream is not None else torch.cuda.current_stream()
     b["R"] = score(p, G, Phi, alpha, tok, R=b.get("R"), stream=stream)
-    sel, keep = select(p, b["R"], sel=b.get("sel_full"), keep=b.get("keep_full"), stream=stream)
+    phys = mode == COMPACT_PHYSICAL
+    maps = None
+    if phys:  # the selection also writes the (token, slot) map that compaction and the scatter use
+        sel, keep, maps = select(p, b["R"], sel=b.get("sel_full"), keep=b.get("keep_full"), tok=tok, slot=slot,
+                                 maps=b.get("maps"), stream=stream)
+        b.setdefault("maps", maps)
+    else:
+        sel, keep = select(p, b["R"], sel=b.get("sel_full"), keep=b.get("keep_full"), stream=stream)
     b.setdefault("sel_full", sel)
     b.setdefault("keep_full", keep)
     # only the new gradient rows are packed: the GEMMs read the saved Phi, X and H rows in
     # place through sel and the packed rows' tokens
     c = compact(p, G, Phi, alpha, tok, slot, sel=sel, keep=keep, mode=mode, out=b.get("compact"),
-                pack_phi=False, stream=stream)
+                pack_phi=False, maps=maps, stream=stream)
     b.setdefault("compact", c)
     if mode == COMPACT_PHYSICAL:
         ctok, cslot = c["ctok"], c["cslot"]
@@ -287,11 +318,12 @@ def backward(p: Problem, *, G, Phi, alpha, tok, slot, W2, X=None, H=None, W1=Non
         ctok, cslot = tok, slot
         phi_rows = hc_rows = None
         x_rows = tok if p.swiglu else None
+    pmap = maps["pmap"] if maps is not None else None
     if overlap_scatter:
         if "side" not in b:
             b["side"] = torch.cuda.Stream(device=p.device)
             b["din_ready"] = torch.cuda.Event()
-            b["side_ws"] = torch.empty_like(p.workspace())
+            b["side_ws"] = None if pmap is not None else torch.empty_like(p.workspace())
         if "out" not in b:
             nout = p.T if scatter_mode == SCATTER_TOKEN else p.T * p.K
             b["out"] = torch.empty(max(nout, 1), p.D if p.swiglu else p.F, dtype=torch.float32, device=p.device)
@@ -303,10 +335,10 @@ def backward(p: Problem, *, G, Phi, alpha, tok, slot, W2, X=None, H=None, W1=Non
         side = b["side"]
         side.wait_event(b["din_ready"])
         out = scatter(p, g["dIn"], ctok, cslot, n_rows=p.rows(mode), mode=scatter_mode, out=b["out"],
-                      ws=b["side_ws"], stream=side)
+                      ws=b["side_ws"], pmap=pmap, stream=side)
         main.wait_stream(side)
     else:
         out = scatter(p, g["dIn"], ctok, cslot, n_rows=p.rows(mode), mode=scatter_mode, out=b.get("out"),
-                      stream=main)
+                      pmap=pmap, stream=main)
     b.setdefault("out", out)
     return {"R": b["R"], "sel": sel, "keep": keep, **c, **g, "out": out}

@@ -67,12 +67,12 @@ def load() -> ctypes.CDLL:
                               ctypes.POINTER(i32), ctypes.POINTER(sz)],
         "lrmoe_score": [P, vp, vp, vp, vp, vp, vp, sz, vp],
         "lrmoe_score_criterion": [P, i32, vp, vp, vp, vp, vp, vp, sz, vp],
-        "lrmoe_select": [P, vp, vp, vp, vp, vp, vp, vp, sz, vp],
-        "lrmoe_compact": [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+        "lrmoe_select": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "lrmoe_compact": [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                           ctypes.c_size_t, vp],
         "lrmoe_grouped_gemm_bwd": [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
                                    sz, vp, vp],
-        "lrmoe_scatter": [P, ctypes.c_int, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp],
+        "lrmoe_scatter": [P, ctypes.c_int, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
         "lrmoe_expert_forward": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
     }
     for name, args in sigs.items():

@@ -109,13 +109,14 @@ lrmoe_status launch_score_gradient(const lrmoe_problem* p, bool magnitude, const
 size_t select_ws_bytes(const lrmoe_problem* p);
 lrmoe_status launch_select(const lrmoe_problem* p, const float* R, const int64_t* seg_off_d,
                            const int32_t* quota_d, const int64_t* cseg_off_d, int32_t* sel,
-                           uint8_t* keep, void* ws, hipStream_t s);
+                           uint8_t* keep, const int32_t* tok, const int32_t* slot, int32_t* pmap,
+                           int32_t* ctok, int32_t* cslot, void* ws, hipStream_t s);
 
 lrmoe_status launch_compact(const lrmoe_problem* p, int64_t rows, bool masked, const int32_t* sel,
                             const uint8_t* keep, const void* G, const void* Phi, const void* X,
                             const void* H, const float* alpha, const int32_t* tok, const int32_t* slot,
                             void* Dlt, void* PhiC, void* XC, void* HC, int32_t* ctok, int32_t* cslot,
-                            void* ws, hipStream_t s);
+                            const int32_t* pmap, void* ws, hipStream_t s);
 size_t compact_ws_bytes(const lrmoe_problem* p);
 
 lrmoe_status launch_expert_forward(const lrmoe_problem* p, const int64_t* seg_off_d, const void* X,
@@ -132,7 +133,7 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
 
 size_t scatter_ws_bytes(const lrmoe_problem* p);
 lrmoe_status launch_scatter(const lrmoe_problem* p, int mode, int64_t n_rows, int width, int rows_dtype,
-                            const void* rows, const int32_t* ctok, const int32_t* cslot, float* out,
-                            void* ws, hipStream_t s);
+                            const void* rows, const int32_t* ctok, const int32_t* cslot, const int32_t* pmap,
+                            float* out, void* ws, hipStream_t s);
 
 }  // namespace lrmoe

@@ -10,9 +10,10 @@
 // gradient rows instead.
 //
 // HBM-bound gather/copy with 16-byte vector accesses, several loads in flight per lane
-// before the matching stores. Physical compaction runs token-major: a [T x K] map from
-// (token, slot) to packed row is built first (each position holds at most one pair), then
-// one wavefront per token writes all of its retained rows. Every pair of a token gathers
+// before the matching stores. Physical compaction runs token-major through a [T x K] map
+// from (token, slot) to packed row (each position holds at most one pair): the selection
+// writes it, with ctok and cslot, when asked to; otherwise it is built here first. Then one
+// wavefront per token writes all of its retained rows. Every pair of a token gathers
 // the same G and X rows, so they come from HBM once and from L2 for the other pairs; in
 // packed-row order the pairs of a token lie in different expert segments and each would
 // fetch the rows again. The zero-masked baseline keeps pair order, one wavefront per row.
@@ -122,30 +123,72 @@ __global__ __launch_bounds__(kThreads) void position_fill_kernel(int64_t n, int3
   if (i < n) map[i] = -1;
 }
 
-// map[t*K + k] = packed row of the retained pair at token t, slot k (pairs whose token or
-// slot is out of range are skipped, and their rows are left untouched).
+// For packed row c (pair j = sel[c]): ctok[c] = tok[j], cslot[c] = slot[j], and
+// map[tok * K + slot] = c. A pair whose token or slot is out of range has no position:
+// ctok[c] = cslot[c] = -1 and no map entry (its packed rows are zeroed by the compaction
+// launch).
 __global__ __launch_bounds__(kThreads) void position_map_kernel(int64_t rows, int64_t N, int T, int K,
                                                                 const int32_t* __restrict__ sel,
                                                                 const int32_t* __restrict__ tok,
                                                                 const int32_t* __restrict__ slot,
-                                                                int32_t* __restrict__ map) {
+                                                                int32_t* __restrict__ map, int32_t* __restrict__ ctok,
+                                                                int32_t* __restrict__ cslot) {
   const int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
   if (c >= rows) return;
   const int64_t j = sel[c];
-  if (j < 0 || j >= N) return;
-  const int t = tok[j], k = slot[j];
-  if (t >= 0 && t < T && k >= 0 && k < K) map[(int64_t)t * K + k] = (int32_t)c;
+  const bool pair_ok = j >= 0 && j < N;
+  const int t = pair_ok ? tok[j] : -1, k = pair_ok ? slot[j] : -1;
+  const bool valid = t >= 0 && t < T && k >= 0 && k < K;
+  ctok[c] = valid ? t : -1;
+  cslot[c] = valid ? k : -1;
+  if (valid) map[(int64_t)t * K + k] = (int32_t)c;
+}
+
+// Zeroes the packed rows of retained pairs that have no (token, slot) position (ctok < 0):
+// token-major compaction never reaches them. Block u of this part of a compaction grid
+// scans packed rows [u * kFixRows, (u+1) * kFixRows), a wavefront 1024 of them; every
+// flagged row is cleared by the whole wavefront.
+constexpr int kFixRows = 4096;
+
+__device__ __forceinline__ void zero_unmapped_rows(int u, int64_t rows, const int32_t* __restrict__ ctok, int dch,
+                                                   int fch, bool swiglu, uint4* __restrict__ Dlt,
+                                                   uint4* __restrict__ PhiC, uint4* __restrict__ XC,
+                                                   uint4* __restrict__ HC) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  const int64_t base = (int64_t)u * kFixRows + (int64_t)wave * (kFixRows / kRowsPerBlock);
+  const uint4 z = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < kFixRows / kRowsPerBlock / kWave; ++i) {
+    const int64_t c = base + (int64_t)i * kWave + lane;
+    uint64_t m = __ballot(c < rows && ctok[c] < 0);
+    while (m) {  // uniform
+      const int b = __builtin_ctzll(m);
+      m &= m - 1;
+      const int64_t r = base + (int64_t)i * kWave + b;
+      for (int cc = lane; cc < dch; cc += kWave) {
+        Dlt[r * dch + cc] = z;
+        if (swiglu && XC != nullptr) XC[r * dch + cc] = z;
+      }
+      if (PhiC != nullptr)
+        for (int cc = lane; cc < fch; cc += kWave) PhiC[r * fch + cc] = z;
+      if (swiglu && HC != nullptr)
+        for (int cc = lane; cc < 2 * fch; cc += kWave) HC[r * 2 * fch + cc] = z;
+    }
+  }
 }
 
 // Physical compaction, one wavefront per token: every retained row of the token in slot order.
 // Generic shapes: each row is gathered section by section.
 template <bool BF16, bool SWIGLU>
 __global__ __launch_bounds__(kThreads) void compact_token_kernel(
-    int T, int K, int dch, int fch, const int32_t* __restrict__ map, const int32_t* __restrict__ sel,
-    const uint4* __restrict__ G, const uint4* __restrict__ Phi, const uint4* __restrict__ X,
-    const uint4* __restrict__ H, const float* __restrict__ alpha, const int32_t* __restrict__ slot,
-    uint4* __restrict__ Dlt, uint4* __restrict__ PhiC, uint4* __restrict__ XC, uint4* __restrict__ HC,
-    int32_t* __restrict__ ctok, int32_t* __restrict__ cslot) {
+    int T, int K, int dch, int fch, int64_t rows, int tblocks, const int32_t* __restrict__ map,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ ctok, const uint4* __restrict__ G,
+    const uint4* __restrict__ Phi, const uint4* __restrict__ X, const uint4* __restrict__ H,
+    const float* __restrict__ alpha, uint4* __restrict__ Dlt, uint4* __restrict__ PhiC, uint4* __restrict__ XC,
+    uint4* __restrict__ HC) {
+  if ((int)blockIdx.x >= tblocks) {  // uniform per block
+    zero_unmapped_rows((int)blockIdx.x - tblocks, rows, ctok, dch, fch, SWIGLU, Dlt, PhiC, XC, HC);
+    return;
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (t >= T) return;  // whole wavefront
@@ -155,10 +198,6 @@ __global__ __launch_bounds__(kThreads) void compact_token_kernel(
     const int64_t j = __builtin_amdgcn_readfirstlane(sel[c]);
     gather_row<BF16, SWIGLU, false>(c, j, t, true, true, alpha[j], dch, fch, lane, G, Phi, X, H, Dlt, PhiC, XC,
                                     HC);
-    if (lane == 0) {
-      ctok[c] = t;
-      cslot[c] = slot[j];
-    }
   }
 }
 
@@ -168,11 +207,15 @@ __global__ __launch_bounds__(kThreads) void compact_token_kernel(
 // the stores of the same pair (vector memory operations complete in issue order).
 template <bool BF16, bool SWIGLU, int DL, int FL>
 __global__ __launch_bounds__(kThreads) void compact_token_reg_kernel(
-    int T, int K, int dch, int fch, const int32_t* __restrict__ map, const int32_t* __restrict__ sel,
-    const uint4* __restrict__ G, const uint4* __restrict__ Phi, const uint4* __restrict__ X,
-    const uint4* __restrict__ H, const float* __restrict__ alpha, const int32_t* __restrict__ slot,
-    uint4* __restrict__ Dlt, uint4* __restrict__ PhiC, uint4* __restrict__ XC, uint4* __restrict__ HC,
-    int32_t* __restrict__ ctok, int32_t* __restrict__ cslot) {
+    int T, int K, int dch, int fch, int64_t rows, int tblocks, const int32_t* __restrict__ map,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ ctok, const uint4* __restrict__ G,
+    const uint4* __restrict__ Phi, const uint4* __restrict__ X, const uint4* __restrict__ H,
+    const float* __restrict__ alpha, uint4* __restrict__ Dlt, uint4* __restrict__ PhiC, uint4* __restrict__ XC,
+    uint4* __restrict__ HC) {
+  if ((int)blockIdx.x >= tblocks) {  // uniform per block
+    zero_unmapped_rows((int)blockIdx.x - tblocks, rows, ctok, dch, fch, SWIGLU, Dlt, PhiC, XC, HC);
+    return;
+  }
   constexpr int HL = SWIGLU ? 2 * FL : 1;
   const int lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -257,10 +300,6 @@ __global__ __launch_bounds__(kThreads) void compact_token_reg_kernel(
         if (cc < hch) HC[(int64_t)c * hch + cc] = hh[u];
       }
     }
-    if (lane == 0) {
-      ctok[c] = t;
-      cslot[c] = slot[j];
-    }
     if (kn >= K) break;
     k = kn;
     c = cn;
@@ -278,17 +317,21 @@ __global__ __launch_bounds__(kThreads) void compact_token_reg_kernel(
 
 // Gradient rows only (the saved rows are read in place by the GEMMs), one wavefront per
 // token, for K <= 64 slots and rows of at most DL x 64 16-byte chunks. All of the token's
-// bookkeeping loads run lane-parallel (lane k: the packed row of slot k, its pair, alpha and
-// slot), three dependent round trips in all, while its G row loads into registers; then every
-// retained slot's row is written from the registers.
+// bookkeeping loads run lane-parallel (lane k: the packed row of slot k, its pair and
+// alpha), three dependent round trips in all, while its G row loads into registers; then
+// every retained slot's row is written from the registers.
 template <bool BF16, int DL>
-__global__ __launch_bounds__(kThreads) void compact_dlt_kernel(int T, int K, int dch, const int32_t* __restrict__ map,
+__global__ __launch_bounds__(kThreads) void compact_dlt_kernel(int T, int K, int dch, int64_t rows, int tblocks,
+                                                               const int32_t* __restrict__ map,
                                                                const int32_t* __restrict__ sel,
+                                                               const int32_t* __restrict__ ctok,
                                                                const uint4* __restrict__ G,
                                                                const float* __restrict__ alpha,
-                                                               const int32_t* __restrict__ slot,
-                                                               uint4* __restrict__ Dlt, int32_t* __restrict__ ctok,
-                                                               int32_t* __restrict__ cslot) {
+                                                               uint4* __restrict__ Dlt) {
+  if ((int)blockIdx.x >= tblocks) {  // uniform per block
+    zero_unmapped_rows((int)blockIdx.x - tblocks, rows, ctok, dch, 0, false, Dlt, nullptr, nullptr, nullptr);
+    return;
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   if (t >= T) return;  // whole wavefront
@@ -301,10 +344,6 @@ __global__ __launch_bounds__(kThreads) void compact_dlt_kernel(int T, int K, int
   const int32_t c = lane < K ? map[(int64_t)t * K + lane] : -1;
   const int64_t j = c >= 0 ? (int64_t)sel[c] : -1;
   const float a = j >= 0 ? alpha[j] : 0.0f;
-  if (c >= 0) {
-    ctok[c] = t;
-    cslot[c] = slot[j];
-  }
   for (int k = 0; k < K; ++k) {
     const int32_t ck = __builtin_amdgcn_readlane(c, k);
     if (ck < 0) continue;  // uniform
@@ -322,7 +361,7 @@ template <bool BF16, bool SWIGLU>
 void launch(int64_t rows, bool masked, const lrmoe_problem* p, const int32_t* sel, const uint8_t* keep,
             const void* G, const void* Phi, const void* X, const void* H, const float* alpha, const int32_t* tok,
             const int32_t* slot, void* Dlt, void* PhiC, void* XC, void* HC, int32_t* ctok, int32_t* cslot,
-            int32_t* map, hipStream_t s) {
+            const int32_t* pmap, int32_t* map, hipStream_t s) {
   const int esz = BF16 ? 2 : 4;
   const int dch = p->D * esz / 16, fch = p->F * esz / 16;
   if (masked) {
@@ -331,26 +370,30 @@ void launch(int64_t rows, bool masked, const lrmoe_problem* p, const int32_t* se
         cslot);
     return;
   }
-  const int64_t positions = (int64_t)p->T * p->K;
-  position_fill_kernel<<<(unsigned)ceil_div(positions, kThreads), kThreads, 0, s>>>(positions, map);
-  position_map_kernel<<<(unsigned)ceil_div(rows, kThreads), kThreads, 0, s>>>(rows, p->N, p->T, p->K, sel, tok, slot,
-                                                                              map);
-  const unsigned grid = (unsigned)ceil_div(p->T, kRowsPerBlock);
+  if (pmap == nullptr) {  // build the (token, slot) map here, with ctok and cslot
+    const int64_t positions = (int64_t)p->T * p->K;
+    position_fill_kernel<<<(unsigned)ceil_div(positions, kThreads), kThreads, 0, s>>>(positions, map);
+    position_map_kernel<<<(unsigned)ceil_div(rows, kThreads), kThreads, 0, s>>>(rows, p->N, p->T, p->K, sel, tok,
+                                                                                slot, map, ctok, cslot);
+    pmap = map;
+  }
+  const int tblocks = (int)ceil_div(p->T, kRowsPerBlock);
+  const unsigned grid = (unsigned)(tblocks + ceil_div(rows, kFixRows));
   const bool dlt_only = PhiC == nullptr && XC == nullptr && HC == nullptr;
   if (dlt_only && p->K <= kWave && dch <= 4 * kWave)
-    compact_dlt_kernel<BF16, 4><<<grid, kThreads, 0, s>>>(p->T, p->K, dch, map, sel, (const uint4*)G, alpha, slot,
-                                                           (uint4*)Dlt, ctok, cslot);
+    compact_dlt_kernel<BF16, 4><<<grid, kThreads, 0, s>>>(p->T, p->K, dch, rows, tblocks, pmap, sel, ctok,
+                                                           (const uint4*)G, alpha, (uint4*)Dlt);
   else if (dlt_only && p->K <= kWave && dch <= 8 * kWave)
-    compact_dlt_kernel<BF16, 8><<<grid, kThreads, 0, s>>>(p->T, p->K, dch, map, sel, (const uint4*)G, alpha, slot,
-                                                           (uint4*)Dlt, ctok, cslot);
+    compact_dlt_kernel<BF16, 8><<<grid, kThreads, 0, s>>>(p->T, p->K, dch, rows, tblocks, pmap, sel, ctok,
+                                                           (const uint4*)G, alpha, (uint4*)Dlt);
   else if (dch <= 4 * kWave && fch <= 2 * kWave)
     compact_token_reg_kernel<BF16, SWIGLU, 4, 2><<<grid, kThreads, 0, s>>>(
-        p->T, p->K, dch, fch, map, sel, (const uint4*)G, (const uint4*)Phi, (const uint4*)X, (const uint4*)H, alpha,
-        slot, (uint4*)Dlt, (uint4*)PhiC, (uint4*)XC, (uint4*)HC, ctok, cslot);
+        p->T, p->K, dch, fch, rows, tblocks, pmap, sel, ctok, (const uint4*)G, (const uint4*)Phi, (const uint4*)X,
+        (const uint4*)H, alpha, (uint4*)Dlt, (uint4*)PhiC, (uint4*)XC, (uint4*)HC);
   else
     compact_token_kernel<BF16, SWIGLU><<<grid, kThreads, 0, s>>>(
-        p->T, p->K, dch, fch, map, sel, (const uint4*)G, (const uint4*)Phi, (const uint4*)X, (const uint4*)H, alpha,
-        slot, (uint4*)Dlt, (uint4*)PhiC, (uint4*)XC, (uint4*)HC, ctok, cslot);
+        p->T, p->K, dch, fch, rows, tblocks, pmap, sel, ctok, (const uint4*)G, (const uint4*)Phi, (const uint4*)X,
+        (const uint4*)H, alpha, (uint4*)Dlt, (uint4*)PhiC, (uint4*)XC, (uint4*)HC);
 }
 
 }  // namespace
@@ -361,13 +404,14 @@ lrmoe_status launch_compact(const lrmoe_problem* p, int64_t rows, bool masked, c
                             const uint8_t* keep, const void* G, const void* Phi, const void* X,
                             const void* H, const float* alpha, const int32_t* tok, const int32_t* slot,
                             void* Dlt, void* PhiC, void* XC, void* HC, int32_t* ctok, int32_t* cslot,
-                            void* ws, hipStream_t s) {
+                            const int32_t* pmap, void* ws, hipStream_t s) {
   if (rows <= 0) return LRMOE_OK;
   const bool bf16 = p->dtype == LRMOE_BF16, sw = p->swiglu != 0;
   int32_t* map = (int32_t*)ws;
 #define LRMOE_COMPACT_CASE(B, S)                                                                               \
   if (bf16 == B && sw == S)                                                                                    \
-    launch<B, S>(rows, masked, p, sel, keep, G, Phi, X, H, alpha, tok, slot, Dlt, PhiC, XC, HC, ctok, cslot, map, s);
+    launch<B, S>(rows, masked, p, sel, keep, G, Phi, X, H, alpha, tok, slot, Dlt, PhiC, XC, HC, ctok, cslot, pmap, \
+                 map, s);
   LRMOE_COMPACT_CASE(true, true)
   LRMOE_COMPACT_CASE(true, false)
   LRMOE_COMPACT_CASE(false, true)

@@ -67,10 +67,12 @@ size_t backward_buffer_bytes(const lrmoe_problem* p, int64_t K_tot, bool packed)
   return b;
 }
 
-// The admission estimate at p's quotas: the backward's buffers plus the scratch the
-// library asks for at those quotas (physical compaction).
+// The admission estimate at p's quotas: the backward's buffers plus the library's scratch
+// at those quotas: the workspace (physical compaction) and the (token, slot) -> packed row
+// map int32 [T x K] that the selection writes for compaction and the scatter.
 size_t backward_estimate(const lrmoe_problem* p, int64_t K_tot, bool packed) {
-  return backward_buffer_bytes(p, K_tot, packed) + ws_need(p, LRMOE_COMPACT_PHYSICAL);
+  return backward_buffer_bytes(p, K_tot, packed) + ws_need(p, LRMOE_COMPACT_PHYSICAL) +
+         sizeof(int32_t) * (size_t)p->T * p->K;
 }
 
 #define LRMOE_TRY(x)                      \
@@ -196,41 +198,45 @@ lrmoe_status lrmoe_expert_forward(const lrmoe_problem* p, const int64_t* seg_off
 
 lrmoe_status lrmoe_select(const lrmoe_problem* p, const float* R, const int64_t* seg_off_d,
                           const int32_t* quota_d, const int64_t* cseg_off_d, int32_t* sel, uint8_t* keep,
+                          const int32_t* tok, const int32_t* slot, int32_t* pmap, int32_t* ctok, int32_t* cslot,
                           void* ws, size_t ws_bytes, lrmoe_stream_t stream) {
   int64_t K_tot = 0;
   LRMOE_TRY(check_problem(p, &K_tot, nullptr));
   if (!seg_off_d || !quota_d || !cseg_off_d) return LRMOE_ERR_INVALID_ARG;
   if ((p->N > 0 && !R) || (K_tot > 0 && !sel)) return LRMOE_ERR_INVALID_ARG;
+  if (pmap && ((p->N > 0 && (!tok || !slot)) || (K_tot > 0 && (!ctok || !cslot)))) return LRMOE_ERR_INVALID_ARG;
+  if (!pmap && (ctok || cslot)) return LRMOE_ERR_INVALID_ARG;
   if (select_ws_bytes(p) > 0 && (!ws || ws_bytes < select_ws_bytes(p))) return LRMOE_ERR_WORKSPACE;
-  return launch_select(p, R, seg_off_d, quota_d, cseg_off_d, sel, keep, ws, (hipStream_t)stream);
+  return launch_select(p, R, seg_off_d, quota_d, cseg_off_d, sel, keep, tok, slot, pmap, ctok, cslot, ws,
+                       (hipStream_t)stream);
 }
 
 lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, const int32_t* sel,
                            const uint8_t* keep, const void* G, const void* Phi, const void* X, const void* H,
                            const float* alpha, const int32_t* tok, const int32_t* slot, void* Dlt, void* PhiC,
-                           void* XC, void* HC, int32_t* ctok, int32_t* cslot, void* ws, size_t ws_bytes,
-                           lrmoe_stream_t stream) {
+                           void* XC, void* HC, int32_t* ctok, int32_t* cslot, const int32_t* pmap, void* ws,
+                           size_t ws_bytes, lrmoe_stream_t stream) {
   int64_t K_tot = 0;
   LRMOE_TRY(check_problem(p, &K_tot, nullptr));
   const bool sw = p->swiglu != 0;
   if (mode == LRMOE_COMPACT_PHYSICAL) {
     if (K_tot == 0) return LRMOE_OK;
-    if (!sel || !G || !alpha || !tok || !slot || !Dlt || !ctok || !cslot || (PhiC && !Phi))
-      return LRMOE_ERR_INVALID_ARG;
+    if (!sel || !G || !alpha || !Dlt || !ctok || (PhiC && !Phi)) return LRMOE_ERR_INVALID_ARG;
+    if (!pmap && (!tok || !slot || !cslot)) return LRMOE_ERR_INVALID_ARG;
     if (sw && ((XC && !X) || (HC && !H))) return LRMOE_ERR_INVALID_ARG;
     if (!sw && (X || H || XC || HC)) return LRMOE_ERR_INVALID_ARG;
-    if (!ws || ws_bytes < compact_ws_bytes(p)) return LRMOE_ERR_WORKSPACE;
+    if (!pmap && (!ws || ws_bytes < compact_ws_bytes(p))) return LRMOE_ERR_WORKSPACE;
     return launch_compact(p, K_tot, false, sel, nullptr, G, Phi, X, H, alpha, tok, slot, Dlt, PhiC, XC, HC,
-                          ctok, cslot, ws, (hipStream_t)stream);
+                          ctok, cslot, pmap, ws, (hipStream_t)stream);
   }
   if (mode == LRMOE_COMPACT_ZERO_MASKED) {
     if (p->N == 0) return LRMOE_OK;
-    if (!keep || !G || !alpha || !tok || !Dlt || PhiC || HC) return LRMOE_ERR_INVALID_ARG;
+    if (!keep || !G || !alpha || !tok || !Dlt || PhiC || HC || pmap) return LRMOE_ERR_INVALID_ARG;
     if ((ctok || cslot) && !slot) return LRMOE_ERR_INVALID_ARG;
     if (sw && XC && !X) return LRMOE_ERR_INVALID_ARG;
     if (!sw && (X || XC)) return LRMOE_ERR_INVALID_ARG;
     return launch_compact(p, p->N, true, nullptr, keep, G, Phi, X, H, alpha, tok, slot, Dlt, nullptr, XC,
-                          nullptr, ctok, cslot, nullptr, (hipStream_t)stream);
+                          nullptr, ctok, cslot, nullptr, nullptr, (hipStream_t)stream);
   }
   return LRMOE_ERR_INVALID_ARG;
 }
@@ -266,14 +272,20 @@ lrmoe_status lrmoe_grouped_gemm_bwd(const lrmoe_problem* p, lrmoe_compact_mode m
 
 lrmoe_status lrmoe_scatter(const lrmoe_problem* p, lrmoe_scatter_mode mode, int64_t n_rows, int32_t width,
                            int32_t rows_dtype, const void* rows, const int32_t* ctok, const int32_t* cslot,
-                           float* out, void* ws, size_t ws_bytes, lrmoe_stream_t stream) {
-  LRMOE_TRY(check_problem(p, nullptr, nullptr));
+                           const int32_t* pmap, float* out, void* ws, size_t ws_bytes, lrmoe_stream_t stream) {
+  int64_t K_tot = 0;
+  LRMOE_TRY(check_problem(p, &K_tot, nullptr));
   if (mode != LRMOE_SCATTER_TOKEN && mode != LRMOE_SCATTER_SLOT) return LRMOE_ERR_INVALID_ARG;
   if (rows_dtype != LRMOE_F32 && rows_dtype != LRMOE_BF16) return LRMOE_ERR_UNSUPPORTED;
   if (n_rows < 0 || n_rows > p->N || width < 8 || width % 8 != 0) return LRMOE_ERR_INVALID_ARG;
-  if (!out || (n_rows > 0 && (!rows || !ctok || !cslot))) return LRMOE_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < scatter_ws_bytes(p)) return LRMOE_ERR_WORKSPACE;
-  return launch_scatter(p, mode, n_rows, width, rows_dtype, rows, ctok, cslot, out, ws, (hipStream_t)stream);
+  if (!out || (n_rows > 0 && !rows)) return LRMOE_ERR_INVALID_ARG;
+  if (pmap) {  // the selection's map addresses the K_tot packed rows
+    if (n_rows != K_tot) return LRMOE_ERR_INVALID_ARG;
+  } else {
+    if (n_rows > 0 && (!ctok || !cslot)) return LRMOE_ERR_INVALID_ARG;
+    if (!ws || ws_bytes < scatter_ws_bytes(p)) return LRMOE_ERR_WORKSPACE;
+  }
+  return launch_scatter(p, mode, n_rows, width, rows_dtype, rows, ctok, cslot, pmap, out, ws, (hipStream_t)stream);
 }
 
 }  // extern "C"

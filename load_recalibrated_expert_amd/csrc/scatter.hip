@@ -4,10 +4,11 @@
 // rows of each token.
 //
 // Each packed row belongs to one (token, slot) position and each position holds at most one
-// pair, so a [T x K] map from position to packed row is built first (fill -1, then one
-// store per row: no conflicts). Token mode then sums, per token, the rows of its K slots in
-// slot order - a fixed order, so the result is deterministic without atomics. Slot mode
-// copies each position's row or writes zeros.
+// pair, so a [T x K] map from position to packed row drives the scatter: the one the
+// selection wrote, or one built here first (fill -1, then one store per row: no
+// conflicts). Token mode then sums, per token, the rows of its K slots in slot order - a
+// fixed order, so the result is deterministic without atomics. Slot mode copies each
+// position's row or writes zeros.
 #include "common.h"
 
 namespace lrmoe {
@@ -154,15 +155,19 @@ __global__ __launch_bounds__(kThreads) void slot_copy_kernel(int64_t positions, 
 size_t scatter_ws_bytes(const lrmoe_problem* p) { return align_up(sizeof(int32_t) * (size_t)p->T * p->K, 256); }
 
 lrmoe_status launch_scatter(const lrmoe_problem* p, int mode, int64_t n_rows, int width, int rows_dtype,
-                            const void* rows, const int32_t* ctok, const int32_t* cslot, float* out,
-                            void* ws, hipStream_t s) {
+                            const void* rows, const int32_t* ctok, const int32_t* cslot, const int32_t* pmap,
+                            float* out, void* ws, hipStream_t s) {
   const int64_t positions = (int64_t)p->T * p->K;
   if (positions == 0) return LRMOE_OK;
-  int32_t* map = (int32_t*)ws;
-  map_fill_kernel<<<(unsigned)ceil_div(positions, kThreads), kThreads, 0, s>>>(positions, map);
-  if (n_rows > 0)
-    map_scatter_kernel<<<(unsigned)ceil_div(n_rows, kThreads), kThreads, 0, s>>>(n_rows, p->T, p->K, ctok,
-                                                                                 cslot, map);
+  const int32_t* map = pmap;
+  if (map == nullptr) {  // build the (token, slot) map from the rows' tokens and slots
+    int32_t* m = (int32_t*)ws;
+    map_fill_kernel<<<(unsigned)ceil_div(positions, kThreads), kThreads, 0, s>>>(positions, m);
+    if (n_rows > 0)
+      map_scatter_kernel<<<(unsigned)ceil_div(n_rows, kThreads), kThreads, 0, s>>>(n_rows, p->T, p->K, ctok,
+                                                                                   cslot, m);
+    map = m;
+  }
   const bool bf16 = rows_dtype == LRMOE_BF16;
   constexpr int per_block = kThreads / kWave;
   if (mode == LRMOE_SCATTER_TOKEN) {

@@ -13,7 +13,12 @@
 // launches: chunk blocks count keys above and equal to the threshold, one block per segment
 // turns the counts into chunk offsets, and chunk blocks write the retained indices at
 // positions given by block-level ballot scans. Kernel boundaries order every step, so no
-// block waits on another and no block needs a device-wide fence.
+// block waits on another and no block needs a device-wide fence. On request the write
+// launch also records, for every retained pair, its packed row in a (token, slot) map and
+// its token and slot in packed order (the init launch clears the map), so compaction and
+// the scatter need no map of their own.
+#include <algorithm>
+
 #include "common.h"
 
 namespace lrmoe {
@@ -31,6 +36,18 @@ struct SegState {
   uint32_t mask;    // bits of prefix that are fixed
   uint32_t need;    // rank still to find among keys matching prefix (ties kept at the end)
   uint32_t mode;
+};
+
+// Optional outputs of the write kernel: for every retained pair j at packed row c, its
+// token and slot (ctok[c], cslot[c]; -1 for both when either is out of range) and the
+// (token, slot) -> packed row map entry pmap[tok * K + slot] = c.
+struct PosOut {
+  const int32_t* tok;
+  const int32_t* slot;
+  int32_t* pmap;  // [T x K] or nullptr
+  int32_t* ctok;
+  int32_t* cslot;
+  int T, K;
 };
 
 struct SelWs {
@@ -85,9 +102,11 @@ __device__ __forceinline__ uint32_t load_chunk(const float* __restrict__ R, int6
 
 __global__ __launch_bounds__(kSelThreads) void select_init_kernel(int E, const int64_t* __restrict__ seg_off,
                                                                   const int32_t* __restrict__ quota,
-                                                                  SelWs w) {
+                                                                  SelWs w, int64_t positions,
+                                                                  int32_t* __restrict__ pmap) {
   const int64_t gid = (int64_t)blockIdx.x * kSelThreads + threadIdx.x;
   if (gid < (int64_t)E * kBins) w.hist[gid] = 0;
+  if (pmap != nullptr && gid < positions) pmap[gid] = -1;  // positions with no retained pair
   if (gid < E) {
     const int64_t n = seg_off[gid + 1] - seg_off[gid];
     const int64_t q = quota[gid];
@@ -254,7 +273,7 @@ __global__ __launch_bounds__(kSelThreads) void select_write_kernel(const float* 
                                                                    const int64_t* __restrict__ cseg_off,
                                                                    SelWs w, int maxch, int64_t K_tot,
                                                                    int32_t* __restrict__ sel,
-                                                                   uint8_t* __restrict__ keep) {
+                                                                   uint8_t* __restrict__ keep, PosOut po) {
   __shared__ uint32_t wtot[kSelPer][2][kSelThreads / kWave];
   const int e = blockIdx.y, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const SegState st = w.state[e];
@@ -268,6 +287,16 @@ __global__ __launch_bounds__(kSelThreads) void select_write_kernel(const float* 
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   uint32_t k[kSelPer];
   const uint32_t ok = load_chunk(R, lo, hi, k);
+  // the pairs' tokens and slots (with the map only), all loaded before any is used, as the keys
+  int32_t pt[kSelPer], ps[kSelPer];
+  if (po.pmap != nullptr) {  // uniform
+#pragma unroll
+    for (int r = 0; r < kSelPer; ++r) {
+      const int64_t i = lo + (int64_t)r * kSelThreads + tid;
+      pt[r] = i < hi ? po.tok[i] : -1;
+      ps[r] = i < hi ? po.slot[i] : -1;
+    }
+  }
   uint64_t bg[kSelPer], be[kSelPer];
 #pragma unroll
   for (int r = 0; r < kSelPer; ++r) {
@@ -304,7 +333,16 @@ __global__ __launch_bounds__(kSelThreads) void select_write_kernel(const float* 
     const bool kp = gt || (eq && eq_before < need);
     if (kp) {
       const int64_t pos = cbase + gt_before + min(eq_before, need);
-      if (pos < cend) sel[pos] = (int32_t)i;
+      if (pos < cend) {
+        sel[pos] = (int32_t)i;
+        if (po.pmap != nullptr) {  // the packed row's token and slot, and its map entry
+          const int t = pt[r], sl = ps[r];
+          const bool valid = t >= 0 && t < po.T && sl >= 0 && sl < po.K;
+          po.ctok[pos] = valid ? t : -1;
+          po.cslot[pos] = valid ? sl : -1;
+          if (valid) po.pmap[(int64_t)t * po.K + sl] = (int32_t)pos;
+        }
+      }
     }
     if (keep != nullptr && (ok >> r & 1)) keep[i] = kp ? 1 : 0;
     run_gt += tg;
@@ -318,14 +356,18 @@ size_t select_ws_bytes(const lrmoe_problem* p) { return carve_bytes(p->E, max_ch
 
 lrmoe_status launch_select(const lrmoe_problem* p, const float* R, const int64_t* seg_off_d,
                            const int32_t* quota_d, const int64_t* cseg_off_d, int32_t* sel,
-                           uint8_t* keep, void* ws, hipStream_t s) {
+                           uint8_t* keep, const int32_t* tok, const int32_t* slot, int32_t* pmap,
+                           int32_t* ctok, int32_t* cslot, void* ws, hipStream_t s) {
   const int E = p->E, maxch = max_chunks(p);
   if (E <= 0) return LRMOE_OK;
   int64_t K_tot = 0;
   for (int e = 0; e < E; ++e) K_tot += p->quota[e];
   SelWs w = carve(ws, E, maxch);
-  select_init_kernel<<<(unsigned)ceil_div((int64_t)E * kBins, kSelThreads), kSelThreads, 0, s>>>(E, seg_off_d,
-                                                                                                   quota_d, w);
+  const int64_t positions = pmap != nullptr ? (int64_t)p->T * p->K : 0;
+  const PosOut po{tok, slot, pmap, ctok, cslot, p->T, p->K};
+  const int64_t init_threads = std::max<int64_t>((int64_t)E * kBins, positions);
+  select_init_kernel<<<(unsigned)ceil_div(init_threads, kSelThreads), kSelThreads, 0, s>>>(E, seg_off_d, quota_d, w,
+                                                                                           positions, pmap);
   const dim3 grid(maxch, E);
   const int shifts[3] = {21, 10, 0}, bits[3] = {11, 11, 10};
   for (int pass = 0; pass < 3; ++pass) {
@@ -334,7 +376,7 @@ lrmoe_status launch_select(const lrmoe_problem* p, const float* R, const int64_t
   }
   select_count_kernel<<<grid, kSelThreads, 0, s>>>(R, seg_off_d, w, maxch);
   select_offs_kernel<<<E, kSelThreads, 0, s>>>(seg_off_d, w, maxch);
-  select_write_kernel<<<grid, kSelThreads, 0, s>>>(R, seg_off_d, cseg_off_d, w, maxch, K_tot, sel, keep);
+  select_write_kernel<<<grid, kSelThreads, 0, s>>>(R, seg_off_d, cseg_off_d, w, maxch, K_tot, sel, keep, po);
   return launch_status();
 }
 

@@ -103,23 +103,40 @@ def test_workspace_size_and_host_side_rejections():
     assert lib.lrmoe_score(ctypes.byref(p), None, None, None, None, None, None, 0, None) == _lib.ERR_INVALID_ARG
     fake = ctypes.c_void_p(0x1000)
     assert lib.lrmoe_score(ctypes.byref(p), fake, fake, fake, fake, fake, None, 0, None) == _lib.ERR_WORKSPACE
-    assert lib.lrmoe_select(ctypes.byref(p), fake, fake, fake, fake, fake, None, None, 0, None) == _lib.ERR_WORKSPACE
-    assert lib.lrmoe_scatter(ctypes.byref(p), 0, 3, 12, _lib.BF16, fake, fake, fake, fake, fake, 1 << 20,
+    nomap = [None] * 5  # tok, slot, pmap, ctok, cslot
+    assert lib.lrmoe_select(ctypes.byref(p), fake, fake, fake, fake, fake, None, *nomap, None, 0,
+                            None) == _lib.ERR_WORKSPACE
+    # the (token, slot) map needs the pairs' tokens and slots and the packed rows' outputs
+    assert lib.lrmoe_select(ctypes.byref(p), fake, fake, fake, fake, fake, None, None, fake, fake, fake, fake,
+                            fake, 1 << 30, None) == _lib.ERR_INVALID_ARG
+    assert lib.lrmoe_select(ctypes.byref(p), fake, fake, fake, fake, fake, None, fake, fake, fake, None, fake,
+                            fake, 1 << 30, None) == _lib.ERR_INVALID_ARG
+    assert lib.lrmoe_select(ctypes.byref(p), fake, fake, fake, fake, fake, None, None, None, None, fake, fake,
+                            fake, 1 << 30, None) == _lib.ERR_INVALID_ARG  # ctok without the map
+    assert lib.lrmoe_scatter(ctypes.byref(p), 0, 3, 12, _lib.BF16, fake, fake, fake, None, fake, fake, 1 << 20,
                              None) == _lib.ERR_INVALID_ARG  # width not a multiple of 8
-    assert lib.lrmoe_compact(ctypes.byref(p), 5, *([None] * 15), None, 0, None) == _lib.ERR_INVALID_ARG
+    # with the selection's map the scatter covers exactly the K_tot packed rows (3 + 0 + 7 = 10 here)
+    assert lib.lrmoe_scatter(ctypes.byref(p), 0, 11, 16, _lib.BF16, fake, None, None, fake, fake, None, 0,
+                             None) == _lib.ERR_INVALID_ARG
+    assert lib.lrmoe_compact(ctypes.byref(p), 5, *([None] * 16), None, 0, None) == _lib.ERR_INVALID_ARG
     sw = [fake] * 15 if p.swiglu else [fake, None, fake, fake, None, None, fake, fake, fake, fake, fake, None,
                                          None, fake, fake]
-    assert lib.lrmoe_compact(ctypes.byref(p), _lib.COMPACT_PHYSICAL, *sw, None, 0, None) == _lib.ERR_WORKSPACE
+    assert lib.lrmoe_compact(ctypes.byref(p), _lib.COMPACT_PHYSICAL, *sw, None, None, 0,
+                             None) == _lib.ERR_WORKSPACE
     q, keep2 = _problem(quota=(6, 0, 7))
     assert lib.lrmoe_grouped_gemm_bwd(ctypes.byref(q), 0, *([fake] * 14), 0, fake, 1 << 30,
                                       None, None) == _lib.ERR_INFEASIBLE_QUOTA
     assert _lib.status_string(_lib.ERR_INFEASIBLE_QUOTA).startswith("infeasible")
     # packing PhiC needs Phi; packing XC needs X
     args = [fake, None, fake, None, None, None, fake, fake, fake, fake, fake, None, None, fake, fake]
-    assert lib.lrmoe_compact(ctypes.byref(p), _lib.COMPACT_PHYSICAL, *args, fake, 1 << 30,
+    assert lib.lrmoe_compact(ctypes.byref(p), _lib.COMPACT_PHYSICAL, *args, None, fake, 1 << 30,
                              None) == _lib.ERR_INVALID_ARG
     args = [fake, None, fake, fake, None, None, fake, fake, fake, fake, None, fake, None, fake, fake]
-    assert lib.lrmoe_compact(ctypes.byref(p), _lib.COMPACT_PHYSICAL, *args, fake, 1 << 30,
+    assert lib.lrmoe_compact(ctypes.byref(p), _lib.COMPACT_PHYSICAL, *args, None, fake, 1 << 30,
+                             None) == _lib.ERR_INVALID_ARG
+    # zero-masked compaction has no packed rows to map
+    args = [None, fake, fake, fake, fake, fake, fake, fake, fake, fake, None, None, None, None, None]
+    assert lib.lrmoe_compact(ctypes.byref(p), _lib.COMPACT_ZERO_MASKED, *args, fake, fake, 1 << 30,
                              None) == _lib.ERR_INVALID_ARG
 
 

@@ -158,6 +158,8 @@ def test_compact(case):
     torch.cuda.synchronize()
     assert np.array_equal(bits(c["PhiC"]), pr.Phi[sel])
     assert torch.equal(c["Dlt"], res["Dlt"])
+    # compaction building its own (token, slot) map gives the selection's ctok and cslot
+    assert torch.equal(c["ctok"], res["ctok"]) and torch.equal(c["cslot"], res["cslot"])
     if pr.cfg.swiglu:
         assert np.array_equal(bits(c["XC"]), pr.X[pr.routing.tok[sel]])
         assert np.array_equal(bits(c["HC"]), pr.H[sel])
@@ -408,3 +410,43 @@ def test_nothing_retained(counts, dtype):
     assert res["sel"].numel() == 0
     for k in ("dW1", "dW2", "out"):
         assert torch.count_nonzero(res[k]).item() == 0, k
+
+
+def test_pairs_without_a_position():
+    """Retained pairs whose token or routing slot is out of range have no (token, slot)
+    position: their ctok and cslot are -1, their packed gradient rows are zero and they add
+    nothing to the weight gradients or the scatter, with the selection's map and with the
+    map compaction and the scatter build themselves. The oracle reference gives those pairs
+    a zero routing weight (and a valid token), so their contributions vanish there too."""
+    cfg = synth.custom("no_position", T=90, K=3, E=3, D=256, F=128, counts=(100, 60, 40), seed=33)
+    pr = synth.make_problem(cfg, quota=(100, 60, 40))  # keep every pair
+    r = pr.routing
+    bad_tok, bad_slot = [3, 71, 150], [20, 199]
+    tok, slot = r.tok.copy(), r.slot.copy()
+    tok[bad_tok] = [-1, cfg.T, -5]
+    slot[bad_slot] = [cfg.K, -1]
+    s = Staged(pr)
+    s.tok = torch.from_numpy(tok).to(DEV)
+    s.slot = torch.from_numpy(slot).to(DEV)
+    res = s.backward()
+    c = lr.compact(s.P, s.G, s.Phi, s.alpha, s.tok, s.slot, sel=res["sel"], keep=res["keep"], pack_phi=False)
+    out2 = lr.scatter(s.P, res["dIn"], c["ctok"], c["cslot"])
+    torch.cuda.synchronize()
+    bad = np.array(bad_tok + bad_slot)
+    sel = res["sel"].cpu().numpy()
+    rows = np.searchsorted(sel, bad)
+    assert np.array_equal(sel[rows], bad)
+    for got in (res, c):
+        assert np.all(got["ctok"].cpu().numpy()[rows] == -1) and np.all(got["cslot"].cpu().numpy()[rows] == -1)
+        assert not bool(got["Dlt"][torch.from_numpy(rows).to(DEV)].float().abs().sum())
+    assert torch.equal(c["Dlt"], res["Dlt"]) and torch.equal(out2, res["out"])
+    alpha0 = r.alpha.copy()
+    alpha0[bad] = 0.0
+    tok0 = tok.copy()
+    tok0[bad_tok] = 0
+    ref = oracle.backward(G=pr.G, Phi=pr.Phi, alpha=alpha0, tok=tok0, slot=r.slot, seg_off=r.seg_off,
+                          quota=pr.quota, dtype="bf16", T=cfg.T, W2=pr.W2, X=pr.X, H=pr.H, W1=pr.W1)
+    for e in range(cfg.E):
+        assert rel_fro(as_f64(res["dW2"][e]), ref["dW2"][e]) <= 5e-3, f"dW2 expert {e}"
+        assert rel_fro(as_f64(res["dW1"][e]), ref["dW1"][e]) <= 5e-3, f"dW1 expert {e}"
+    assert rel_fro(as_f64(res["out"]), ref["out"]) <= 5e-3

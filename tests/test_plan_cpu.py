@@ -27,7 +27,8 @@ def _dims(cfg):
 
 
 def _ws_fn(cfg, seg, mode=_lib.COMPACT_PHYSICAL):
-    """lrmoe_workspace_size at given quotas (the scratch the library asks for)."""
+    """The scratch the library asks for at given quotas: lrmoe_workspace_size plus the
+    selection's (token, slot) -> packed row map, int32 [T x K]."""
     dt = _lib.BF16 if cfg.dtype == "bf16" else _lib.F32
 
     def ws(q):
@@ -35,7 +36,7 @@ def _ws_fn(cfg, seg, mode=_lib.COMPACT_PHYSICAL):
                                            np.asarray(q, dtype=np.int32))
         n = ctypes.c_size_t(0)
         assert _lib.load().lrmoe_workspace_size(ctypes.byref(c), mode, ctypes.byref(n)) == _lib.OK
-        return int(n.value)
+        return int(n.value) + 4 * cfg.T * cfg.K
     return ws
 
 
@@ -126,7 +127,8 @@ def test_workspace_holds_the_split_reduction_partials():
         chunks = [-(-int(m) // 12288) for m in q if m > 12288]
         partials = sum(chunks) * tiles * 256 * 256 * 4
         ws = _ws_fn(cfg, seg)(q)
-        assert partials > 0 and partials <= ws <= partials + (1 << 20), (rho, partials, ws)
+        pmap = 4 * cfg.T * cfg.K
+        assert partials > 0 and partials + pmap <= ws <= partials + pmap + (1 << 20), (rho, partials, ws)
         c, keep = _lib.make_problem_struct(cfg.E, cfg.T, cfg.K, cfg.D, cfg.F, cfg.swiglu, _lib.BF16, seg,
                                            q.astype(np.int32))
         n = ctypes.c_size_t(0)

@@ -187,6 +187,23 @@ lrmoe_status lrmoe_select(const lrmoe_problem* p, const float* R, const int64_t*
                           uint8_t* keep, const int32_t* tok, const int32_t* slot, int32_t* pmap,
                           int32_t* ctok, int32_t* cslot, void* ws, size_t ws_bytes, lrmoe_stream_t stream);
 
+/* lrmoe_select without a workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments and results as lrmoe_select minus (ws, ws_bytes). Its scratch is a fixed
+ * 4 MiB array of the library's, one per GPU, held until the process ends; the call
+ * allocates and frees nothing. The stream's device must be the current device. The
+ * selection needs E x 8 KB of digit histograms, E x 16 B of segment state and 16 B per
+ * expert per 4096-pair chunk of the longest segment (each part rounded up to 256 B; about
+ * 150 KB for 16 experts of up to 200k pairs); a problem that needs more than 4 MiB is
+ * refused with LRMOE_ERR_WORKSPACE before any launch. The selection's first launch clears
+ * what it accumulates into, so a call does not depend on the previous call's contents.
+ * All calls on one GPU share the array: calls that overlap in time on one GPU (other
+ * streams, other host threads) race; calls in order on one stream do not. */
+lrmoe_status lrmoe_select_noalloc(const lrmoe_problem* p, const float* R, const int64_t* seg_off_d,
+                                  const int32_t* quota_d, const int64_t* cseg_off_d, int32_t* sel,
+                                  uint8_t* keep, const int32_t* tok, const int32_t* slot, int32_t* pmap,
+                                  int32_t* ctok, int32_t* cslot, lrmoe_stream_t stream);
+
 /* Step 3 - compaction (section 3.1 "compact runtime", section 3.4 / Figure 4).
  * PHYSICAL, for packed row c < K_tot with j = sel[c], t = tok[j]:
  *   Dlt[c]  = alpha[j] * G[t]   (weighted cotangent, Eq. 5; one rounding to the storage dtype,

@@ -179,6 +179,20 @@ def select(p: Problem, R, sel=None, keep=None, want_keep=True, tok=None, slot=No
     return out + ({"pmap": m["pmap"][:p.T * p.K], "ctok": m["ctok"][:p.K_tot], "cslot": m["cslot"][:p.K_tot]},)
 
 
+def select_noalloc(p: Problem, R, sel, keep=None, tok=None, slot=None, maps=None, stream=None):
+    """lrmoe_select_noalloc: step 2 with the library's fixed per-GPU scratch instead of a
+    workspace, for callers that cannot allocate. The caller passes every output (``sel``
+    [K_tot], optional ``keep`` [N]; with ``tok``/``slot`` also ``maps`` = {"pmap", "ctok",
+    "cslot"}); nothing is allocated here."""
+    m = maps if tok is not None else None
+    _lib.check(library().lrmoe_select_noalloc(ctypes.byref(p.c), _ptr(R), _ptr(p.seg_off_d), _ptr(p.quota_d),
+                                              _ptr(p.cseg_off_d), _ptr(sel), _ptr(keep), _ptr(tok), _ptr(slot),
+                                              _ptr(m["pmap"]) if m else None, _ptr(m["ctok"]) if m else None,
+                                              _ptr(m["cslot"]) if m else None, _stream(stream)),
+               "lrmoe_select_noalloc")
+    return sel, keep, m
+
+
 def compact(p: Problem, G, Phi, alpha, tok, slot, sel=None, keep=None, X=None, H=None,
             mode=COMPACT_PHYSICAL, out=None, pack_phi=True, maps=None, stream=None):
     """Always writes Dlt; ctok/cslot too unless ``maps`` (the map, ctok and cslot that

@@ -22,7 +22,8 @@ SCATTER_TOKEN, SCATTER_SLOT = 0, 1
 
 EXPORTS = ("lrmoe_status_string", "lrmoe_version", "lrmoe_validate", "lrmoe_workspace_size",
            "lrmoe_backward_bytes", "lrmoe_plan_quotas", "lrmoe_score", "lrmoe_score_criterion", "lrmoe_select",
-           "lrmoe_compact", "lrmoe_grouped_gemm_bwd", "lrmoe_scatter", "lrmoe_expert_forward")
+           "lrmoe_compact", "lrmoe_grouped_gemm_bwd", "lrmoe_scatter", "lrmoe_expert_forward",
+           "lrmoe_select_noalloc")
 
 
 class LrmoeError(RuntimeError):
@@ -68,6 +69,7 @@ def load() -> ctypes.CDLL:
         "lrmoe_score": [P, vp, vp, vp, vp, vp, vp, sz, vp],
         "lrmoe_score_criterion": [P, i32, vp, vp, vp, vp, vp, vp, sz, vp],
         "lrmoe_select": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp],
+        "lrmoe_select_noalloc": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
         "lrmoe_compact": [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                           ctypes.c_size_t, vp],
         "lrmoe_grouped_gemm_bwd": [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,

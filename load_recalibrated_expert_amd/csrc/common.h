@@ -112,6 +112,12 @@ lrmoe_status launch_select(const lrmoe_problem* p, const float* R, const int64_t
                            uint8_t* keep, const int32_t* tok, const int32_t* slot, int32_t* pmap,
                            int32_t* ctok, int32_t* cslot, void* ws, hipStream_t s);
 
+size_t select_noalloc_max_bytes();
+lrmoe_status launch_select_noalloc(const lrmoe_problem* p, const float* R, const int64_t* seg_off_d,
+                                   const int32_t* quota_d, const int64_t* cseg_off_d, int32_t* sel, uint8_t* keep,
+                                   const int32_t* tok, const int32_t* slot, int32_t* pmap, int32_t* ctok,
+                                   int32_t* cslot, hipStream_t s);
+
 lrmoe_status launch_compact(const lrmoe_problem* p, int64_t rows, bool masked, const int32_t* sel,
                             const uint8_t* keep, const void* G, const void* Phi, const void* X,
                             const void* H, const float* alpha, const int32_t* tok, const int32_t* slot,

@@ -211,6 +211,21 @@ lrmoe_status lrmoe_select(const lrmoe_problem* p, const float* R, const int64_t*
                        (hipStream_t)stream);
 }
 
+lrmoe_status lrmoe_select_noalloc(const lrmoe_problem* p, const float* R, const int64_t* seg_off_d,
+                                  const int32_t* quota_d, const int64_t* cseg_off_d, int32_t* sel, uint8_t* keep,
+                                  const int32_t* tok, const int32_t* slot, int32_t* pmap, int32_t* ctok,
+                                  int32_t* cslot, lrmoe_stream_t stream) {
+  int64_t K_tot = 0;
+  LRMOE_TRY(check_problem(p, &K_tot, nullptr));
+  if (!seg_off_d || !quota_d || !cseg_off_d) return LRMOE_ERR_INVALID_ARG;
+  if ((p->N > 0 && !R) || (K_tot > 0 && !sel)) return LRMOE_ERR_INVALID_ARG;
+  if (pmap && ((p->N > 0 && (!tok || !slot)) || (K_tot > 0 && (!ctok || !cslot)))) return LRMOE_ERR_INVALID_ARG;
+  if (!pmap && (ctok || cslot)) return LRMOE_ERR_INVALID_ARG;
+  if (select_ws_bytes(p) > select_noalloc_max_bytes()) return LRMOE_ERR_WORKSPACE;
+  return launch_select_noalloc(p, R, seg_off_d, quota_d, cseg_off_d, sel, keep, tok, slot, pmap, ctok, cslot,
+                               (hipStream_t)stream);
+}
+
 lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, const int32_t* sel,
                            const uint8_t* keep, const void* G, const void* Phi, const void* X, const void* H,
                            const float* alpha, const int32_t* tok, const int32_t* slot, void* Dlt, void* PhiC,

@@ -18,6 +18,7 @@
 // its token and slot in packed order (the init launch clears the map), so compaction and
 // the scatter need no map of their own.
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -378,6 +379,53 @@ lrmoe_status launch_select(const lrmoe_problem* p, const float* R, const int64_t
   select_offs_kernel<<<E, kSelThreads, 0, s>>>(seg_off_d, w, maxch);
   select_write_kernel<<<grid, kSelThreads, 0, s>>>(R, seg_off_d, cseg_off_d, w, maxch, K_tot, sel, keep, po);
   return launch_status();
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+
+namespace {
+
+// Scratch of the allocation-free selection (lrmoe_select_noalloc): a fixed array that every
+// GPU the library runs on holds until the process ends. Host code never passes the array's
+// name to a kernel: it is a host-side stand-in, not a device address. The device address is
+// fetched once per device, with that device current, and kept.
+constexpr size_t kNoAllocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on the first call on that device).
+lrmoe_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return LRMOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return LRMOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return LRMOE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return LRMOE_OK;
+}
+
+}  // namespace
+
+size_t select_noalloc_max_bytes() { return kNoAllocScratchBytes; }
+
+lrmoe_status launch_select_noalloc(const lrmoe_problem* p, const float* R, const int64_t* seg_off_d,
+                                   const int32_t* quota_d, const int64_t* cseg_off_d, int32_t* sel, uint8_t* keep,
+                                   const int32_t* tok, const int32_t* slot, int32_t* pmap, int32_t* ctok,
+                                   int32_t* cslot, hipStream_t s) {
+  if (select_ws_bytes(p) > kNoAllocScratchBytes) return LRMOE_ERR_WORKSPACE;
+  void* ptr = nullptr;
+  const lrmoe_status st = noalloc_scratch(&ptr);
+  if (st != LRMOE_OK) return st;
+  // the selection clears what it accumulates into (histograms, segment state) in its own
+  // first launch, so the previous call's contents do no harm
+  return launch_select(p, R, seg_off_d, quota_d, cseg_off_d, sel, keep, tok, slot, pmap, ctok, cslot, ptr, s);
 }
 
 }  // namespace lrmoe

@@ -211,3 +211,20 @@ def test_product_path_does_not_touch_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", text, re.M), f
                 assert "synth" not in re.findall(r"^\s*(?:import|from)\s+(\w+)", text, re.M), f
+
+
+def test_select_noalloc_refuses_problems_beyond_its_scratch():
+    """lrmoe_select_noalloc's fixed 4 MiB scratch holds E x 8 KB of digit histograms: 1100
+    experts need more, which is refused on the host before any launch; bad arguments are
+    refused as for lrmoe_select."""
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    counts = np.full(1100, 3)
+    p, keep = _problem(E=1100, T=4000, K=1, counts=counts, quota=np.ones(1100, dtype=np.int32))
+    assert lib.lrmoe_select_noalloc(ctypes.byref(p), fake, fake, fake, fake, fake, None, None, None, None, None,
+                                    None, None) == _lib.ERR_WORKSPACE
+    q, keep2 = _problem()
+    assert lib.lrmoe_select_noalloc(ctypes.byref(q), None, fake, fake, fake, fake, None, None, None, None, None,
+                                    None, None) == _lib.ERR_INVALID_ARG
+    assert lib.lrmoe_select_noalloc(ctypes.byref(q), fake, fake, fake, fake, fake, None, None, None, None, fake,
+                                    None, None) == _lib.ERR_INVALID_ARG

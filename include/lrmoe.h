@@ -117,8 +117,11 @@ lrmoe_status lrmoe_validate(const lrmoe_problem* p, int64_t* K_tot, int64_t* cse
  * chunk counts; the (token, slot) -> packed row map int32 [T x K] of compaction and
  * scatter; the grouped GEMM's weight-gradient plan plus its split-K partials, one
  * 256 x 256 fp32 tile per (chunk, weight-gradient tile) of every expert whose rows (the
- * retained rows q_e, or n_e when zero-masked) exceed 12288 and are cut into chunks of at
- * most 12288. The partials dominate at large quotas, so the size depends on them. */
+ * retained rows q_e, or n_e when zero-masked) are cut into more than one chunk. Chunks hold
+ * at most 12288 rows, or 8192 or 6144 when the library's schedule model finds that one
+ * expert's long chunks would leave the GPU's eight XCDs unevenly loaded (a deterministic
+ * function of the row counts). The partials dominate at large quotas, so the size depends
+ * on them. */
 lrmoe_status lrmoe_workspace_size(const lrmoe_problem* p, lrmoe_compact_mode mode, size_t* bytes);
 
 /* Host-only. Device bytes one physical-compaction backward holds at p's quotas, besides

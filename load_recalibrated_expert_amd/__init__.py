@@ -79,16 +79,20 @@ class Problem:
         self.quota_d = torch.from_numpy(self.quota).to(self.device)
         self.cseg_off_d = torch.from_numpy(self.cseg_off).to(self.device)
         self._ws = None
+        self._ws_size = {}
 
     @property
     def torch_dtype(self):
         return torch.bfloat16 if self.dtype == BF16 else torch.float32
 
     def workspace_size(self, mode=COMPACT_PHYSICAL) -> int:
-        n = ctypes.c_size_t(0)
-        _lib.check(library().lrmoe_workspace_size(ctypes.byref(self.c), mode, ctypes.byref(n)),
-                   "lrmoe_workspace_size")
-        return int(n.value)
+        """lrmoe_workspace_size, asked once per mode (the quotas are fixed for the problem)."""
+        if mode not in self._ws_size:
+            n = ctypes.c_size_t(0)
+            _lib.check(library().lrmoe_workspace_size(ctypes.byref(self.c), mode, ctypes.byref(n)),
+                       "lrmoe_workspace_size")
+            self._ws_size[mode] = int(n.value)
+        return self._ws_size[mode]
 
     def workspace(self, mode=COMPACT_PHYSICAL) -> torch.Tensor:
         """The problem's scratch buffer, large enough for every call in ``mode`` (it grows

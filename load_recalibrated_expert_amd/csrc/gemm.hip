@@ -25,6 +25,7 @@
 // f32 path (small problems): plain fp32 FMA kernels, no bf16 anywhere.
 #include <algorithm>
 #include <functional>
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -61,7 +62,9 @@ using CfgD = TileCfg<8, 256, 4>;  // data gradients
 constexpr int BN = CfgW::BN, STAGES = CfgW::STAGES;
 // threads of the small kernels (plan, split-K reduction, f32 path)
 constexpr int kAuxThr = 512;
-constexpr int64_t kKcMax = 12288;          // max packed rows per weight-gradient chunk
+// Candidate lengths (packed rows) of a weight-gradient chunk, the longest first; the host
+// picks one per problem (wgrad_schedule)
+constexpr int64_t kKcCandidates[] = {12288, 8192, 6144};
 constexpr uint32_t kOOB = 0x80000000u;     // buffer offset past num_records: the load returns 0
 
 // Kernel attributes of a block of C::NWAVE wavefronts: with one wavefront per SIMD the
@@ -804,6 +807,7 @@ struct WgradArgs {
   int64_t* plan_pbase;  // [E] first partial tile of expert e (split experts only)
   float* partials;      // [npartials x BM x BN]
   int accumulate;
+  int64_t kc_max;       // longest chunk (packed rows), chosen by the host
   // Items (planned order) of XCD x: [xlo[x], xlo[x+1]). The ranges are contiguous, so the
   // tiles sharing operand panels stay in one L2, and cut so every XCD gets the same number
   // of K steps: items are sorted by decreasing length, so equal item counts would hand the
@@ -811,13 +815,13 @@ struct WgradArgs {
   int xlo[9];
 };
 
-__host__ __device__ inline void expert_split(int64_t m, int& s, int& kc) {
+__host__ __device__ inline void expert_split(int64_t m, int64_t kc_max, int& s, int& kc) {
   if (m <= 0) {
     s = 1;
     kc = 0;
     return;
   }
-  const int64_t sc = (m + kKcMax - 1) / kKcMax;
+  const int64_t sc = (m + kc_max - 1) / kc_max;
   const int64_t per = (m + sc - 1) / sc;
   s = (int)sc;
   kc = (int)((per + BK - 1) / BK * BK);
@@ -829,7 +833,7 @@ __global__ __launch_bounds__(kAuxThr) void wgrad_plan_kernel(WgradArgs g) {
   const int tiles = g.t[0].tiles + (g.ntypes > 1 ? g.t[1].tiles : 0);
   for (int e = threadIdx.x; e < E; e += kAuxThr) {
     int s, kc;
-    expert_split(g.row_off[e + 1] - g.row_off[e], s, kc);
+    expert_split(g.row_off[e + 1] - g.row_off[e], g.kc_max, s, kc);
     g.plan_s[e] = s;
     g.plan_kc[e] = kc;
   }
@@ -1070,12 +1074,12 @@ struct WgradLayout {
 
 int wgrad_tiles(int M, int N) { return (int)(ceil_div(M, BM) * ceil_div(N, BN)); }
 
-WgradLayout wgrad_layout(const lrmoe_problem* p, const int64_t* row_off_h) {
+WgradLayout wgrad_layout(const lrmoe_problem* p, const int64_t* row_off_h, int64_t kc_max) {
   const int tiles = wgrad_tiles(p->F, p->D) + (p->swiglu ? wgrad_tiles(p->D, 2 * p->F) : 0);
   WgradLayout L{};
   for (int e = 0; e < p->E; ++e) {
     const int64_t m = row_off_h[e + 1] - row_off_h[e];
-    const int64_t s = m <= 0 ? 1 : ceil_div(m, kKcMax);
+    const int64_t s = m <= 0 ? 1 : ceil_div(m, kc_max);
     L.nitems += s * tiles;
     if (s > 1) {
       L.npartials += s * tiles;
@@ -1087,21 +1091,28 @@ WgradLayout wgrad_layout(const lrmoe_problem* p, const int64_t* row_off_h) {
   return L;
 }
 
-// Splits the weight-gradient items, in the order the plan kernel gives them (experts by
-// decreasing chunk length, ties by id; chunk-major within an expert), into 8 contiguous
-// ranges, one per XCD. An item costs its K steps plus 8 for its prologue and epilogue. The
-// split minimises the largest range's finishing time when its 32 CUs take items in order
-// as they free up: a bisection on that time, each probe filling the ranges greedily.
-// Returns the largest range's item count. Any monotone split covers every item exactly
-// once, so the split only affects balance, never results.
-int64_t wgrad_xcd_ranges(const lrmoe_problem* p, const int64_t* row_off_h, int (&xlo)[9]) {
+// The weight-gradient schedule of one problem: the chunk length and the items' split into 8
+// contiguous ranges, one per XCD (hardware sends block i to XCD i % 8).
+struct WgradSchedule {
+  int64_t kc_max;
+  int xlo[9];
+  int64_t per_xcd;  // items of the largest range
+};
+
+// Items in the order the plan kernel gives them (experts by decreasing chunk length, ties by
+// id; chunk-major within an expert), cut into 8 contiguous ranges. An item costs its K steps
+// plus 8 for its prologue and epilogue. The cut minimises the largest range's finishing time
+// when its 32 CUs take items in order as they free up: a bisection on that time, each probe
+// filling the ranges greedily. Returns that time. Any monotone split covers every item
+// exactly once, so the split only affects balance, never results.
+int64_t wgrad_xcd_ranges(const lrmoe_problem* p, const int64_t* row_off_h, int64_t kc_max, int (&xlo)[9]) {
   constexpr int kXcd = 8, kCuPerXcd = 32;
   const int E = p->E;
   const int tiles = wgrad_tiles(p->F, p->D) + (p->swiglu ? wgrad_tiles(p->D, 2 * p->F) : 0);
   std::vector<int> order(E), S(E), KC(E);
   for (int e = 0; e < E; ++e) {
     order[e] = e;
-    expert_split(row_off_h[e + 1] - row_off_h[e], S[e], KC[e]);
+    expert_split(row_off_h[e + 1] - row_off_h[e], kc_max, S[e], KC[e]);
   }
   std::sort(order.begin(), order.end(), [&](int a, int b) { return KC[a] != KC[b] ? KC[a] > KC[b] : a < b; });
   std::vector<int64_t> cost;  // per item, planned order
@@ -1134,7 +1145,12 @@ int64_t wgrad_xcd_ranges(const lrmoe_problem* p, const int64_t* row_off_h, int (
     }
     return i == n;
   };
-  int64_t lo_t = std::max(longest, ceil_div(total, (int64_t)kXcd * kCuPerXcd)), hi_t = total;
+  // bracket the answer by doubling from its lower bound (it is rarely far above it), then bisect
+  int64_t lo_t = std::max(longest, ceil_div(total, (int64_t)kXcd * kCuPerXcd)), hi_t = lo_t;
+  for (int tmp[9]; !fill(hi_t, tmp);) {
+    lo_t = hi_t + 1;
+    hi_t = std::min(total, 2 * hi_t);
+  }
   while (lo_t < hi_t) {
     const int64_t mid = lo_t + (hi_t - lo_t) / 2;
     int tmp[9];
@@ -1142,9 +1158,56 @@ int64_t wgrad_xcd_ranges(const lrmoe_problem* p, const int64_t* row_off_h, int (
     else lo_t = mid + 1;
   }
   fill(lo_t, xlo);
-  int64_t mx = 0;
-  for (int x = 0; x < kXcd; ++x) mx = std::max<int64_t>(mx, xlo[x + 1] - xlo[x]);
-  return mx;
+  return lo_t;
+}
+
+// Chooses the chunk length among kKcCandidates: contiguous XCD ranges balance well only when
+// the items are small against a range, so one dominant expert (most of the retained rows)
+// gets shorter chunks, while shorter chunks cost partial tiles that the split-K reduction
+// streams. Modelled time, in K steps per CU: the ranges' finishing time plus 1/16 step per
+// partial tile (a 256 x 256 fp32 tile written once and read once, over the whole chip).
+WgradSchedule wgrad_schedule_compute(const lrmoe_problem* p, const int64_t* row_off_h) {
+  WgradSchedule best{};
+  int64_t best_cost = -1;
+  for (int64_t kc : kKcCandidates) {
+    WgradSchedule w{};
+    w.kc_max = kc;
+    const int64_t t = wgrad_xcd_ranges(p, row_off_h, kc, w.xlo);
+    const int64_t cost = t + wgrad_layout(p, row_off_h, kc).npartials / 16;
+    if (best_cost < 0 || cost < best_cost) {
+      best = w;
+      best_cost = cost;
+    }
+  }
+  for (int x = 0; x < 8; ++x) best.per_xcd = std::max<int64_t>(best.per_xcd, best.xlo[x + 1] - best.xlo[x]);
+  return best;
+}
+
+// The schedule costs about a millisecond of host time for a 128-expert layer, and a training
+// loop asks for the same routing's schedule several times (workspace size, then the launch),
+// so the last few are kept, keyed by everything the schedule reads.
+WgradSchedule wgrad_schedule(const lrmoe_problem* p, const int64_t* row_off_h) {
+  constexpr int kKeep = 8;
+  struct Entry {
+    std::vector<int64_t> key;
+    WgradSchedule sched;
+  };
+  static std::mutex mu;
+  static Entry memo[kKeep];
+  static int next = 0;
+  std::vector<int64_t> key = {p->E, p->D, p->F, p->swiglu};
+  key.reserve(4 + (size_t)p->E);
+  for (int e = 0; e < p->E; ++e) key.push_back(row_off_h[e + 1] - row_off_h[e]);
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    for (const Entry& m : memo)
+      if (m.key == key) return m.sched;
+  }
+  const WgradSchedule w = wgrad_schedule_compute(p, row_off_h);
+  std::lock_guard<std::mutex> lk(mu);
+  memo[next] = Entry{std::move(key), w};
+  next = (next + 1) % kKeep;
+  return w;
 }
 
 }  // namespace
@@ -1178,7 +1241,7 @@ lrmoe_status launch_expert_forward(const lrmoe_problem* p, const int64_t* seg_of
 
 size_t gemm_ws_bytes(const lrmoe_problem* p, const int64_t* row_off_h) {
   if (p->dtype != LRMOE_BF16) return 0;
-  const WgradLayout L = wgrad_layout(p, row_off_h);
+  const WgradLayout L = wgrad_layout(p, row_off_h, wgrad_schedule(p, row_off_h).kc_max);
   return L.plan_bytes + L.partial_bytes;
 }
 
@@ -1272,7 +1335,8 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
   }
   if (mark_din() != LRMOE_OK) return LRMOE_ERR_HIP;
 
-  const WgradLayout L = wgrad_layout(p, row_off_h);
+  const WgradSchedule sched = wgrad_schedule(p, row_off_h);
+  const WgradLayout L = wgrad_layout(p, row_off_h, sched.kc_max);
   WgradArgs w{};
   w.t[0] = WgradType{(const uint16_t*)PhiC, F, phi_rows, phi_nrows, (const uint16_t*)Dlt, D, dW2, F, D,
                      (int)ceil_div(F, BM), (int)ceil_div(D, BN), wgrad_tiles(F, D)};
@@ -1292,8 +1356,10 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
   w.plan_pbase = (int64_t*)(b + align_up(sizeof(int) * (4 * (size_t)E + 1), 8));
   w.partials = (float*)(b + L.plan_bytes);
   w.accumulate = accumulate;
+  w.kc_max = sched.kc_max;
+  for (int x = 0; x < 9; ++x) w.xlo[x] = sched.xlo[x];
   if (E > 0) {
-    const int64_t per_xcd = wgrad_xcd_ranges(p, row_off_h, w.xlo);
+    const int64_t per_xcd = sched.per_xcd;
     wgrad_plan_kernel<<<1, kAuxThr, 0, s>>>(w);
     const unsigned grid = (unsigned)(8 * per_xcd);
     const bool g0 = phi_rows != nullptr, g1 = x_rows != nullptr;

@@ -135,3 +135,29 @@ def test_workspace_holds_the_split_reduction_partials():
         assert _lib.load().lrmoe_backward_bytes(ctypes.byref(c), 0, ctypes.byref(n)) == _lib.OK
         bufs = oracle.backward_bytes(E=cfg.E, N=int(seg[-1]), K_tot=int(q.sum()), **_dims(cfg))
         assert n.value == bufs + ws
+
+
+
+def _partials_bytes(cfg, q, kc):
+    tiles = -(-cfg.F // 256) * -(-cfg.D // 256) + -(-cfg.D // 256) * -(-2 * cfg.F // 256)
+    return sum(-(-int(m) // kc) for m in q if m > kc) * tiles * 256 * 256 * 4
+
+
+@pytest.mark.parametrize("name,rho,kc", [("qwen3_30b_a3b_share", "0.6", 12288),
+                                         ("glm45_106b_a12b_share", "0.6", 12288),
+                                         ("glm_quota_sweep", "1.0", 12288),
+                                         ("extreme_skew", "0.4", 8192)])
+def test_chunk_length_follows_the_expert_balance(name, rho, kc):
+    """The weight-gradient chunk length is 12288 rows unless one expert's long chunks would
+    load the eight XCDs unevenly: with 70% of the retained rows in one expert (the
+    extreme-skew routing) 8192-row chunks win despite their extra partial tiles. The
+    workspace holds the partials of exactly the chosen length (plus the map and under 1 MiB
+    of plan and compaction scratch), so its size tells which length was taken."""
+    cfg = synth.CONFIGS[name]
+    counts = np.diff(synth.make_routing(cfg).seg_off).astype(np.int64)
+    seg = np.concatenate([[0], np.cumsum(counts)])
+    q = oracle.ceil_quotas(counts, rho)
+    ws = _ws_fn(cfg, seg)(q)
+    pmap = 4 * cfg.T * cfg.K
+    fits = [c for c in (12288, 8192, 6144) if 0 <= ws - pmap - _partials_bytes(cfg, q, c) <= (1 << 20)]
+    assert fits == [kc], (ws, fits)

@@ -5,6 +5,8 @@ backward -> scatter) over one layer invocation of the workload, inputs resident 
 HBM. Prints ONE JSON line. Default workload: the Qwen3-30B-A3B-shaped single-GPU
 expert share (32,768 tokens x top-8 = 262,144 pairs over 16 local experts, D=2048,
 intermediate 768, retention 0.6, bf16 with fp32 accumulation), seeded synthetic data.
+The line also carries an object timing the GLM4.5-106B-A12B-shaped share the same way
+(GPU timing and roofline only), unless --second none.
 """
 from __future__ import annotations
 
@@ -33,6 +35,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="qwen3_30b_a3b_share")
     ap.add_argument("--rho", default=None)
+    ap.add_argument("--second", default="glm45_106b_a12b_share",
+                    help="a second workload timed after the first (GPU timing and roofline only, no oracle), "
+                         "reported as an object of its own; 'none' skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-masked", action="store_true")
     ap.add_argument("--overlap", action="store_true",
@@ -84,6 +89,12 @@ def algorithmic_bytes(cfg, N, K_tot, packed=False, criterion="lrm"):
     width = D if cfg.swiglu else F
     scatter = K_tot * width * e + T * width * 4
     return {"score": score, "compact": compact, "scatter": scatter}
+
+
+def profile_key(cfg, rho):
+    """Name of a workload's profiles: the config, plus the retention ratio when it is not the
+    config's first one (the quota sweep's other ratios)."""
+    return cfg.name if str(rho) == str(cfg.rhos[0]) else f"{cfg.name}_rho{rho}"
 
 
 def recorded_traffic(workload):
@@ -216,138 +227,149 @@ def main():
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[args.config]
     rho = args.rho or cfg.rhos[0]
-    t0 = time.time()
-    pr = synth.make_problem(cfg, rho=rho)
-    gen_s = time.time() - t0
-    r = pr.routing
-    dt = cfg.dtype
-    P = lr.Problem(E=cfg.E, T=cfg.T, K=cfg.K, D=cfg.D, F=cfg.F, swiglu=cfg.swiglu,
-                   dtype=lr.BF16 if dt == "bf16" else lr.F32, seg_off=r.seg_off, quota=pr.quota, device=dev)
-    T_ = lambda a: to_dev(np, torch, a, dt, dev)  # noqa: E731
-    ins = dict(G=T_(pr.G), Phi=T_(pr.Phi), W2=T_(pr.W2), X=T_(pr.X) if pr.X is not None else None,
-               H=T_(pr.H) if pr.H is not None else None, W1=T_(pr.W1) if pr.W1 is not None else None,
-               alpha=torch.from_numpy(r.alpha).to(dev), tok=torch.from_numpy(r.tok).to(dev),
-               slot=torch.from_numpy(r.slot).to(dev))
-    print(f"# workload {cfg.name} rho={rho} N={P.N} K_tot={P.K_tot} generated in {gen_s:.1f}s", file=sys.stderr,
-          flush=True)
-
-    if args.copy_calib_mib > 0:
-        n = args.copy_calib_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
     overlap = args.overlap
 
-    def run(mode, bufs, timing=None):
-        """One step; with `timing`, HIP events bracket each step's call on the stream it runs on
-        (the scatter's on the second stream when it overlaps the weight gradients)."""
-        G, Phi, alpha, tok, slot = ins["G"], ins["Phi"], ins["alpha"], ins["tok"], ins["slot"]
-        main = torch.cuda.current_stream()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)] if timing is not None else None
-        rec = (lambda i, s=None: ev[i].record(s if s is not None else main)) if ev else (lambda i, s=None: None)
-        if overlap and "side" not in bufs:
-            bufs["side"] = torch.cuda.Stream(device=dev)
-            bufs["din_ready"] = torch.cuda.Event()
-            bufs["side_ws"] = torch.empty_like(P.workspace())
-            bufs["out"] = torch.empty(P.T, cfg.D if cfg.swiglu else cfg.F, dtype=torch.float32, device=dev)
-        rec(0)
-        if args.criterion == "random":  # uniform draws made once on the host: the scores are an input
-            if "R" not in bufs:
-                bufs["R"] = torch.from_numpy(np.random.default_rng(cfg.seed).random(P.N).astype(np.float32)).to(dev)
-            R = bufs["R"]
-        else:
-            crit_lrm = args.criterion == "lrm"
-            R = lr.score(P, G, Phi if crit_lrm else None, alpha if crit_lrm else None, tok, R=bufs.get("R"),
-                         criterion=args.criterion)
-            bufs["R"] = R
-        rec(1)
-        phys = mode == lr.COMPACT_PHYSICAL
-        maps = None
-        if phys:  # the selection writes the (token, slot) map that compaction and the scatter use
-            sel, keep, maps = lr.select(P, R, sel=bufs.get("sel"), keep=bufs.get("keep"), tok=tok, slot=slot,
-                                        maps=bufs.get("maps"))
-            bufs.setdefault("maps", maps)
-        else:
-            sel, keep = lr.select(P, R, sel=bufs.get("sel"), keep=bufs.get("keep"))
-        bufs.setdefault("sel", sel)
-        bufs.setdefault("keep", keep)
-        rec(2)
-        c = lr.compact(P, G, Phi, alpha, tok, slot, sel=sel, keep=keep, X=ins["X"] if args.packed else None,
-                       mode=mode, out=bufs.get("c"), pack_phi=args.packed, maps=maps)
-        bufs.setdefault("c", c)
-        rec(3)
-        ctok, cslot = (c["ctok"], c["cslot"]) if phys else (tok, slot)
-        hc_rows = sel if (phys and cfg.swiglu) else None
-        if args.packed:
-            PhiC, XC, phi_rows, x_rows = (c["PhiC"] if phys else Phi), c.get("XC"), None, None
-        else:  # Phi and X read in place: pair rows through sel, token rows through ctok (tok)
-            PhiC, XC = Phi, ins["X"]
-            phi_rows = sel if phys else None
-            x_rows = ctok if cfg.swiglu else None
-        g = lr.grouped_gemm_bwd(P, c["Dlt"], PhiC, ins["W2"], XC=XC, HC=ins["H"], W1=ins["W1"], mode=mode,
-                                out=bufs.get("g"), hc_rows=hc_rows, phi_rows=phi_rows, x_rows=x_rows,
-                                din_ready=bufs["din_ready"] if overlap else None)
-        bufs.setdefault("g", g)
-        rec(4)
-        if overlap:  # the scatter runs under the weight gradients, on the second stream
-            side = bufs["side"]
-            side.wait_event(bufs["din_ready"])
-            rec(6, side)
-            lr.scatter(P, g["dIn"], ctok, cslot, n_rows=P.rows(mode), out=bufs["out"], ws=bufs["side_ws"],
-                       pmap=maps["pmap"] if maps else None, stream=side)
-            rec(7, side)
-            main.wait_stream(side)
-        else:
-            out = lr.scatter(P, g["dIn"], ctok, cslot, n_rows=P.rows(mode), out=bufs.get("out"),
-                             pmap=maps["pmap"] if maps else None)
-            bufs.setdefault("out", out)
-        rec(5)
-        if ev:
-            timing.append(ev)
+    def workload(cfg, rho):
+        """Times one workload's step on the GPU; returns its measurements and the closures the
+        optional extra timings reuse."""
+        t0 = time.time()
+        pr = synth.make_problem(cfg, rho=rho)
+        gen_s = time.time() - t0
+        r = pr.routing
+        dt = cfg.dtype
+        P = lr.Problem(E=cfg.E, T=cfg.T, K=cfg.K, D=cfg.D, F=cfg.F, swiglu=cfg.swiglu,
+                       dtype=lr.BF16 if dt == "bf16" else lr.F32, seg_off=r.seg_off, quota=pr.quota, device=dev)
+        T_ = lambda a: to_dev(np, torch, a, dt, dev)  # noqa: E731
+        ins = dict(G=T_(pr.G), Phi=T_(pr.Phi), W2=T_(pr.W2), X=T_(pr.X) if pr.X is not None else None,
+                   H=T_(pr.H) if pr.H is not None else None, W1=T_(pr.W1) if pr.W1 is not None else None,
+                   alpha=torch.from_numpy(r.alpha).to(dev), tok=torch.from_numpy(r.tok).to(dev),
+                   slot=torch.from_numpy(r.slot).to(dev))
+        print(f"# workload {cfg.name} rho={rho} N={P.N} K_tot={P.K_tot} generated in {gen_s:.1f}s", file=sys.stderr,
+              flush=True)
 
-    def measure(mode):
-        bufs = {}
-        for _ in range(args.warmup):
-            run(mode, bufs)
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        for _ in range(args.steps):
-            run(mode, bufs)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t
-        # second pass: per-step HIP events (same stream as the launches)
-        timing = []
-        for _ in range(args.steps):
-            run(mode, bufs, timing)
-        torch.cuda.synchronize()
-        names = ["score", "select", "compact", "grouped_gemm_bwd", "scatter"]
-        per = {n: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in timing])) for i, n in enumerate(names)}
-        if overlap:
-            per["scatter"] = float(np.mean([ev[6].elapsed_time(ev[7]) for ev in timing]))
-        return wall, per, bufs
+        if args.copy_calib_mib > 0:
+            n = args.copy_calib_mib << 20
+            src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
 
-    wall, per, phys_bufs = measure(lr.COMPACT_PHYSICAL)
+        def run(mode, bufs, timing=None):
+            """One step; with `timing`, HIP events bracket each step's call on the stream it runs on
+            (the scatter's on the second stream when it overlaps the weight gradients)."""
+            G, Phi, alpha, tok, slot = ins["G"], ins["Phi"], ins["alpha"], ins["tok"], ins["slot"]
+            main = torch.cuda.current_stream()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)] if timing is not None else None
+            rec = (lambda i, s=None: ev[i].record(s if s is not None else main)) if ev else (lambda i, s=None: None)
+            if overlap and "side" not in bufs:
+                bufs["side"] = torch.cuda.Stream(device=dev)
+                bufs["din_ready"] = torch.cuda.Event()
+                bufs["side_ws"] = torch.empty_like(P.workspace())
+                bufs["out"] = torch.empty(P.T, cfg.D if cfg.swiglu else cfg.F, dtype=torch.float32, device=dev)
+            rec(0)
+            if args.criterion == "random":  # uniform draws made once on the host: the scores are an input
+                if "R" not in bufs:
+                    bufs["R"] = torch.from_numpy(np.random.default_rng(cfg.seed).random(P.N).astype(np.float32)).to(dev)
+                R = bufs["R"]
+            else:
+                crit_lrm = args.criterion == "lrm"
+                R = lr.score(P, G, Phi if crit_lrm else None, alpha if crit_lrm else None, tok, R=bufs.get("R"),
+                             criterion=args.criterion)
+                bufs["R"] = R
+            rec(1)
+            phys = mode == lr.COMPACT_PHYSICAL
+            maps = None
+            if phys:  # the selection writes the (token, slot) map that compaction and the scatter use
+                sel, keep, maps = lr.select(P, R, sel=bufs.get("sel"), keep=bufs.get("keep"), tok=tok, slot=slot,
+                                            maps=bufs.get("maps"))
+                bufs.setdefault("maps", maps)
+            else:
+                sel, keep = lr.select(P, R, sel=bufs.get("sel"), keep=bufs.get("keep"))
+            bufs.setdefault("sel", sel)
+            bufs.setdefault("keep", keep)
+            rec(2)
+            c = lr.compact(P, G, Phi, alpha, tok, slot, sel=sel, keep=keep, X=ins["X"] if args.packed else None,
+                           mode=mode, out=bufs.get("c"), pack_phi=args.packed, maps=maps)
+            bufs.setdefault("c", c)
+            rec(3)
+            ctok, cslot = (c["ctok"], c["cslot"]) if phys else (tok, slot)
+            hc_rows = sel if (phys and cfg.swiglu) else None
+            if args.packed:
+                PhiC, XC, phi_rows, x_rows = (c["PhiC"] if phys else Phi), c.get("XC"), None, None
+            else:  # Phi and X read in place: pair rows through sel, token rows through ctok (tok)
+                PhiC, XC = Phi, ins["X"]
+                phi_rows = sel if phys else None
+                x_rows = ctok if cfg.swiglu else None
+            g = lr.grouped_gemm_bwd(P, c["Dlt"], PhiC, ins["W2"], XC=XC, HC=ins["H"], W1=ins["W1"], mode=mode,
+                                    out=bufs.get("g"), hc_rows=hc_rows, phi_rows=phi_rows, x_rows=x_rows,
+                                    din_ready=bufs["din_ready"] if overlap else None)
+            bufs.setdefault("g", g)
+            rec(4)
+            if overlap:  # the scatter runs under the weight gradients, on the second stream
+                side = bufs["side"]
+                side.wait_event(bufs["din_ready"])
+                rec(6, side)
+                lr.scatter(P, g["dIn"], ctok, cslot, n_rows=P.rows(mode), out=bufs["out"], ws=bufs["side_ws"],
+                           pmap=maps["pmap"] if maps else None, stream=side)
+                rec(7, side)
+                main.wait_stream(side)
+            else:
+                out = lr.scatter(P, g["dIn"], ctok, cslot, n_rows=P.rows(mode), out=bufs.get("out"),
+                                 pmap=maps["pmap"] if maps else None)
+                bufs.setdefault("out", out)
+            rec(5)
+            if ev:
+                timing.append(ev)
+
+        def measure(mode):
+            bufs = {}
+            for _ in range(args.warmup):
+                run(mode, bufs)
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            for _ in range(args.steps):
+                run(mode, bufs)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t
+            # second pass: per-step HIP events (same stream as the launches)
+            timing = []
+            for _ in range(args.steps):
+                run(mode, bufs, timing)
+            torch.cuda.synchronize()
+            names = ["score", "select", "compact", "grouped_gemm_bwd", "scatter"]
+            per = {n: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in timing])) for i, n in enumerate(names)}
+            if overlap:
+                per["scatter"] = float(np.mean([ev[6].elapsed_time(ev[7]) for ev in timing]))
+            return wall, per, bufs
+
+        wall, per, phys_bufs = measure(lr.COMPACT_PHYSICAL)
+        bytes_ = algorithmic_bytes(cfg, P.N, P.K_tot, packed=args.packed, criterion=args.criterion)
+        fl = gemm_flops(cfg, P.K_tot)
+        peak = BF16_PEAK_TFLOPS if dt == "bf16" else FP32_PEAK_TFLOPS
+        gemm_tf = fl / (per["grouped_gemm_bwd"] * 1e-3) / 1e12
+        kernels = {
+            "score": ({"ms": per["score"], "GB/s": bytes_["score"] / per["score"] / 1e6,
+                       "hbm_frac": bytes_["score"] / per["score"] / 1e6 / HBM_PEAK_GBS} if bytes_["score"] else
+                      {"ms": per["score"], "note": "no score kernel: uniform draws made once on the host"}),
+            "select": {"ms": per["select"]},
+            "compact": {"ms": per["compact"], "GB/s": bytes_["compact"] / per["compact"] / 1e6,
+                        "hbm_frac": bytes_["compact"] / per["compact"] / 1e6 / HBM_PEAK_GBS},
+            "grouped_gemm_bwd": {"ms": per["grouped_gemm_bwd"], "TFLOP/s": gemm_tf, "mfma_frac": gemm_tf / peak},
+            "scatter": {"ms": per["scatter"], "GB/s": bytes_["scatter"] / per["scatter"] / 1e6,
+                        "hbm_frac": bytes_["scatter"] / per["scatter"] / 1e6 / HBM_PEAK_GBS},
+        }
+        return dict(pr=pr, P=P, ins=ins, measure=measure, wall=wall, per=per, phys_bufs=phys_bufs,
+                    kernels=kernels, gemm_tf=gemm_tf, fl=fl, peak=peak, gen_s=gen_s)
+
+    W = workload(cfg, rho)
+    pr, P, ins, measure, wall, per, phys_bufs = (W[k] for k in ("pr", "P", "ins", "measure", "wall", "per",
+                                                                 "phys_bufs"))
+    kernels, gemm_tf, fl, peak = W["kernels"], W["gemm_tf"], W["fl"], W["peak"]
     ms = wall / args.steps * 1e3
     value = P.K_tot * args.steps / wall
-    bytes_ = algorithmic_bytes(cfg, P.N, P.K_tot, packed=args.packed, criterion=args.criterion)
-    fl = gemm_flops(cfg, P.K_tot)
-    peak = BF16_PEAK_TFLOPS if dt == "bf16" else FP32_PEAK_TFLOPS
-    gemm_tf = fl / (per["grouped_gemm_bwd"] * 1e-3) / 1e12
-    kernels = {
-        "score": ({"ms": per["score"], "GB/s": bytes_["score"] / per["score"] / 1e6,
-                   "hbm_frac": bytes_["score"] / per["score"] / 1e6 / HBM_PEAK_GBS} if bytes_["score"] else
-                  {"ms": per["score"], "note": "no score kernel: uniform draws made once on the host"}),
-        "select": {"ms": per["select"]},
-        "compact": {"ms": per["compact"], "GB/s": bytes_["compact"] / per["compact"] / 1e6,
-                    "hbm_frac": bytes_["compact"] / per["compact"] / 1e6 / HBM_PEAK_GBS},
-        "grouped_gemm_bwd": {"ms": per["grouped_gemm_bwd"], "TFLOP/s": gemm_tf, "mfma_frac": gemm_tf / peak},
-        "scatter": {"ms": per["scatter"], "GB/s": bytes_["scatter"] / per["scatter"] / 1e6,
-                    "hbm_frac": bytes_["scatter"] / per["scatter"] / 1e6 / HBM_PEAK_GBS},
-    }
+    dt = cfg.dtype
     result = {
         "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -357,7 +379,7 @@ def main():
                    "mode": "physical compaction", "criterion": args.criterion,
                    "scatter": "second stream, under the weight gradients" if overlap else "after the GEMM call"},
         "roofline": {"bound": "mfma", "achieved": gemm_tf, "peak": peak, "unit": "TFLOP/s",
-                     "frac": gemm_tf / peak, "traffic": recorded_traffic(cfg.name),
+                     "frac": gemm_tf / peak, "traffic": recorded_traffic(profile_key(cfg, rho)),
                      "kernel": "lrmoe_grouped_gemm_bwd (FC2 dgrad+SwiGLU, FC1 dgrad, FC1+FC2 wgrad launches)",
                      "flops_per_launch": fl},
         "kernels": kernels,
@@ -405,6 +427,22 @@ def main():
             "note": "FC1 with the SwiGLU forward fused, FC2 scaled by the routing weight, over all N pairs; "
                     "then the token combine (scatter)",
         }
+    if args.second != "none" and args.second != cfg.name:
+        # the pages' second model shape, GPU timing only (no oracle run at this size)
+        c2 = synth.CONFIGS[args.second]
+        W2_ = workload(c2, c2.rhos[0])
+        P2 = W2_["P"]
+        result[args.second] = {
+            "workload": c2.name, "rho": c2.rhos[0], "pairs": P2.N, "retained_pairs": P2.K_tot,
+            "steps": args.steps, "ms_per_step": W2_["wall"] / args.steps * 1e3,
+            "value": P2.K_tot * args.steps / W2_["wall"], "unit": "pairs/s",
+            "roofline": {"bound": "mfma", "achieved": W2_["gemm_tf"], "peak": W2_["peak"], "unit": "TFLOP/s",
+                         "frac": W2_["gemm_tf"] / W2_["peak"],
+                         "traffic": recorded_traffic(profile_key(c2, c2.rhos[0])),
+                         "flops_per_launch": W2_["fl"]},
+            "kernels": W2_["kernels"],
+        }
+        del W2_, P2
     if not args.no_cpu_baseline and args.criterion == "lrm":  # the oracle's backward scores with LRM
         cb = cpu_baseline(pr, args.cpu_sample_frac)
         ref = cb.pop("_out", None)

@@ -168,6 +168,12 @@ def compact(sel, tok, slot, alpha, G, Phi, dtype: str, X=None, H=None):
     Dlt[c]  = alpha_j * g_{tok_j}   (the weighted cotangent, Eq. 5; exact in fp64)
     PhiC[c] = Phi[j],  XC[c] = X[tok_j],  HC[c] = H[j]
     ctok[c] = tok_j,   cslot[c] = slot_j
+    PhiW[c] = alpha_j * Phi[j]      (exact in fp64)
+
+    PhiW carries the routing weight on the saved activation instead of the gradient: the
+    FC2 weight gradient of appendix 7.1 (Eq. 6-8) sums alpha_j phi_j^T g_t over the pairs,
+    a product linear in each factor, so PhiW^T g_{ctok} over an expert's rows is the same
+    sum as PhiC^T Dlt, and a path that reads g rows by token needs no Dlt at all.
     """
     sel = np.asarray(sel, dtype=np.int64)
     t = np.asarray(tok, dtype=np.int64)[sel]
@@ -175,6 +181,7 @@ def compact(sel, tok, slot, alpha, G, Phi, dtype: str, X=None, H=None):
     out = {
         "Dlt": a[:, None] * widen(np.asarray(G)[t], dtype),
         "PhiC": widen(np.asarray(Phi)[sel], dtype),
+        "PhiW": a[:, None] * widen(np.asarray(Phi)[sel], dtype),
         "ctok": t.astype(np.int64),
         "cslot": np.asarray(slot, dtype=np.int64)[sel],
     }

@@ -402,6 +402,28 @@ def check_compact_identity(o, seed=2):
         np.testing.assert_array_equal(c["Dlt"][i], float(r.alpha[j]) * g)
 
 
+def check_weighted_phi_vs_autograd(o, seed=9):
+    """Appendix 7.1 (Eq. 6-8): dW2 sums alpha_j phi_j g_t^T over the retained pairs, so the
+    FC2 weight gradient from the alpha-weighted saved rows PhiW and the unweighted token
+    gradient rows equals autograd's with dropped pairs masked, and with every routing
+    weight 1 PhiW is PhiC itself."""
+    p = _small_swiglu(seed=seed, counts=(9, 3, 0, 8), E=4, T=9, K=3, D=6, F=4)
+    r = p.routing
+    q = synth.quotas(np.diff(r.seg_off), "0.5")
+    R = o.score(p.G, p.Phi, r.alpha, r.tok, "bf16")
+    sel, cseg_off, _ = o.select(R.astype(np.float32), r.seg_off, q)
+    c = o.compact(sel, r.tok, r.slot, r.alpha, p.G, p.Phi, "bf16", X=p.X, H=p.H)
+    g_rows = o.widen(p.G, "bf16")[np.asarray(c["ctok"], dtype=np.int64)]
+    _, dW2, _, _ = o.swiglu_expert_backward(cseg_off, g_rows, c["PhiW"], c["XC"], c["HC"],
+                                            o.widen(p.W1, "bf16"), o.widen(p.W2, "bf16"))
+    mask = np.zeros(len(r.tok))
+    mask[sel] = 1.0
+    _, dW2_ref, _ = autograd_swiglu(p, mask)
+    assert _rel(dW2, dW2_ref) < 1e-12
+    ones = o.compact(sel, r.tok, r.slot, np.ones_like(r.alpha), p.G, p.Phi, "bf16")
+    np.testing.assert_array_equal(ones["PhiW"], ones["PhiC"])
+
+
 def check_swiglu_dense_vs_autograd(o, seed=4):
     """Retention 1.0 keeps every pair, so the packed backward must equal the unpruned
     dense backward of the expert forward (torch autograd, float64)."""
@@ -520,6 +542,7 @@ ALL_CHECKS = {
     "select_per_expert": check_select_per_expert,
     "fig4_worked_example": check_fig4_worked_example,
     "compact_identity": check_compact_identity,
+    "weighted_phi_vs_autograd": check_weighted_phi_vs_autograd,
     "swiglu_dense_vs_autograd": check_swiglu_dense_vs_autograd,
     "swiglu_masked_vs_autograd": check_swiglu_masked_vs_autograd,
     "linear_masked_vs_autograd": check_linear_masked_vs_autograd,
@@ -667,6 +690,19 @@ def _compact_alpha_twice(sel, tok, slot, alpha, G, Phi, dtype, X=None, H=None):
     return out
 
 
+def _compact_phiw_unweighted(sel, tok, slot, alpha, G, Phi, dtype, X=None, H=None):
+    out = oracle.compact(sel, tok, slot, alpha, G, Phi, dtype, X=X, H=H)
+    out["PhiW"] = out["PhiC"]
+    return out
+
+
+def _compact_phiw_alpha_by_packed_row(sel, tok, slot, alpha, G, Phi, dtype, X=None, H=None):
+    out = oracle.compact(sel, tok, slot, alpha, G, Phi, dtype, X=X, H=H)
+    a = np.asarray(alpha, dtype=np.float64)[: len(sel)]
+    out["PhiW"] = a[:, None] * out["PhiC"]
+    return out
+
+
 def _compact_token_off_by_one(sel, tok, slot, alpha, G, Phi, dtype, X=None, H=None):
     t = np.asarray(tok).copy()
     t = np.minimum(t + 1, np.asarray(G).shape[0] - 1)
@@ -728,6 +764,9 @@ PLANTED = [
     ("select_ties_to_higher_index", dict(select=_select_ties_high_index), ["select_exhaustive_ties"]),
     ("compact_alpha_applied_twice", dict(compact=_compact_alpha_twice),
      ["compact_identity", "swiglu_dense_vs_autograd", "linear_masked_vs_autograd"]),
+    ("compact_phiw_unweighted", dict(compact=_compact_phiw_unweighted), ["weighted_phi_vs_autograd"]),
+    ("compact_phiw_alpha_of_packed_row", dict(compact=_compact_phiw_alpha_by_packed_row),
+     ["weighted_phi_vs_autograd"]),
     ("compact_wrong_token", dict(compact=_compact_token_off_by_one),
      ["compact_identity", "swiglu_masked_vs_autograd"]),
     ("swiglu_wrong_derivative", dict(swiglu_expert_backward=_swiglu_wrong_dsilu),

@@ -46,6 +46,10 @@ def parse():
     ap.add_argument("--packed", action="store_true",
                     help="compaction also packs the saved Phi and X rows (PhiC, XC) and the GEMMs read the "
                          "packed copies, instead of reading Phi and X in place through sel and ctok")
+    ap.add_argument("--path", default="gathered", choices=["gathered", "packed_dlt"],
+                    help="physical step 3-4 variant: 'gathered' (default) packs the weighted saved rows "
+                         "PhiW = alpha Phi[sel] and the GEMMs read the gradient rows G[ctok] by token; "
+                         "'packed_dlt' packs the weighted gradient rows Dlt instead")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="before timing, run 3 device-to-device copies of this many MiB (a plain copy kernel "
                          "of known size, used to scale hardware byte counters)")
@@ -67,7 +71,7 @@ def to_dev(np_mod, torch, a, dtype, dev):
     return torch.from_numpy(a).to(dev)
 
 
-def algorithmic_bytes(cfg, N, K_tot, packed=False, criterion="lrm"):
+def algorithmic_bytes(cfg, N, K_tot, packed=False, criterion="lrm", path="packed_dlt"):
     """Bytes each step reads once and writes once (storage dtype e; f32 scores/outputs)."""
     e = 2 if cfg.dtype == "bf16" else 4
     T, D, F = cfg.T, cfg.D, cfg.F
@@ -80,7 +84,9 @@ def algorithmic_bytes(cfg, N, K_tot, packed=False, criterion="lrm"):
     # compact reads each token's G row once and writes every retained pair's Dlt row once;
     # packed, it also reads each token's X row and each retained pair's Phi row once and
     # writes their copies (the saved [gate | up] rows are always read in place by the GEMM)
-    if not packed:
+    if path == "gathered":  # each retained pair's Phi row read once, its PhiW row written once
+        compact = 2 * K_tot * F * e + K_tot * (4 + 4)
+    elif not packed:
         compact = T * D * e + K_tot * D * e
     elif cfg.swiglu:
         compact = (2 * T * D + K_tot * F) * e + K_tot * (2 * D + F) * e
@@ -213,6 +219,8 @@ def parity(np, bufs, ref, pr, band=1e-5):
 
 def main():
     args = parse()
+    if args.packed:  # packing the saved rows is a variant of the packed-Dlt path
+        args.path = "packed_dlt"
     if args.gpus != 1:
         print(f"bench.py measures one GPU's expert share; --gpus {args.gpus} is not supported "
               f"(it runs on one GPU; the expert-parallel sharding across GPUs is a design, not code here).",
@@ -290,9 +298,15 @@ def main():
             bufs.setdefault("sel", sel)
             bufs.setdefault("keep", keep)
             rec(2)
-            c = lr.compact(P, G, Phi, alpha, tok, slot, sel=sel, keep=keep, X=ins["X"] if args.packed else None,
-                           mode=mode, out=bufs.get("c"), pack_phi=args.packed, maps=maps)
-            bufs.setdefault("c", c)
+            gathered = phys and args.path == "gathered"
+            if gathered:  # weighted saved rows only; the GEMMs read G, X and H in place
+                PhiW = lr.compact_weighted(P, sel, Phi, alpha, out=bufs.get("PhiW"))
+                bufs.setdefault("PhiW", PhiW)
+                c = {"ctok": maps["ctok"], "cslot": maps["cslot"]}
+            else:
+                c = lr.compact(P, G, Phi, alpha, tok, slot, sel=sel, keep=keep, X=ins["X"] if args.packed else None,
+                               mode=mode, out=bufs.get("c"), pack_phi=args.packed, maps=maps)
+                bufs.setdefault("c", c)
             rec(3)
             ctok, cslot = (c["ctok"], c["cslot"]) if phys else (tok, slot)
             hc_rows = sel if (phys and cfg.swiglu) else None
@@ -302,9 +316,14 @@ def main():
                 PhiC, XC = Phi, ins["X"]
                 phi_rows = sel if phys else None
                 x_rows = ctok if cfg.swiglu else None
-            g = lr.grouped_gemm_bwd(P, c["Dlt"], PhiC, ins["W2"], XC=XC, HC=ins["H"], W1=ins["W1"], mode=mode,
-                                    out=bufs.get("g"), hc_rows=hc_rows, phi_rows=phi_rows, x_rows=x_rows,
-                                    din_ready=bufs["din_ready"] if overlap else None)
+            if gathered:
+                g = lr.grouped_gemm_bwd_gathered(P, G, alpha, sel, ctok, PhiW, ins["W2"], X=ins["X"], H=ins["H"],
+                                                 W1=ins["W1"], out=bufs.get("g"),
+                                                 din_ready=bufs["din_ready"] if overlap else None)
+            else:
+                g = lr.grouped_gemm_bwd(P, c["Dlt"], PhiC, ins["W2"], XC=XC, HC=ins["H"], W1=ins["W1"], mode=mode,
+                                        out=bufs.get("g"), hc_rows=hc_rows, phi_rows=phi_rows, x_rows=x_rows,
+                                        din_ready=bufs["din_ready"] if overlap else None)
             bufs.setdefault("g", g)
             rec(4)
             if overlap:  # the scatter runs under the weight gradients, on the second stream
@@ -345,7 +364,7 @@ def main():
             return wall, per, bufs
 
         wall, per, phys_bufs = measure(lr.COMPACT_PHYSICAL)
-        bytes_ = algorithmic_bytes(cfg, P.N, P.K_tot, packed=args.packed, criterion=args.criterion)
+        bytes_ = algorithmic_bytes(cfg, P.N, P.K_tot, packed=args.packed, criterion=args.criterion, path=args.path)
         fl = gemm_flops(cfg, P.K_tot)
         peak = BF16_PEAK_TFLOPS if dt == "bf16" else FP32_PEAK_TFLOPS
         gemm_tf = fl / (per["grouped_gemm_bwd"] * 1e-3) / 1e12
@@ -376,7 +395,7 @@ def main():
         "vs_baseline": None, "dtype": dt, "data": "synthetic (seeded; pages' shapes, no dataset)",
         "config": {"workload": cfg.name, "T": cfg.T, "top_k": cfg.K, "local_experts": cfg.E, "D": cfg.D,
                    "F": cfg.F, "swiglu": cfg.swiglu, "rho": rho, "pairs": P.N, "retained_pairs": P.K_tot,
-                   "mode": "physical compaction", "criterion": args.criterion,
+                   "mode": "physical compaction", "path": args.path, "criterion": args.criterion,
                    "scatter": "second stream, under the weight gradients" if overlap else "after the GEMM call"},
         "roofline": {"bound": "mfma", "achieved": gemm_tf, "peak": peak, "unit": "TFLOP/s",
                      "frac": gemm_tf / peak, "traffic": recorded_traffic(profile_key(cfg, rho)),

@@ -12,6 +12,8 @@
  *   lrmoe_select           per-expert top-q under quotas      (section 3.3; appendix 7.2)
  *   lrmoe_compact          packing into expert segments       (sections 3.1, 3.4, Figure 4)
  *   lrmoe_grouped_gemm_bwd variable-size grouped GEMMs        (section 3.4)
+ *   or, with the gradient rows read by token instead of packed:
+ *   lrmoe_compact_weighted, lrmoe_grouped_gemm_bwd_gathered
  *   lrmoe_scatter          inverse mapping to token order     (section 3.1)
  *
  * Beside the path:
@@ -128,9 +130,11 @@ lrmoe_status lrmoe_workspace_size(const lrmoe_problem* p, lrmoe_compact_mode mod
  * its inputs (G, Phi, X, H, W1, W2, alpha, tok, slot): its scratch, the workspace
  * (lrmoe_workspace_size for LRMOE_COMPACT_PHYSICAL at these quotas) and the (token, slot)
  * map pmap int32 [T x K] of lrmoe_select, plus the buffers
- *   R f32 [N], keep u8 [N]; sel, ctok, cslot int32 [K_tot]; Dlt [K_tot x D];
- *   with packed != 0 the packed saved rows PhiC [K_tot x F] (SwiGLU: also XC [K_tot x D]
- *   and HC [K_tot x 2F]); SwiGLU: dH [K_tot x 2F]; dIn [K_tot x w]; f32 weight gradients
+ *   R f32 [N], keep u8 [N]; sel, ctok, cslot int32 [K_tot]; the packed rows of step 3:
+ *   with packed = 0 the weighted saved rows PhiW [K_tot x F] of lrmoe_compact_weighted
+ *   (the path of lrmoe_grouped_gemm_bwd_gathered), with packed != 0 the weighted
+ *   gradient rows Dlt [K_tot x D] and the packed saved rows PhiC [K_tot x F] (SwiGLU: also
+ *   XC [K_tot x D] and HC [K_tot x 2F]); SwiGLU: dH [K_tot x 2F]; dIn [K_tot x w]; f32 weight gradients
  *   dW2 [E x F x D] (SwiGLU: dW1 [E x D x 2F]); the scatter output f32 [T x w]
  * (storage dtype where not marked; w = D for SwiGLU experts, F for FC2-only ones). This is
  * the memory the retention quotas decide: the estimate quota admission compares with the
@@ -273,6 +277,41 @@ lrmoe_status lrmoe_grouped_gemm_bwd(const lrmoe_problem* p, lrmoe_compact_mode m
                                     const void* W1, float* dW2, float* dW1, void* dH, void* dIn,
                                     int32_t accumulate, void* ws, size_t ws_bytes, lrmoe_stream_t stream,
                                     lrmoe_event_t din_ready);
+
+/* Step 3 for the path that reads gradient rows by token (no Dlt; section 3.1's compact
+ * runtime gathers the retained rows, here the saved activation rows carry the weight).
+ * PHYSICAL packing only: for packed row c < K_tot of retained pair j = sel[c],
+ *   PhiW[c] = alpha[j] * Phi[j]      storage dtype [K_tot x F], out
+ * rounded once to the storage dtype (bf16: nearest-even of the exact product). A pair
+ * outside [0, N) gives a zero row. The FC2 weight gradient is linear in each of phi and
+ * the gradient row (appendix 7.1, Eq. 6-8), so PhiW^T g_tok over an expert's rows equals
+ * PhiC^T Dlt. No workspace; nothing to do when K_tot = 0. */
+lrmoe_status lrmoe_compact_weighted(const lrmoe_problem* p, const int32_t* sel, const void* Phi, const float* alpha,
+                                    void* PhiW, lrmoe_stream_t stream);
+
+/* Step 4 without a materialised Dlt (section 3.4's grouped GEMMs over the packed
+ * segments; section 3.1). PHYSICAL rows: expert e owns packed rows [cseg_off[e],
+ * cseg_off[e+1]) (cseg_off_d: device copy, int64 [E+1]). Packed row c belongs to pair
+ * j = sel[c] of token t = ctok[c] (the selection's outputs); G [T x D] holds the layer's
+ * output-gradient rows by token, read in place:
+ *   dPhi[c]   = alpha[j] * (G[t] W2[e]^T)              (internal, fp32 before the scale)
+ *   dW2[e] (+)= sum_c PhiW[c]^T G[t]                   f32 [E x F x D]
+ *   dH, dW1, dIn as in lrmoe_grouped_gemm_bwd with gate, up = H[j] and the FC1 input
+ *   X[t] (H [N x 2F] and X [T x D] read in place); dH [K_tot x 2F], dIn [K_tot x D]
+ * PhiW comes from lrmoe_compact_weighted. The results equal lrmoe_grouped_gemm_bwd's on
+ * Dlt[c] = alpha[j] G[t] up to rounding: alpha scales the fp32 products instead of the
+ * stored gradient rows, and in dW2 the rounding moves onto PhiW. A packed row whose t is
+ * outside [0, T) contributes nothing (zero gradient row); j outside [0, N) reads zero
+ * weight and zero [gate | up]. For swiglu = 0: dIn = dPhi [K_tot x F] and dH, X, H, W1, dW1
+ * must be NULL. T * D * element size must be under 2 GiB (else LRMOE_ERR_UNSUPPORTED).
+ * Workspace: as lrmoe_grouped_gemm_bwd in PHYSICAL mode. accumulate and din_ready as
+ * there. */
+lrmoe_status lrmoe_grouped_gemm_bwd_gathered(const lrmoe_problem* p, const int64_t* cseg_off_d, const void* G,
+                                             const float* alpha, const int32_t* sel, const int32_t* ctok,
+                                             const void* PhiW, const void* X, const void* H, const void* W2,
+                                             const void* W1, float* dW2, float* dW1, void* dH, void* dIn,
+                                             int32_t accumulate, void* ws, size_t ws_bytes, lrmoe_stream_t stream,
+                                             lrmoe_event_t din_ready);
 
 /* The forward that produces the backward's saved context (Algorithm 1's
  * FullForwardAndSaveContext; section 3.1: the forward keeps every routed pair). For every

@@ -21,7 +21,8 @@ from . import _lib
 from ._lib import (BF16, COMPACT_PHYSICAL, COMPACT_ZERO_MASKED, F32, SCATTER_SLOT, SCATTER_TOKEN,
                    InfeasibleQuotaError, LrmoeError)
 
-__all__ = ["Problem", "score", "select", "compact", "grouped_gemm_bwd", "scatter", "backward",
+__all__ = ["Problem", "score", "select", "select_noalloc", "compact", "compact_weighted", "grouped_gemm_bwd",
+           "grouped_gemm_bwd_gathered", "expert_forward", "scatter", "backward", "backward_bytes", "plan_quotas",
            "library", "BF16", "F32", "COMPACT_PHYSICAL", "COMPACT_ZERO_MASKED", "SCATTER_TOKEN",
            "SCATTER_SLOT", "LrmoeError", "InfeasibleQuotaError"]
 
@@ -263,6 +264,44 @@ def grouped_gemm_bwd(p: Problem, Dlt, PhiC, W2, XC=None, HC=None, W1=None, mode=
     return res
 
 
+def compact_weighted(p: Problem, sel, Phi, alpha, out=None, stream=None):
+    """Step 3 for the path that reads gradient rows by token: PhiW[c] = alpha[sel[c]] *
+    Phi[sel[c]] over the K_tot packed rows (lrmoe_compact_weighted)."""
+    PhiW = out if out is not None else torch.empty(max(p.K_tot, 1), p.F, dtype=p.torch_dtype, device=p.device)
+    _lib.check(library().lrmoe_compact_weighted(ctypes.byref(p.c), _ptr(sel), _ptr(Phi), _ptr(alpha), _ptr(PhiW),
+                                                _stream(stream)), "lrmoe_compact_weighted")
+    return PhiW[:p.K_tot]
+
+
+def grouped_gemm_bwd_gathered(p: Problem, G, alpha, sel, ctok, PhiW, W2, X=None, H=None, W1=None, out=None,
+                              accumulate=False, din_ready=None, stream=None):
+    """Step 4 without a packed Dlt (lrmoe_grouped_gemm_bwd_gathered): gradient rows G[ctok]
+    and X[ctok] read by token, H[sel] and alpha[sel] by pair, PhiW from compact_weighted.
+    Same outputs as grouped_gemm_bwd in physical mode."""
+    rows = p.K_tot
+    dt = p.torch_dtype
+    dev = p.device
+    o = dict(out or {})
+    o.setdefault("dW2", torch.empty(p.E, p.F, p.D, dtype=torch.float32, device=dev))
+    if p.swiglu:
+        o.setdefault("dW1", torch.empty(p.E, p.D, 2 * p.F, dtype=torch.float32, device=dev))
+        o.setdefault("dH", torch.empty(max(rows, 1), 2 * p.F, dtype=dt, device=dev))
+        o.setdefault("dIn", torch.empty(max(rows, 1), p.D, dtype=dt, device=dev))
+    else:
+        o.setdefault("dIn", torch.empty(max(rows, 1), p.F, dtype=dt, device=dev))
+    ws = p.workspace(COMPACT_PHYSICAL)
+    _lib.check(library().lrmoe_grouped_gemm_bwd_gathered(
+        ctypes.byref(p.c), _ptr(p.cseg_off_d), _ptr(G), _ptr(alpha), _ptr(sel), _ptr(ctok), _ptr(PhiW), _ptr(X),
+        _ptr(H), _ptr(W2), _ptr(W1), _ptr(o["dW2"]), _ptr(o.get("dW1")), _ptr(o.get("dH")), _ptr(o["dIn"]),
+        int(bool(accumulate)), _ptr(ws), ws.numel(), _stream(stream), _event(din_ready, stream)),
+        "lrmoe_grouped_gemm_bwd_gathered")
+    res = dict(o)
+    res["dIn"] = o["dIn"][:rows]
+    if "dH" in o:
+        res["dH"] = o["dH"][:rows]
+    return res
+
+
 def expert_forward(p: Problem, X, tok, alpha, W1, W2, out=None, stream=None):
     """The forward that saves the backward's context: H = X[tok] W1 ([gate | up]),
     Phi = silu(gate) * up, Y = alpha * Phi W2 (rows of the N pairs, expert-major).
@@ -299,8 +338,14 @@ def scatter(p: Problem, rows_t, ctok, cslot, n_rows=None, mode=SCATTER_TOKEN, ou
 
 
 def backward(p: Problem, *, G, Phi, alpha, tok, slot, W2, X=None, H=None, W1=None, mode=COMPACT_PHYSICAL,
-             scatter_mode=SCATTER_TOKEN, bufs=None, overlap_scatter=False, stream=None):
+             scatter_mode=SCATTER_TOKEN, bufs=None, overlap_scatter=False, packed_dlt=False, stream=None):
     """The whole path: score -> select -> compact -> grouped GEMMs -> scatter.
+
+    Physical compaction packs only the weighted saved rows PhiW = alpha Phi[sel] and the
+    grouped GEMMs read the gradient rows G[ctok], the FC1 inputs X[ctok] and the saved
+    [gate | up] rows H[sel] in place (compact_weighted, grouped_gemm_bwd_gathered). With
+    ``packed_dlt`` (and always in zero-masked mode) compaction packs the weighted gradient
+    rows Dlt instead and grouped_gemm_bwd reads them.
 
     ``bufs`` (a dict, optional) carries preallocated outputs between calls; it is
     filled on first use. With ``overlap_scatter`` the scatter runs on a second stream as
@@ -322,11 +367,15 @@ def backward(p: Problem, *, G, Phi, alpha, tok, slot, W2, X=None, H=None, W1=Non
         sel, keep = select(p, b["R"], sel=b.get("sel_full"), keep=b.get("keep_full"), stream=stream)
     b.setdefault("sel_full", sel)
     b.setdefault("keep_full", keep)
-    # only the new gradient rows are packed: the GEMMs read the saved Phi, X and H rows in
-    # place through sel and the packed rows' tokens
-    c = compact(p, G, Phi, alpha, tok, slot, sel=sel, keep=keep, mode=mode, out=b.get("compact"),
-                pack_phi=False, maps=maps, stream=stream)
-    b.setdefault("compact", c)
+    gathered = phys and not packed_dlt
+    if gathered:  # the weighted saved rows only; G, X and H are read in place
+        PhiW = compact_weighted(p, sel, Phi, alpha, out=b.get("PhiW"), stream=stream)
+        b.setdefault("PhiW", PhiW)
+        c = {"PhiW": PhiW, "ctok": maps["ctok"], "cslot": maps["cslot"]}
+    else:  # the weighted gradient rows; the GEMMs read Phi, X and H in place through sel and ctok
+        c = compact(p, G, Phi, alpha, tok, slot, sel=sel, keep=keep, mode=mode, out=b.get("compact"),
+                    pack_phi=False, maps=maps, stream=stream)
+        b.setdefault("compact", c)
     if mode == COMPACT_PHYSICAL:
         ctok, cslot = c["ctok"], c["cslot"]
         phi_rows = sel
@@ -345,9 +394,13 @@ def backward(p: Problem, *, G, Phi, alpha, tok, slot, W2, X=None, H=None, W1=Non
         if "out" not in b:
             nout = p.T if scatter_mode == SCATTER_TOKEN else p.T * p.K
             b["out"] = torch.empty(max(nout, 1), p.D if p.swiglu else p.F, dtype=torch.float32, device=p.device)
-    g = grouped_gemm_bwd(p, c["Dlt"], Phi, W2, XC=X, HC=H, W1=W1, mode=mode, out=b.get("gemm"),
-                         hc_rows=hc_rows, phi_rows=phi_rows, x_rows=x_rows,
-                         din_ready=b["din_ready"] if overlap_scatter else None, stream=main)
+    if gathered:
+        g = grouped_gemm_bwd_gathered(p, G, alpha, sel, ctok, PhiW, W2, X=X, H=H, W1=W1, out=b.get("gemm"),
+                                      din_ready=b["din_ready"] if overlap_scatter else None, stream=main)
+    else:
+        g = grouped_gemm_bwd(p, c["Dlt"], Phi, W2, XC=X, HC=H, W1=W1, mode=mode, out=b.get("gemm"),
+                             hc_rows=hc_rows, phi_rows=phi_rows, x_rows=x_rows,
+                             din_ready=b["din_ready"] if overlap_scatter else None, stream=main)
     b.setdefault("gemm", g)
     if overlap_scatter:
         side = b["side"]

@@ -23,7 +23,7 @@ SCATTER_TOKEN, SCATTER_SLOT = 0, 1
 EXPORTS = ("lrmoe_status_string", "lrmoe_version", "lrmoe_validate", "lrmoe_workspace_size",
            "lrmoe_backward_bytes", "lrmoe_plan_quotas", "lrmoe_score", "lrmoe_score_criterion", "lrmoe_select",
            "lrmoe_compact", "lrmoe_grouped_gemm_bwd", "lrmoe_scatter", "lrmoe_expert_forward",
-           "lrmoe_select_noalloc")
+           "lrmoe_select_noalloc", "lrmoe_compact_weighted", "lrmoe_grouped_gemm_bwd_gathered")
 
 
 class LrmoeError(RuntimeError):
@@ -74,6 +74,9 @@ def load() -> ctypes.CDLL:
                           ctypes.c_size_t, vp],
         "lrmoe_grouped_gemm_bwd": [P, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp,
                                    sz, vp, vp],
+        "lrmoe_compact_weighted": [P, vp, vp, vp, vp, vp],
+        "lrmoe_grouped_gemm_bwd_gathered": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, sz,
+                                            vp, vp],
         "lrmoe_scatter": [P, ctypes.c_int, i64, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp],
         "lrmoe_expert_forward": [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp],
     }

@@ -124,6 +124,8 @@ lrmoe_status launch_compact(const lrmoe_problem* p, int64_t rows, bool masked, c
                             void* Dlt, void* PhiC, void* XC, void* HC, int32_t* ctok, int32_t* cslot,
                             const int32_t* pmap, void* ws, hipStream_t s);
 size_t compact_ws_bytes(const lrmoe_problem* p);
+lrmoe_status launch_compact_weighted_phi(const lrmoe_problem* p, int64_t rows, const int32_t* sel,
+                                         const void* Phi, const float* alpha, void* PhiW, hipStream_t s);
 
 lrmoe_status launch_expert_forward(const lrmoe_problem* p, const int64_t* seg_off_d, const void* X,
                                    const int32_t* tok, const float* alpha, const void* W1, const void* W2, void* H,
@@ -132,8 +134,8 @@ size_t gemm_ws_bytes(const lrmoe_problem* p, const int64_t* row_off_h);
 lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_off_h,
                                      const int64_t* row_off_d, const void* Dlt, const void* PhiC,
                                      const void* XC, const void* HC, const int32_t* hc_rows,
-                                     const int32_t* phi_rows, const int32_t* x_rows, const void* W2,
-                                     const void* W1,
+                                     const int32_t* phi_rows, const int32_t* x_rows, const int32_t* dlt_rows,
+                                     const float* alpha, const void* W2, const void* W1,
                                      float* dW2, float* dW1, void* dH, void* dIn, int accumulate,
                                      void* ws, hipStream_t s, hipEvent_t din_ready);
 

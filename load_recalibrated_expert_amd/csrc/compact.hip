@@ -357,6 +357,42 @@ __global__ __launch_bounds__(kThreads) void compact_dlt_kernel(int T, int K, int
   }
 }
 
+// Weighted saved rows for the path that reads gradient rows by token: PhiW[c] =
+// alpha_j * Phi[j] for j = sel[c] (one rounding to the storage dtype), a pair outside [0, N)
+// giving a zero row. A block covers kWRows packed rows as one run of 16-byte chunks, so
+// consecutive lanes read and write consecutive chunks of a row and rows follow each other
+// without gaps; each thread keeps kU chunks in flight.
+constexpr int kWRows = 16;
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void compact_weighted_phi_kernel(int64_t rows, int64_t N, int fch,
+                                                                        const int32_t* __restrict__ sel,
+                                                                        const uint4* __restrict__ Phi,
+                                                                        const float* __restrict__ alpha,
+                                                                        uint4* __restrict__ PhiW) {
+  const int64_t r0 = (int64_t)blockIdx.x * kWRows;
+  const int nr = (int)min<int64_t>(kWRows, rows - r0);
+  const int n = nr * fch;  // chunks of this block
+  for (int l0 = threadIdx.x; l0 < n; l0 += kThreads * kU) {
+    uint4 v[kU];
+    float a[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int l = l0 + u * kThreads;
+      const int r = l / fch, ch = l - r * fch;
+      const int64_t j = l < n ? (int64_t)sel[r0 + r] : -1;
+      const bool ok = j >= 0 && j < N;
+      a[u] = ok ? alpha[j] : 0.0f;
+      v[u] = ok ? ld_stream(Phi + j * fch + ch) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int l = l0 + u * kThreads;
+      if (l < n) PhiW[r0 * fch + l] = BF16 ? scale_bf16x8(a[u], v[u]) : scale_f32x4(a[u], v[u]);
+    }
+  }
+}
+
 template <bool BF16, bool SWIGLU>
 void launch(int64_t rows, bool masked, const lrmoe_problem* p, const int32_t* sel, const uint8_t* keep,
             const void* G, const void* Phi, const void* X, const void* H, const float* alpha, const int32_t* tok,
@@ -397,6 +433,21 @@ void launch(int64_t rows, bool masked, const lrmoe_problem* p, const int32_t* se
 }
 
 }  // namespace
+
+lrmoe_status launch_compact_weighted_phi(const lrmoe_problem* p, int64_t rows, const int32_t* sel,
+                                         const void* Phi, const float* alpha, void* PhiW, hipStream_t s) {
+  if (rows <= 0) return LRMOE_OK;
+  const bool bf16 = p->dtype == LRMOE_BF16;
+  const int fch = p->F * (bf16 ? 2 : 4) / 16;
+  const unsigned grid = (unsigned)ceil_div(rows, kWRows);
+  if (bf16)
+    compact_weighted_phi_kernel<true><<<grid, kThreads, 0, s>>>(rows, p->N, fch, sel, (const uint4*)Phi, alpha,
+                                                                (uint4*)PhiW);
+  else
+    compact_weighted_phi_kernel<false><<<grid, kThreads, 0, s>>>(rows, p->N, fch, sel, (const uint4*)Phi, alpha,
+                                                                 (uint4*)PhiW);
+  return launch_status();
+}
 
 size_t compact_ws_bytes(const lrmoe_problem* p) { return align_up(sizeof(int32_t) * (size_t)p->T * p->K, 256); }
 

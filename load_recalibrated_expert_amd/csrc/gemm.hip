@@ -481,8 +481,12 @@ __device__ __forceinline__ uint4 pack_bf16x8(const float (&v)[8]) {
 enum { EPI_SWIGLU = 0, EPI_STORE = 1 };
 
 struct DgradArgs {
-  const uint16_t* A;   // [rows x K] packed rows (Dlt or dH)
+  const uint16_t* A;   // [rows x K] packed rows (Dlt or dH), or the matrix a_rows gathers from
   int64_t lda;
+  const int32_t* a_rows;  // row c of A is A[a_rows[c]] (nullptr: row c); outside [0, a_nrows): zeros
+  int64_t a_nrows;
+  const float* alpha;     // nullptr, or row c of the product is scaled by alpha[hc_rows[c]] (its
+                          // pair's routing weight; hc_rows then maps packed rows to pairs)
   const uint16_t* W;   // [E x N x K] weights viewed as rows n with K contiguous
   int64_t ldw, w_estride;
   int N, K;            // output columns, reduction length
@@ -491,7 +495,7 @@ struct DgradArgs {
   int E;
   // epilogue
   const uint16_t* HC;  // SwiGLU: saved [gate | up] rows, 2F wide
-  const int32_t* hc_rows;  // row of HC for packed row c (nullptr: row c)
+  const int32_t* hc_rows;  // row of HC (and pair of alpha) for packed row c (nullptr: row c)
   int64_t hc_nrows;        // rows of HC: a mapped row outside [0, hc_nrows) reads as zeros
   uint16_t* out;       // SwiGLU: dH [rows x 2F]; STORE: [rows x N]
   int64_t ldo;
@@ -513,6 +517,7 @@ struct DgradArgs {
 template <int B>
 struct HcBatch {
   uint4 gw[B], uw[B];
+  float a[B];  // the rows' routing weights (1 when the product is not scaled)
   uint32_t okm;
 };
 
@@ -551,6 +556,7 @@ __device__ __forceinline__ void swiglu_half(StageBufs<C>& sm, const acc_t<C>& ac
       const int64_t hb = ok ? hrow[i] * ld + n0 + tc : 0;
       bt.gw[b] = *(const uint4*)(hc + hb);
       bt.uw[b] = *(const uint4*)(hc + hb + F);
+      bt.a[b] = g.alpha != nullptr ? g.alpha[ok ? hrow[i] : 0] : 1.0f;
     }
   };
   auto finish = [&](HcBatch<B>& bt, int i0) {
@@ -559,7 +565,8 @@ __device__ __forceinline__ void swiglu_half(StageBufs<C>& sm, const acc_t<C>& ac
       const int r = tr0 + kRowStep * (i0 + b), c8 = tc / 8;
       const float4 lo = st[r * P + ((2 * c8) ^ (r & 15))];
       const float4 hi = st[r * P + ((2 * c8 + 1) ^ (r & 15))];
-      const float dphi[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      const float av = bt.a[b];
+      const float dphi[8] = {av * lo.x, av * lo.y, av * lo.z, av * lo.w, av * hi.x, av * hi.y, av * hi.z, av * hi.w};
       const bool ok = (bt.okm >> b) & 1u;  // rows outside the tile or HC read as zeros
       const uint32_t gg[4] = {ok ? bt.gw[b].x : 0u, ok ? bt.gw[b].y : 0u, ok ? bt.gw[b].z : 0u, ok ? bt.gw[b].w : 0u};
       const uint32_t uu[4] = {ok ? bt.uw[b].x : 0u, ok ? bt.uw[b].y : 0u, ok ? bt.uw[b].z : 0u, ok ? bt.uw[b].w : 0u};
@@ -641,7 +648,8 @@ __global__ LRMOE_GEMM_ATTR(CfgD) void dgrad_kernel(DgradArgs g) {
   zero_acc<C>(acc);
   DmaK<C::NWAVE, BM> la;
   DmaK<C::NWAVE, C::BN> lb;
-  la.init(g.A + row0 * g.lda, g.lda, rows_valid);
+  if (g.a_rows != nullptr) la.init_rows(g.A, g.lda, rows_valid, g.a_rows + row0, g.a_nrows);
+  else la.init(g.A + row0 * g.lda, g.lda, rows_valid);
   lb.init(g.W + (int64_t)e * g.w_estride + (int64_t)n0 * g.ldw, g.ldw, n_valid);
   gemm_mainloop<C, false, false>(lds, la, lb, g.K, 0, 0, acc, wm, wn, lane);
 
@@ -650,7 +658,17 @@ __global__ LRMOE_GEMM_ATTR(CfgD) void dgrad_kernel(DgradArgs g) {
   } else {
     uint16_t* __restrict__ out = g.out;
     epilogue_staged<C>(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
-      if (tr < rows_valid && tc < n_valid) *(uint4*)(out + (row0 + tr) * g.ldo + n0 + tc) = pack_bf16x8(v);
+      if (tr < rows_valid && tc < n_valid) {
+        float w[8];
+        float av = 1.0f;
+        if (g.alpha != nullptr) {
+          const int64_t j = g.hc_rows[row0 + tr];
+          av = j >= 0 && j < g.hc_nrows ? g.alpha[j] : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = av * v[i];
+        *(uint4*)(out + (row0 + tr) * g.ldo + n0 + tc) = pack_bf16x8(w);
+      }
     });
   }
 }
@@ -788,10 +806,12 @@ struct WgradType {
   int64_t lda;
   const int32_t* a_rows;  // packed row c is row a_rows[c] of A (nullptr: row c)
   int64_t a_nrows;        // rows of A when gathered
-  const uint16_t* B;  // [rows x N] (N contiguous)
+  const uint16_t* B;  // [rows x N] (N contiguous), or the matrix that b_rows gathers from
   int64_t ldb;
   float* out;         // [E x M x N]
   int M, N, ntm, ntn, tiles;
+  const int32_t* b_rows;  // packed row c is row b_rows[c] of B (nullptr: row c)
+  int64_t b_nrows;        // rows of B when gathered
 };
 
 struct WgradArgs {
@@ -865,9 +885,11 @@ __global__ __launch_bounds__(kAuxThr) void wgrad_plan_kernel(WgradArgs g) {
 }
 
 // G0, G1: the A operand of weight-gradient type 0 (FC2: Phi) / type 1 (FC1: X) is gathered
-// through its row map (a compile-time choice, so neither loader carries the other's code).
-template <bool G0, bool G1>
+// through its row map; GB0: the B operand of type 0 (the gradient rows) is (compile-time
+// choices, so no loader carries another's code).
+template <bool G0, bool G1, bool GB0>
 __global__ LRMOE_GEMM_ATTR(CfgW) void wgrad_kernel(WgradArgs g) {
+  static_assert(!(G0 && GB0), "type 0 gathers at most one operand");
   using C = CfgW;
   __shared__ StageBufs<C> lds;
   // hardware sends block i to XCD i % 8; the grid holds 8 x (largest range) blocks
@@ -898,15 +920,22 @@ __global__ LRMOE_GEMM_ATTR(CfgW) void wgrad_kernel(WgradArgs g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   acc_t<C> acc;
   zero_acc<C>(acc);
-  DmaT<C::NL> lb;
-  lb.init(T.B + (r0 + k_begin) * T.ldb + n0, T.ldb, n_valid);
-  if ((G0 || G1) && (ty == 0 ? G0 : G1)) {
+  if (GB0 && ty == 0) {  // packed A, gathered B
+    DmaT<C::NL> la;
+    DmaTG<C::NL> lb;
+    la.init(T.A + (r0 + k_begin) * T.lda + m0, T.lda, m_valid);
+    lb.init(T.B + n0, T.ldb, n_valid, T.b_rows + r0 + k_begin, klen, T.b_nrows);
+    gemm_mainloop<C, true, true>(lds, la, lb, klen, (uint32_t)(T.lda * 2), 0, acc, wm, wn, lane);
+  } else if ((G0 || G1) && (ty == 0 ? G0 : G1)) {  // gathered A, packed B
     DmaTG<C::NL> la;
+    DmaT<C::NL> lb;
     la.init(T.A + m0, T.lda, m_valid, T.a_rows + r0 + k_begin, klen, T.a_nrows);
+    lb.init(T.B + (r0 + k_begin) * T.ldb + n0, T.ldb, n_valid);
     gemm_mainloop<C, true, true>(lds, la, lb, klen, 0, (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
   } else {
-    DmaT<C::NL> la;
+    DmaT<C::NL> la, lb;
     la.init(T.A + (r0 + k_begin) * T.lda + m0, T.lda, m_valid);
+    lb.init(T.B + (r0 + k_begin) * T.ldb + n0, T.ldb, n_valid);
     gemm_mainloop<C, true, true>(lds, la, lb, klen, (uint32_t)(T.lda * 2), (uint32_t)(T.ldb * 2), acc, wm, wn, lane);
   }
 
@@ -1016,9 +1045,12 @@ __device__ __forceinline__ int find_expert(const int64_t* row_off, int E, int64_
   return lo;
 }
 
-// out[r][n] = sum_k A[r][k] * W[e(r)][n][k]; SwiGLU epilogue or plain store.
+// out[r][n] = a(r) sum_k A[ar(r)][k] * W[e(r)][n][k]; SwiGLU epilogue or plain store. ar(r) =
+// a_rows[r] (rows outside [0, a_nrows) read as zeros) or r; a(r) = alpha[hc_rows[r]] or 1.
 template <int EPI>
 __global__ __launch_bounds__(kAuxThr) void f32_dgrad_kernel(const float* __restrict__ A, int64_t lda,
+                                                         const int32_t* __restrict__ a_rows, int64_t a_nrows,
+                                                         const float* __restrict__ alpha,
                                                          const float* __restrict__ W, int64_t ldw,
                                                          int64_t w_estride, int N, int K,
                                                          const int64_t* __restrict__ row_off, int E,
@@ -1029,13 +1061,17 @@ __global__ __launch_bounds__(kAuxThr) void f32_dgrad_kernel(const float* __restr
   const int n = blockIdx.y * kAuxThr + threadIdx.x;
   if (n >= N) return;
   const int e = find_expert(row_off, E, r);
-  const float* a = A + r * lda;
+  const int64_t ar = a_rows != nullptr ? (int64_t)a_rows[r] : r;
+  const bool a_ok = a_rows == nullptr || (ar >= 0 && ar < a_nrows);
+  const float* a = A + (a_ok ? ar : 0) * lda;
   const float* w = W + (int64_t)e * w_estride + (int64_t)n * ldw;
   float acc = 0.0f;
-  for (int k = 0; k < K; ++k) acc = fmaf(a[k], w[k], acc);
+  if (a_ok)
+    for (int k = 0; k < K; ++k) acc = fmaf(a[k], w[k], acc);
+  const int64_t hr = hc_rows != nullptr ? (int64_t)hc_rows[r] : r;
+  const bool ok = hr >= 0 && hr < hc_nrows;  // rows outside HC read as zeros
+  if (alpha != nullptr) acc *= ok ? alpha[hr] : 0.0f;
   if (EPI == EPI_SWIGLU) {
-    const int64_t hr = hc_rows != nullptr ? (int64_t)hc_rows[r] : r;
-    const bool ok = hr >= 0 && hr < hc_nrows;  // rows outside HC read as zeros
     const float gate = ok ? HC[hr * 2 * F + n] : 0.0f, up = ok ? HC[hr * 2 * F + F + n] : 0.0f;
     const float s = 1.0f / (1.0f + expf(-gate));
     out[r * 2 * F + n] = acc * up * (s * (1.0f + gate * (1.0f - s)));
@@ -1045,11 +1081,14 @@ __global__ __launch_bounds__(kAuxThr) void f32_dgrad_kernel(const float* __restr
   }
 }
 
-// out[e][i][j] (+)= sum over rows r of expert e of A[ar(r)][i] * B[r][j], with ar(r) =
-// a_rows[r] (rows outside [0, a_nrows) read as zeros) or r when a_rows is nullptr
+// out[e][i][j] (+)= sum over rows r of expert e of A[ar(r)][i] * B[br(r)][j], with ar(r) =
+// a_rows[r] (rows outside [0, a_nrows) read as zeros) or r when a_rows is nullptr, and br
+// likewise from b_rows
 __global__ __launch_bounds__(kAuxThr) void f32_wgrad_kernel(const float* __restrict__ A, int64_t lda,
                                                          const int32_t* __restrict__ a_rows, int64_t a_nrows,
-                                                         const float* __restrict__ B, int64_t ldb, int M, int N,
+                                                         const float* __restrict__ B, int64_t ldb,
+                                                         const int32_t* __restrict__ b_rows, int64_t b_nrows,
+                                                         int M, int N,
                                                          const int64_t* __restrict__ row_off,
                                                          float* __restrict__ out, int accumulate) {
   const int e = blockIdx.z, i = blockIdx.y;
@@ -1059,7 +1098,9 @@ __global__ __launch_bounds__(kAuxThr) void f32_wgrad_kernel(const float* __restr
   for (int64_t r = row_off[e]; r < row_off[e + 1]; ++r) {
     const int64_t ar = a_rows != nullptr ? (int64_t)a_rows[r] : r;
     const float a = (a_rows == nullptr || (ar >= 0 && ar < a_nrows)) ? A[ar * lda + i] : 0.0f;
-    acc = fmaf(a, B[r * ldb + j], acc);
+    const int64_t br = b_rows != nullptr ? (int64_t)b_rows[r] : r;
+    const float b = (b_rows == nullptr || (br >= 0 && br < b_nrows)) ? B[br * ldb + j] : 0.0f;
+    acc = fmaf(a, b, acc);
   }
   float* q = out + ((int64_t)e * M + i) * N + j;
   *q = accumulate ? *q + acc : acc;
@@ -1248,8 +1289,8 @@ size_t gemm_ws_bytes(const lrmoe_problem* p, const int64_t* row_off_h) {
 lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_off_h,
                                      const int64_t* row_off_d, const void* Dlt, const void* PhiC,
                                      const void* XC, const void* HC, const int32_t* hc_rows,
-                                     const int32_t* phi_rows, const int32_t* x_rows, const void* W2,
-                                     const void* W1,
+                                     const int32_t* phi_rows, const int32_t* x_rows, const int32_t* dlt_rows,
+                                     const float* alpha, const void* W2, const void* W1,
                                      float* dW2, float* dW1, void* dH, void* dIn, int accumulate,
                                      void* ws, hipStream_t s, hipEvent_t din_ready) {
   const int E = p->E, D = p->D, F = p->F;
@@ -1262,32 +1303,36 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
   // rows of the (possibly gathered) saved matrices: pair rows or token rows when mapped
   const int64_t hc_nrows = hc_rows ? p->N : rows, phi_nrows = phi_rows ? p->N : rows;
   const int64_t x_nrows = x_rows ? (int64_t)p->T : rows;
+  // gradient rows read by token (dlt_rows: a token per packed row) from G [T x D]
+  const int64_t dlt_nrows = dlt_rows ? (int64_t)p->T : rows;
   if (p->dtype == LRMOE_F32) {
     const float* dl = (const float*)Dlt;
     if (p->swiglu) {
       if (rows > 0) {
         f32_dgrad_kernel<EPI_SWIGLU><<<dim3((unsigned)rows, (unsigned)ceil_div(F, kAuxThr)), kAuxThr, 0, s>>>(
-            dl, D, (const float*)W2, D, (int64_t)F * D, F, D, row_off_d, E, (const float*)HC, hc_rows, hc_nrows,
-            (float*)dH, 2 * F, F);
+            dl, D, dlt_rows, dlt_nrows, alpha, (const float*)W2, D, (int64_t)F * D, F, D, row_off_d, E,
+            (const float*)HC, hc_rows, hc_nrows, (float*)dH, 2 * F, F);
         f32_dgrad_kernel<EPI_STORE><<<dim3((unsigned)rows, (unsigned)ceil_div(D, kAuxThr)), kAuxThr, 0, s>>>(
-            (const float*)dH, 2 * F, (const float*)W1, 2 * F, (int64_t)D * 2 * F, D, 2 * F, row_off_d, E, nullptr,
-            nullptr, 0, (float*)dIn, D, F);
+            (const float*)dH, 2 * F, nullptr, 0, nullptr, (const float*)W1, 2 * F, (int64_t)D * 2 * F, D, 2 * F,
+            row_off_d, E, nullptr, nullptr, 0, (float*)dIn, D, F);
       }
       if (mark_din() != LRMOE_OK) return LRMOE_ERR_HIP;
       if (E > 0) {
         f32_wgrad_kernel<<<dim3((unsigned)ceil_div(D, kAuxThr), F, E), kAuxThr, 0, s>>>(
-            (const float*)PhiC, F, phi_rows, phi_nrows, dl, D, F, D, row_off_d, dW2, accumulate);
+            (const float*)PhiC, F, phi_rows, phi_nrows, dl, D, dlt_rows, dlt_nrows, F, D, row_off_d, dW2, accumulate);
         f32_wgrad_kernel<<<dim3((unsigned)ceil_div(2 * F, kAuxThr), D, E), kAuxThr, 0, s>>>(
-            (const float*)XC, D, x_rows, x_nrows, (const float*)dH, 2 * F, D, 2 * F, row_off_d, dW1, accumulate);
+            (const float*)XC, D, x_rows, x_nrows, (const float*)dH, 2 * F, nullptr, 0, D, 2 * F, row_off_d, dW1,
+            accumulate);
       }
     } else {
       if (rows > 0)
         f32_dgrad_kernel<EPI_STORE><<<dim3((unsigned)rows, (unsigned)ceil_div(F, kAuxThr)), kAuxThr, 0, s>>>(
-            dl, D, (const float*)W2, D, (int64_t)F * D, F, D, row_off_d, E, nullptr, nullptr, 0, (float*)dIn, F, F);
+            dl, D, dlt_rows, dlt_nrows, alpha, (const float*)W2, D, (int64_t)F * D, F, D, row_off_d, E, nullptr,
+            hc_rows, hc_nrows, (float*)dIn, F, F);
       if (mark_din() != LRMOE_OK) return LRMOE_ERR_HIP;
       if (E > 0)
         f32_wgrad_kernel<<<dim3((unsigned)ceil_div(D, kAuxThr), F, E), kAuxThr, 0, s>>>(
-            (const float*)PhiC, F, phi_rows, phi_nrows, dl, D, F, D, row_off_d, dW2, accumulate);
+            (const float*)PhiC, F, phi_rows, phi_nrows, dl, D, dlt_rows, dlt_nrows, F, D, row_off_d, dW2, accumulate);
     }
     return launch_status();
   }
@@ -1298,6 +1343,11 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
   DgradArgs d2{};
   d2.A = (const uint16_t*)Dlt;
   d2.lda = D;
+  d2.a_rows = dlt_rows;
+  d2.a_nrows = dlt_nrows;
+  d2.alpha = alpha;
+  d2.hc_rows = hc_rows;  // the pairs of the routing weights (and of HC's rows)
+  d2.hc_nrows = hc_nrows;
   d2.W = (const uint16_t*)W2;
   d2.ldw = D;
   d2.w_estride = (int64_t)F * D;
@@ -1309,14 +1359,14 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
   d2.F = F;
   if (p->swiglu) {
     d2.HC = (const uint16_t*)HC;
-    d2.hc_rows = hc_rows;
-    d2.hc_nrows = hc_nrows;
     d2.out = (uint16_t*)dH;
     d2.ldo = 2 * F;
     if (mtiles > 0) dgrad_kernel<EPI_SWIGLU><<<(unsigned)(mtiles * d2.ntn), CfgD::NTHR, 0, s>>>(d2);
     DgradArgs d1 = d2;
     d1.A = (const uint16_t*)dH;
     d1.lda = 2 * F;
+    d1.a_rows = nullptr;
+    d1.alpha = nullptr;
     d1.W = (const uint16_t*)W1;
     d1.ldw = 2 * F;
     d1.w_estride = (int64_t)D * 2 * F;
@@ -1339,7 +1389,7 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
   const WgradLayout L = wgrad_layout(p, row_off_h, sched.kc_max);
   WgradArgs w{};
   w.t[0] = WgradType{(const uint16_t*)PhiC, F, phi_rows, phi_nrows, (const uint16_t*)Dlt, D, dW2, F, D,
-                     (int)ceil_div(F, BM), (int)ceil_div(D, BN), wgrad_tiles(F, D)};
+                     (int)ceil_div(F, BM), (int)ceil_div(D, BN), wgrad_tiles(F, D), dlt_rows, dlt_nrows};
   w.ntypes = 1;
   if (p->swiglu) {
     w.t[1] = WgradType{(const uint16_t*)XC, D, x_rows, x_nrows, (const uint16_t*)dH, 2 * F, dW1, D, 2 * F,
@@ -1362,12 +1412,14 @@ lrmoe_status launch_grouped_gemm_bwd(const lrmoe_problem* p, const int64_t* row_
     const int64_t per_xcd = sched.per_xcd;
     wgrad_plan_kernel<<<1, kAuxThr, 0, s>>>(w);
     const unsigned grid = (unsigned)(8 * per_xcd);
-    const bool g0 = phi_rows != nullptr, g1 = x_rows != nullptr;
+    const bool g0 = phi_rows != nullptr, g1 = x_rows != nullptr, gb0 = dlt_rows != nullptr;
     if (per_xcd > 0) {
-      if (g0 && g1) wgrad_kernel<true, true><<<grid, CfgW::NTHR, 0, s>>>(w);
-      else if (g0) wgrad_kernel<true, false><<<grid, CfgW::NTHR, 0, s>>>(w);
-      else if (g1) wgrad_kernel<false, true><<<grid, CfgW::NTHR, 0, s>>>(w);
-      else wgrad_kernel<false, false><<<grid, CfgW::NTHR, 0, s>>>(w);
+      if (gb0 && g1) wgrad_kernel<false, true, true><<<grid, CfgW::NTHR, 0, s>>>(w);
+      else if (gb0) wgrad_kernel<false, false, true><<<grid, CfgW::NTHR, 0, s>>>(w);
+      else if (g0 && g1) wgrad_kernel<true, true, false><<<grid, CfgW::NTHR, 0, s>>>(w);
+      else if (g0) wgrad_kernel<true, false, false><<<grid, CfgW::NTHR, 0, s>>>(w);
+      else if (g1) wgrad_kernel<false, true, false><<<grid, CfgW::NTHR, 0, s>>>(w);
+      else wgrad_kernel<false, false, false><<<grid, CfgW::NTHR, 0, s>>>(w);
     }
     if (L.nreduce > 0) wgrad_reduce_kernel<<<(unsigned)(L.nreduce * kRedParts), kAuxThr, 0, s>>>(w);
   }

@@ -57,8 +57,8 @@ size_t backward_buffer_bytes(const lrmoe_problem* p, int64_t K_tot, bool packed)
   const size_t w = sw ? D : F;
   size_t b = N * sizeof(float) + N;            // R, keep
   b += K * 3 * sizeof(int32_t);                // sel, ctok, cslot
-  b += K * D * e;                              // Dlt
-  if (packed) b += K * F * e + (sw ? K * D * e + K * 2 * F * e : 0);  // PhiC (XC, HC)
+  if (!packed) b += K * F * e;                 // PhiW
+  else b += K * D * e + K * F * e + (sw ? K * D * e + K * 2 * F * e : 0);  // Dlt, PhiC (XC, HC)
   if (sw) b += K * 2 * F * e;                  // dH
   b += K * w * e;                              // dIn
   b += E * F * D * sizeof(float);              // dW2
@@ -281,8 +281,45 @@ lrmoe_status lrmoe_grouped_gemm_bwd(const lrmoe_problem* p, lrmoe_compact_mode m
     return LRMOE_ERR_UNSUPPORTED;
   if (ws_bytes < gemm_ws_bytes(p, row_off_h) || (!ws && gemm_ws_bytes(p, row_off_h) > 0))
     return LRMOE_ERR_WORKSPACE;
-  return launch_grouped_gemm_bwd(p, row_off_h, row_off_d, Dlt, PhiC, XC, HC, hc_rows, phi_rows, x_rows, W2, W1,
-                                 dW2, dW1, dH, dIn, accumulate, ws, (hipStream_t)stream, (hipEvent_t)din_ready);
+  return launch_grouped_gemm_bwd(p, row_off_h, row_off_d, Dlt, PhiC, XC, HC, hc_rows, phi_rows, x_rows, nullptr,
+                                 nullptr, W2, W1, dW2, dW1, dH, dIn, accumulate, ws, (hipStream_t)stream,
+                                 (hipEvent_t)din_ready);
+}
+
+lrmoe_status lrmoe_compact_weighted(const lrmoe_problem* p, const int32_t* sel, const void* Phi, const float* alpha,
+                                    void* PhiW, lrmoe_stream_t stream) {
+  int64_t K_tot = 0;
+  LRMOE_TRY(check_problem(p, &K_tot, nullptr));
+  if (K_tot == 0) return LRMOE_OK;
+  if (!sel || !Phi || !alpha || !PhiW) return LRMOE_ERR_INVALID_ARG;
+  return launch_compact_weighted_phi(p, K_tot, sel, Phi, alpha, PhiW, (hipStream_t)stream);
+}
+
+lrmoe_status lrmoe_grouped_gemm_bwd_gathered(const lrmoe_problem* p, const int64_t* cseg_off_d, const void* G,
+                                             const float* alpha, const int32_t* sel, const int32_t* ctok,
+                                             const void* PhiW, const void* X, const void* H, const void* W2,
+                                             const void* W1, float* dW2, float* dW1, void* dH, void* dIn,
+                                             int32_t accumulate, void* ws, size_t ws_bytes, lrmoe_stream_t stream,
+                                             lrmoe_event_t din_ready) {
+  std::vector<int64_t> cseg;
+  int64_t K_tot = 0;
+  LRMOE_TRY(check_problem(p, &K_tot, &cseg));
+  if (accumulate != 0 && accumulate != 1) return LRMOE_ERR_INVALID_ARG;
+  if (!cseg_off_d || !W2 || !dW2) return LRMOE_ERR_INVALID_ARG;
+  if (K_tot > 0 && (!G || !alpha || !sel || !ctok || !PhiW || !dIn)) return LRMOE_ERR_INVALID_ARG;
+  if (p->swiglu) {
+    if (!W1 || !dW1 || (K_tot > 0 && (!X || !H || !dH))) return LRMOE_ERR_INVALID_ARG;
+  } else if (W1 || dW1 || dH || X || H) {
+    return LRMOE_ERR_INVALID_ARG;
+  }
+  // G and X are read by token with 32-bit byte offsets
+  const int64_t esz = p->dtype == LRMOE_BF16 ? 2 : 4;
+  if ((int64_t)p->T * p->D * esz >= ((int64_t)1 << 31)) return LRMOE_ERR_UNSUPPORTED;
+  const size_t need = gemm_ws_bytes(p, cseg.data());
+  if (ws_bytes < need || (!ws && need > 0)) return LRMOE_ERR_WORKSPACE;
+  return launch_grouped_gemm_bwd(p, cseg.data(), cseg_off_d, G, PhiW, X, H, sel, nullptr, p->swiglu ? ctok : nullptr,
+                                 ctok, alpha, W2, W1, dW2, dW1, dH, dIn, accumulate, ws, (hipStream_t)stream,
+                                 (hipEvent_t)din_ready);
 }
 
 lrmoe_status lrmoe_scatter(const lrmoe_problem* p, lrmoe_scatter_mode mode, int64_t n_rows, int32_t width,

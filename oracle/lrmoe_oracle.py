@@ -318,17 +318,21 @@ def backward_bytes(*, T, E, D, F, swiglu, dtype, N, K_tot, packed=False, workspa
     scratch layout, so the caller supplies it) plus the buffers, listed one by one (e =
     bytes of the storage dtype; w = D for SwiGLU experts, F for an FC2-only expert):
       scores R f32 [N], keep flags u8 [N]; sel, ctok, cslot int32 [K_tot];
-      Dlt [K_tot x D] e; packed saved rows PhiC [K_tot x F] e (SwiGLU: XC [K_tot x D],
-      HC [K_tot x 2F] too); SwiGLU dH [K_tot x 2F] e; input gradients [K_tot x w] e;
+      the packed rows of step 3: by default only the weighted saved rows PhiW [K_tot x F] e
+      (the gradient, saved-activation and FC1-input rows are then read in place, by token or
+      by pair); with ``packed`` the weighted gradient rows Dlt [K_tot x D] e and the saved
+      rows PhiC [K_tot x F] e (SwiGLU: XC [K_tot x D], HC [K_tot x 2F] too);
+      SwiGLU dH [K_tot x 2F] e; input gradients [K_tot x w] e;
       weight gradients f32: dW2 [E x F x D] (SwiGLU: dW1 [E x D x 2F]); scatter output
       f32 [T x w]."""
     e = 2 if dtype == "bf16" else 4
     w = D if swiglu else F
     b = 4 * N + N
     b += 3 * 4 * K_tot
-    b += K_tot * D * e
-    if packed:
+    if not packed:
         b += K_tot * F * e
+    else:
+        b += K_tot * D * e + K_tot * F * e
         if swiglu:
             b += K_tot * D * e + K_tot * 2 * F * e
     if swiglu:

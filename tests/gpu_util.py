@@ -59,10 +59,10 @@ class Staged:
         self.tok = torch.from_numpy(r.tok).to(DEV)
         self.slot = torch.from_numpy(r.slot).to(DEV)
 
-    def backward(self, mode=lr.COMPACT_PHYSICAL, scatter_mode=lr.SCATTER_TOKEN, bufs=None):
+    def backward(self, mode=lr.COMPACT_PHYSICAL, scatter_mode=lr.SCATTER_TOKEN, bufs=None, packed_dlt=False):
         return lr.backward(self.P, G=self.G, Phi=self.Phi, alpha=self.alpha, tok=self.tok, slot=self.slot,
                            W2=self.W2, X=self.X, H=self.H, W1=self.W1, mode=mode, scatter_mode=scatter_mode,
-                           bufs=bufs)
+                           bufs=bufs, packed_dlt=packed_dlt)
 
 
 def rel_fro(a, b) -> float:

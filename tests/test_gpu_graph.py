@@ -26,7 +26,7 @@ def test_backward_step_replays_in_a_graph(name, rho):
         return lr.backward(s.P, G=s.G, Phi=s.Phi, alpha=s.alpha, tok=s.tok, slot=s.slot, W2=s.W2, X=s.X, H=s.H,
                            W1=s.W1, bufs=bufs)
 
-    keys = ("R", "sel", "Dlt", "dW2", "dIn", "out") + (("dW1", "dH") if sw else ())
+    keys = ("R", "sel", "PhiW", "dW2", "dIn", "out") + (("dW1", "dH") if sw else ())
     side = torch.cuda.Stream()
     with torch.cuda.stream(side):
         for _ in range(3):  # first calls allocate every buffer; capture needs them in place

@@ -1,9 +1,10 @@
 """GPU parity at the largest addresses the path accepts.
 
-The weight-gradient GEMM reads the expert input X in place, through the packed rows'
-token map, with 32-bit byte offsets; the library accepts that while T * D * 2 < 2^31 and
-rejects larger X (unsupported). Here T = 2^20 - 1 and D = 1024, so X and G are
-2^31 - 2048 bytes each and the gathered rows of the last tokens sit just under the limit.
+The grouped GEMMs read the expert input X and the gradient rows G in place, through the
+packed rows' token map, with 32-bit byte offsets; the library accepts that while
+T * D * 2 < 2^31 and rejects larger X and G (unsupported). Here T = 2^20 - 1 and D = 1024,
+so X and G are 2^31 - 2048 bytes each and the gathered rows of the last tokens sit just
+under the limit.
 The forward's FC1 launch gathers X the same way. The token-order scatter writes a
 [T x D] fp32 output of 4 GiB, past 32-bit byte offsets.
 
@@ -89,7 +90,7 @@ def test_limit_score_select_compact(limit):
     # ctok holds original token ids; the oracle's are renumbered
     assert np.array_equal(res["ctok"].cpu().numpy(), limit["toks"][ref["ctok"]])
     assert np.array_equal(res["cslot"].cpu().numpy(), ref["cslot"])
-    assert np.array_equal(bits(res["Dlt"]), oracle.round_bf16(ref["Dlt"]))
+    assert np.array_equal(bits(res["PhiW"]), oracle.round_bf16(ref["PhiW"]))
 
 
 def test_limit_grouped_gemm(limit):

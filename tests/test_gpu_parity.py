@@ -5,13 +5,15 @@ split reductions, dims that are not tile multiples). Calls go through the C ABI.
 Tolerances (derived in the design notes from the arithmetic each step does):
 * score: |R - R_oracle| <= 1e-6 R_oracle.
 * select / compaction indices: bit-exact (selection taken on f32 scores on both sides).
-* compaction rows: bit-exact copies; Dlt = bf16 nearest of the exact alpha*g.
-* GEMM outputs against the exact oracle: the packed gradient rows Dlt and dH are stored
+* compaction rows: bit-exact copies; PhiW = bf16 nearest of the exact alpha*phi (the
+  default path), Dlt = bf16 nearest of the exact alpha*g (the packed-Dlt path).
+* GEMM outputs against the exact oracle: the packed rows PhiW or Dlt and dH are stored
   in bf16 (relative rounding error <= 2^-9, rms ~1.1e-3), so weight gradients, dH and
   input gradients get rel. Frobenius <= 5e-3 per expert (spec bar 2e-2), and every
   packed input-gradient row <= 2e-2.
-* GEMM outputs against the oracle fed the bf16-stored Dlt: FC2 weight gradient rel.
-  Frobenius <= 1e-5 (fp32 accumulation only); dH per element <= 2^-8 |ref| + 2e-5 rms(row).
+* GEMM outputs against the oracle fed what the GEMMs read at its stored precision (PhiW
+  and the token rows of G, or the bf16-stored Dlt): FC2 weight gradient rel. Frobenius
+  <= 1e-5 (fp32 accumulation only); dH per element <= 2^-8 |ref| + 2e-5 rms(row).
 * f32 path: rel. Frobenius <= 1e-5.
 """
 import numpy as np
@@ -82,6 +84,7 @@ def case(request):
     r = pr.routing
     log(f"case {request.param}: GPU path (N={s.P.N}, K_tot={s.P.K_tot})")
     res = s.backward()
+    res["packed_dlt"] = s.backward(packed_dlt=True)  # the path that packs Dlt
     torch.cuda.synchronize()
     ref = oracle.backward(G=pr.G, Phi=pr.Phi, alpha=r.alpha, tok=r.tok, slot=r.slot, seg_off=r.seg_off,
                           quota=pr.quota, dtype=pr.cfg.dtype, T=pr.cfg.T, W2=pr.W2, X=pr.X, H=pr.H, W1=pr.W1)
@@ -150,32 +153,42 @@ def test_compact(case):
     assert np.array_equal(res["ctok"].cpu().numpy(), ref["ctok"])
     assert np.array_equal(res["cslot"].cpu().numpy(), ref["cslot"])
     sel = ref["sel"]
-    # the path packs only the gradient rows: the GEMMs read Phi, X and H in place
-    assert "PhiC" not in res and "XC" not in res and "HC" not in res
+    # the default path packs only the weighted saved rows PhiW (one rounding of the exact
+    # product); the GEMMs read G, X and H in place
+    assert "Dlt" not in res and "PhiC" not in res and "XC" not in res and "HC" not in res
+    if dt == "bf16":
+        assert np.array_equal(bits(res["PhiW"]), oracle.round_bf16(ref["PhiW"]))
+    else:
+        assert np.array_equal(res["PhiW"].cpu().numpy(), np.asarray(ref["PhiW"], dtype=np.float32))
+    # the packed-Dlt path packs the weighted gradient rows only
+    dl = res["packed_dlt"]
+    assert "PhiC" not in dl and "XC" not in dl and "HC" not in dl
     # packing the saved rows on request: bitwise Phi[sel], X[tok[sel]], H[sel]
     c = lr.compact(s.P, s.G, s.Phi, s.alpha, s.tok, s.slot, sel=res["sel"], keep=res["keep"],
                    X=s.X if pr.cfg.swiglu else None, H=s.H if pr.cfg.swiglu else None)
     torch.cuda.synchronize()
     assert np.array_equal(bits(c["PhiC"]), pr.Phi[sel])
-    assert torch.equal(c["Dlt"], res["Dlt"])
+    assert torch.equal(c["Dlt"], dl["Dlt"])
     # compaction building its own (token, slot) map gives the selection's ctok and cslot
     assert torch.equal(c["ctok"], res["ctok"]) and torch.equal(c["cslot"], res["cslot"])
     if pr.cfg.swiglu:
         assert np.array_equal(bits(c["XC"]), pr.X[pr.routing.tok[sel]])
         assert np.array_equal(bits(c["HC"]), pr.H[sel])
     if dt == "bf16":
-        assert np.array_equal(bits(res["Dlt"]), oracle.round_bf16(ref["Dlt"]))
+        assert np.array_equal(bits(dl["Dlt"]), oracle.round_bf16(ref["Dlt"]))
     else:
-        np.testing.assert_allclose(as_f64(res["Dlt"]), ref["Dlt"], rtol=2 ** -23, atol=0)
+        np.testing.assert_allclose(as_f64(dl["Dlt"]), ref["Dlt"], rtol=2 ** -23, atol=0)
 
 
-def test_grouped_gemm(case):
+@pytest.mark.parametrize("variant", ["gathered", "packed_dlt"])
+def test_grouped_gemm(case, variant):
     name, pr, s, res, ref = case
+    res = res if variant == "gathered" else res["packed_dlt"]
     E = pr.cfg.E
     cseg = ref["cseg_off"]
     f32 = pr.cfg.dtype == "f32"
     bar = 1e-5 if f32 else 2e-2      # spec bar
-    derived = 1e-5 if f32 else 5e-3  # bf16 storage of Dlt and dH: ~1.1e-3 rms each
+    derived = 1e-5 if f32 else 5e-3  # bf16 storage of Dlt (or PhiW) and dH: ~1.1e-3 rms each
     dW2 = as_f64(res["dW2"])
     for e in range(E):
         assert rel_fro(dW2[e], ref["dW2"][e]) <= derived, f"{name}: dW2 expert {e}"
@@ -195,10 +208,12 @@ def test_grouped_gemm(case):
 
 
 def test_grouped_gemm_at_storage_precision(case):
-    """Same GEMMs against the oracle fed the packed gradient rows at their stored precision
-    (bf16 for the pages' BF16 storage, f32 for the tiny config): the FC2 weight gradient
-    then differs only by fp32 accumulation, and dH by that plus its own storage rounding."""
+    """The packed-Dlt path's GEMMs against the oracle fed the packed gradient rows at their
+    stored precision (bf16 for the pages' BF16 storage, f32 for the tiny config): the FC2
+    weight gradient then differs only by fp32 accumulation, and dH by that plus its own
+    storage rounding."""
     name, pr, s, res, ref = case
+    res = res["packed_dlt"]
     bf16 = pr.cfg.dtype == "bf16"
     if bf16:
         dlt = oracle.widen(oracle.round_bf16(ref["Dlt"]), "bf16")
@@ -221,6 +236,41 @@ def test_grouped_gemm_at_storage_precision(case):
     got2 = as_f64(res["dW2"])
     for e in range(pr.cfg.E):
         assert rel_fro(got2[e], dW2[e]) <= 1e-5, f"{name}: dW2 expert {e}"
+
+
+def test_gathered_at_storage_precision(case):
+    """The default path's GEMMs (gradient rows G[ctok] read by token, the FC2 data gradient
+    scaled by alpha in fp32, the FC2 weight gradient from the stored PhiW) against the oracle
+    fed what they read: the FC2 weight gradient differs by fp32 accumulation only, and dH
+    (against the exact oracle, since the gradient rows are not rounded on this path) by that
+    and its own storage rounding."""
+    name, pr, s, res, ref = case
+    dt = pr.cfg.dtype
+    bf16 = dt == "bf16"
+    g = res
+    cseg = ref["cseg_off"]
+    dW2 = as_f64(g["dW2"])
+    if pr.cfg.swiglu:
+        got, dH = as_f64(g["dH"]), ref["dH"]
+        if bf16:
+            rms = np.sqrt(np.mean(dH ** 2, axis=1, keepdims=True))
+            assert np.all(np.abs(got - dH) <= 2 ** -8 * np.abs(dH) + 2e-5 * rms), name
+        else:
+            assert rel_fro(got, dH) <= 1e-5, name
+    else:  # one rounding of the scaled fp32 product
+        assert rel_fro(as_f64(g["dIn"]), ref["dPhi"]) <= (4e-3 if bf16 else 1e-5), name
+    # FC2 weight gradient against the oracle fed the stored PhiW and the token rows
+    phiw = oracle.widen(oracle.round_bf16(ref["PhiW"]), "bf16") if bf16 else \
+        np.asarray(ref["PhiW"], dtype=np.float32).astype(np.float64)
+    g_rows = oracle.widen(pr.G, dt)[np.asarray(ref["ctok"], dtype=np.int64)]
+    W2 = oracle.widen(pr.W2, dt)
+    if pr.cfg.swiglu:
+        _, dW2_s, _, _ = oracle.swiglu_expert_backward(cseg, g_rows, phiw, ref["XC"], ref["HC"],
+                                                       oracle.widen(pr.W1, dt), W2)
+    else:
+        dW2_s, _ = oracle.linear_expert_backward(cseg, g_rows, phiw, W2)
+    for e in range(pr.cfg.E):
+        assert rel_fro(dW2[e], dW2_s[e]) <= 1e-5, f"{name}: dW2 expert {e} at storage precision"
 
 
 def test_scatter_token_order(case):
@@ -269,7 +319,7 @@ def test_deterministic(case):
     name, pr, s, res, ref = case
     again = s.backward()
     torch.cuda.synchronize()
-    for k in ("R", "sel", "Dlt", "dW2", "dIn", "out") + (("dW1", "dH") if pr.cfg.swiglu else ()):
+    for k in ("R", "sel", "PhiW", "dW2", "dIn", "out") + (("dW1", "dH") if pr.cfg.swiglu else ()):
         assert torch.equal(res[k], again[k]), k
 
 
@@ -288,15 +338,20 @@ def test_scatter_overlapped_with_weight_gradients_matches_serial(case):
 def test_accumulate_adds_to_weight_gradients():
     pr = _make("swiglu_ragged")
     s = Staged(pr)
-    res = s.backward()
-    base2, base1 = res["dW2"].clone(), res["dW1"].clone()
-    c = res
+    c = s.backward(packed_dlt=True)
+    base2, base1 = c["dW2"].clone(), c["dW1"].clone()
     g = lr.grouped_gemm_bwd(s.P, c["Dlt"], s.Phi, s.W2, XC=s.X, HC=s.H, hc_rows=c["sel"], phi_rows=c["sel"],
                             x_rows=c["ctok"], W1=s.W1, out={"dW2": base2.clone(), "dW1": base1.clone()},
                             accumulate=True)
+    r = s.backward()
+    b2, b1 = r["dW2"].clone(), r["dW1"].clone()
+    h = lr.grouped_gemm_bwd_gathered(s.P, s.G, s.alpha, r["sel"], r["ctok"], r["PhiW"], s.W2, X=s.X, H=s.H,
+                                     W1=s.W1, out={"dW2": b2.clone(), "dW1": b1.clone()}, accumulate=True)
     torch.cuda.synchronize()
     assert torch.allclose(g["dW2"], 2 * base2, rtol=1e-6, atol=1e-6)
     assert torch.allclose(g["dW1"], 2 * base1, rtol=1e-6, atol=1e-6)
+    assert torch.allclose(h["dW2"], 2 * b2, rtol=1e-6, atol=1e-6)
+    assert torch.allclose(h["dW1"], 2 * b1, rtol=1e-6, atol=1e-6)
 
 
 @pytest.mark.parametrize("name", ["swiglu_ragged", "swiglu_split_k", "swiglu_f32", "linear_bf16"])
@@ -306,7 +361,7 @@ def test_packed_rows_match_reading_them_in_place(name):
     products in the same order, only the loads differ)."""
     pr = _make(name)
     s = Staged(pr)
-    res = s.backward()
+    res = s.backward(packed_dlt=True)
     sw = pr.cfg.swiglu
     c = lr.compact(s.P, s.G, s.Phi, s.alpha, s.tok, s.slot, sel=res["sel"], keep=res["keep"],
                    X=s.X if sw else None, H=s.H if sw else None)
@@ -365,6 +420,37 @@ def test_row_maps_out_of_range_read_zeros(name):
     torch.cuda.synchronize()
     for k in ("dW1", "dW2", "dH", "dIn"):
         assert torch.equal(got[k], want[k]), k
+
+
+@pytest.mark.parametrize("name", ["swiglu_ragged", "swiglu_f32", "linear_bf16"])
+def test_gathered_maps_out_of_range_read_zeros(name):
+    """The path reading gradient rows by token: a packed row whose token (ctok) or pair
+    (sel) lies outside the matrices reads zero gradient, FC1-input, [gate | up] and weighted
+    saved rows and a zero routing weight, so it adds nothing: the same gradients, bit for
+    bit, as valid maps with a zero routing weight on those rows."""
+    pr = _make(name)
+    s = Staged(pr)
+    res = s.backward()
+    torch.cuda.synchronize()
+    sw = pr.cfg.swiglu
+    K_tot = s.P.K_tot
+    rng = np.random.default_rng(4)
+    bad = rng.choice(K_tot, size=max(1, K_tot // 10), replace=False)
+    bad_t = torch.from_numpy(bad).to(DEV)
+    sel_bad, ctok_bad = res["sel"].clone(), res["ctok"].clone()
+    sel_bad[bad_t] = torch.from_numpy(np.where(bad % 2 == 0, -1, s.P.N + 7).astype(np.int32)).to(DEV)
+    ctok_bad[bad_t] = torch.from_numpy(np.where(bad % 3 == 0, pr.cfg.T, -5).astype(np.int32)).to(DEV)
+    alpha0 = s.alpha.clone()
+    alpha0[res["sel"][bad_t].long()] = 0.0
+    kw = dict(X=s.X, H=s.H, W1=s.W1) if sw else {}
+    got = lr.grouped_gemm_bwd_gathered(s.P, s.G, s.alpha, sel_bad, ctok_bad,
+                                       lr.compact_weighted(s.P, sel_bad, s.Phi, s.alpha), s.W2, **kw)
+    want = lr.grouped_gemm_bwd_gathered(s.P, s.G, alpha0, res["sel"], res["ctok"],
+                                        lr.compact_weighted(s.P, res["sel"], s.Phi, alpha0), s.W2, **kw)
+    torch.cuda.synchronize()
+    for k in (("dW1", "dW2", "dH", "dIn") if sw else ("dW2", "dIn")):
+        assert torch.equal(got[k], want[k]), k
+    assert not bool(got["dIn"][bad_t].float().abs().sum())
 
 
 def test_all_equal_scores_break_ties_by_index():
@@ -428,17 +514,21 @@ def test_pairs_without_a_position():
     s = Staged(pr)
     s.tok = torch.from_numpy(tok).to(DEV)
     s.slot = torch.from_numpy(slot).to(DEV)
-    res = s.backward()
+    res = s.backward(packed_dlt=True)
     c = lr.compact(s.P, s.G, s.Phi, s.alpha, s.tok, s.slot, sel=res["sel"], keep=res["keep"], pack_phi=False)
     out2 = lr.scatter(s.P, res["dIn"], c["ctok"], c["cslot"])
+    gat = s.backward()  # gradient rows read by token: a row with ctok = -1 reads zeros
     torch.cuda.synchronize()
     bad = np.array(bad_tok + bad_slot)
     sel = res["sel"].cpu().numpy()
     rows = np.searchsorted(sel, bad)
+    rows_t = torch.from_numpy(rows).to(DEV)
     assert np.array_equal(sel[rows], bad)
-    for got in (res, c):
+    for got in (res, c, gat):
         assert np.all(got["ctok"].cpu().numpy()[rows] == -1) and np.all(got["cslot"].cpu().numpy()[rows] == -1)
-        assert not bool(got["Dlt"][torch.from_numpy(rows).to(DEV)].float().abs().sum())
+    for got in (res, c):
+        assert not bool(got["Dlt"][rows_t].float().abs().sum())
+    assert not bool(gat["dIn"][rows_t].float().abs().sum())
     assert torch.equal(c["Dlt"], res["Dlt"]) and torch.equal(out2, res["out"])
     alpha0 = r.alpha.copy()
     alpha0[bad] = 0.0
@@ -450,3 +540,7 @@ def test_pairs_without_a_position():
         assert rel_fro(as_f64(res["dW2"][e]), ref["dW2"][e]) <= 5e-3, f"dW2 expert {e}"
         assert rel_fro(as_f64(res["dW1"][e]), ref["dW1"][e]) <= 5e-3, f"dW1 expert {e}"
     assert rel_fro(as_f64(res["out"]), ref["out"]) <= 5e-3
+    for e in range(cfg.E):
+        assert rel_fro(as_f64(gat["dW2"][e]), ref["dW2"][e]) <= 5e-3, f"gathered dW2 expert {e}"
+        assert rel_fro(as_f64(gat["dW1"][e]), ref["dW1"][e]) <= 5e-3, f"gathered dW1 expert {e}"
+    assert rel_fro(as_f64(gat["out"]), ref["out"]) <= 5e-3

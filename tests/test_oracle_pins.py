@@ -204,9 +204,10 @@ def _buffer_bytes_of_outputs(o, p, packed):
     size = lambda a: int(np.prod(np.asarray(a).shape))  # noqa: E731
     b = 4 * size(out["R"]) + 1 * size(out["R"])          # scores, keep flags
     b += 4 * (size(out["sel"]) + size(out["ctok"]) + size(out["cslot"]))
-    b += e * size(out["Dlt"])
-    if packed:
-        b += e * size(out["PhiC"])
+    if not packed:
+        b += e * size(out["PhiW"])
+    else:
+        b += e * (size(out["Dlt"]) + size(out["PhiC"]))
         if p.cfg.swiglu:
             b += e * (size(out["XC"]) + size(out["HC"]))
     if p.cfg.swiglu:

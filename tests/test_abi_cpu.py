@@ -228,3 +228,47 @@ def test_select_noalloc_refuses_problems_beyond_its_scratch():
                                     None, None) == _lib.ERR_INVALID_ARG
     assert lib.lrmoe_select_noalloc(ctypes.byref(q), fake, fake, fake, fake, fake, None, None, None, None, fake,
                                     None, None) == _lib.ERR_INVALID_ARG
+
+
+def _gathered(p, swiglu=True, **kw):
+    """lrmoe_grouped_gemm_bwd_gathered with every pointer set (fake device addresses) except
+    those overridden; returns the status of the host checks."""
+    fake = ctypes.c_void_p(0x1000)
+    a = dict(cseg=fake, G=fake, alpha=fake, sel=fake, ctok=fake, PhiW=fake, X=fake if swiglu else None,
+             H=fake if swiglu else None, W2=fake, W1=fake if swiglu else None, dW2=fake,
+             dW1=fake if swiglu else None, dH=fake if swiglu else None, dIn=fake, acc=0, ws=None, ws_bytes=0)
+    a.update(kw)
+    return _lib.load().lrmoe_grouped_gemm_bwd_gathered(
+        ctypes.byref(p), a["cseg"], a["G"], a["alpha"], a["sel"], a["ctok"], a["PhiW"], a["X"], a["H"], a["W2"],
+        a["W1"], a["dW2"], a["dW1"], a["dH"], a["dIn"], a["acc"], a["ws"], a["ws_bytes"], None, None)
+
+
+def test_gathered_path_host_checks():
+    """The path that reads gradient rows by token: lrmoe_compact_weighted and
+    lrmoe_grouped_gemm_bwd_gathered refuse missing buffers, SwiGLU-only arguments on a
+    linear problem, a G or X of 2 GiB or more (32-bit offsets) and a missing workspace,
+    on the host, before any launch."""
+    lib = _lib.load()
+    fake = ctypes.c_void_p(0x1000)
+    p, keep = _problem()
+    assert lib.lrmoe_compact_weighted(ctypes.byref(p), None, fake, fake, fake, None) == _lib.ERR_INVALID_ARG
+    assert lib.lrmoe_compact_weighted(ctypes.byref(p), fake, fake, None, fake, None) == _lib.ERR_INVALID_ARG
+    z, keep_z = _problem(quota=(0, 0, 0))  # nothing retained: nothing to check or launch
+    assert lib.lrmoe_compact_weighted(ctypes.byref(z), None, None, None, None, None) == _lib.OK
+    bad_q, keep_b = _problem(quota=(6, 0, 7))
+    assert lib.lrmoe_compact_weighted(ctypes.byref(bad_q), fake, fake, fake, fake, None) == _lib.ERR_INFEASIBLE_QUOTA
+    # every buffer the step reads or writes is required
+    for k in ("cseg", "G", "alpha", "sel", "ctok", "PhiW", "X", "H", "W2", "W1", "dW2", "dW1", "dH", "dIn"):
+        assert _gathered(p, **{k: None}) == _lib.ERR_INVALID_ARG, k
+    assert _gathered(p, acc=2) == _lib.ERR_INVALID_ARG
+    # the weight-gradient plan needs the workspace the library asks for
+    assert _gathered(p) == _lib.ERR_WORKSPACE
+    # a linear (FC2-only) problem takes no SwiGLU operands
+    lin, keep_l = _problem(swiglu=0)
+    assert _gathered(lin, swiglu=False, X=fake) == _lib.ERR_INVALID_ARG
+    assert _gathered(lin, swiglu=False, dH=fake) == _lib.ERR_INVALID_ARG
+    # G and X of T * D * 2 bytes = 2^24 * 64 * 2 = 2 GiB are read with 32-bit offsets: refused
+    big, keep_g = _problem(E=1, T=1 << 24, K=1, D=64, F=32, counts=(8,), quota=(3,))
+    assert _gathered(big) == _lib.ERR_UNSUPPORTED
+    ok, keep_o = _problem(E=1, T=(1 << 24) - 1, K=1, D=64, F=32, counts=(8,), quota=(3,))
+    assert _gathered(ok) == _lib.ERR_WORKSPACE  # the checks move on to the missing workspace

@@ -199,11 +199,12 @@ lrmoe_status lrmoe_select(const lrmoe_problem* p, const float* R, const int64_t*
  * same arguments and results as lrmoe_select minus (ws, ws_bytes). Its scratch is a fixed
  * 4 MiB array of the library's, one per GPU, held until the process ends; the call
  * allocates and frees nothing. The stream's device must be the current device. The
- * selection needs E x 8 KB of digit histograms, E x 16 B of segment state and 16 B per
- * expert per 4096-pair chunk of the longest segment (each part rounded up to 256 B; about
- * 150 KB for 16 experts of up to 200k pairs); a problem that needs more than 4 MiB is
- * refused with LRMOE_ERR_WORKSPACE before any launch. The selection's first launch clears
- * what it accumulates into, so a call does not depend on the previous call's contents.
+ * selection needs E x 20 KB of digit histograms (one per radix pass), E x 64 B of segment
+ * state and 16 B per expert per 4096-pair chunk of the longest segment (each part rounded
+ * up to 256 B; about 340 KB for 16 experts of up to 200k pairs); a problem that needs more
+ * than 4 MiB is refused with LRMOE_ERR_WORKSPACE before any launch. The selection's first
+ * launch clears what it accumulates into, so a call does not depend on the previous call's
+ * contents.
  * All calls on one GPU share the array: calls that overlap in time on one GPU (other
  * streams, other host threads) race; calls in order on one stream do not. */
 lrmoe_status lrmoe_select_noalloc(const lrmoe_problem* p, const float* R, const int64_t* seg_off_d,

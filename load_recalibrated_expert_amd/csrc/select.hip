@@ -6,13 +6,16 @@
 //
 // Scores are non-negative f32, so their bit patterns order like unsigned integers. The
 // q_e-th largest key of every segment is found by a three-pass most-significant-digit
-// radix select (11, 11 and 10 bits). A pass is two launches: chunk blocks (4096 keys of one
-// segment each) build LDS histograms of the digit among keys that still match the fixed
-// prefix and add them to the segment's global histogram; then one block per segment scans
-// its histogram from the highest bin and fixes the digit. The write side is three more
-// launches: chunk blocks count keys above and equal to the threshold, one block per segment
-// turns the counts into chunk offsets, and chunk blocks write the retained indices at
-// positions given by block-level ballot scans. Kernel boundaries order every step, so no
+// radix select (11, 11 and 10 bits). In pass p, chunk blocks (4096 keys of one segment
+// each) build LDS histograms of the digit among keys that still match the prefix fixed so
+// far and add them to the segment's global histogram of that pass (each pass has its own).
+// The digit of pass p is fixed in the next launch, by every one of its blocks: each scans
+// the finished histogram from the highest bin (a few KB from L2) and block 0 of the segment
+// records the resulting state for the launches after it. The write side is two launches:
+// chunk blocks count keys above and equal to the threshold (fixing the last digit first),
+// and chunk blocks write the retained indices at positions given by the counts of the
+// chunks before them and block-level ballot scans (segments of more than 256 chunks get
+// those offsets from a launch of their own). Kernel boundaries order every step, so no
 // block waits on another and no block needs a device-wide fence. On request the write
 // launch also records, for every retained pair, its packed row in a (token, slot) map and
 // its token and slot in packed order (the init launch clears the map), so compaction and
@@ -29,6 +32,11 @@ constexpr int kSelThreads = 256;
 constexpr int kSelPer = 16;
 constexpr int kChunk = kSelThreads * kSelPer;  // keys per chunk block
 constexpr int kBins = 2048;
+constexpr int kPasses = 3;
+constexpr int kShift[kPasses] = {21, 10, 0}, kBits[kPasses] = {11, 11, 10};
+constexpr int kPassBins = (1 << 11) + (1 << 11) + (1 << 10);  // histogram bins of all passes
+// segments of at most this many chunks get their write offsets inside the write launch
+constexpr int kFusedOffsMaxChunks = kSelThreads;
 
 enum : uint32_t { kKeepNone = 0, kKeepAll = 1, kKeepThreshold = 2 };
 
@@ -52,11 +60,13 @@ struct PosOut {
 };
 
 struct SelWs {
-  uint32_t* hist;    // [E][kBins]
-  SegState* state;   // [E]
+  uint32_t* hist;    // [E][kPassBins]: pass 0 bins, then pass 1, then pass 2
+  SegState* state;   // [kPasses + 1][E]: state[p] holds the digits of passes < p
   uint32_t* counts;  // [E][maxch][2]  keys above / equal to the threshold, per chunk
   uint32_t* offs;    // [E][maxch][2]  exclusive prefix of counts within the segment
 };
+
+__host__ __device__ constexpr int pass_bin0(int pass) { return pass == 0 ? 0 : pass == 1 ? 2048 : 4096; }
 
 int max_chunks(const lrmoe_problem* p) {
   int64_t m = 1;
@@ -69,9 +79,9 @@ SelWs carve(void* ws, int E, int maxch) {
   SelWs w;
   size_t o = 0;
   w.hist = (uint32_t*)(b + o);
-  o = align_up(o + sizeof(uint32_t) * (size_t)E * kBins, 256);
+  o = align_up(o + sizeof(uint32_t) * (size_t)E * kPassBins, 256);
   w.state = (SegState*)(b + o);
-  o = align_up(o + sizeof(SegState) * (size_t)E, 256);
+  o = align_up(o + sizeof(SegState) * (size_t)E * (kPasses + 1), 256);
   w.counts = (uint32_t*)(b + o);
   o = align_up(o + sizeof(uint32_t) * 2 * (size_t)E * maxch, 256);
   w.offs = (uint32_t*)(b + o);
@@ -80,8 +90,8 @@ SelWs carve(void* ws, int E, int maxch) {
 
 size_t carve_bytes(int E, int maxch) {
   size_t o = 0;
-  o = align_up(o + sizeof(uint32_t) * (size_t)E * kBins, 256);
-  o = align_up(o + sizeof(SegState) * (size_t)E, 256);
+  o = align_up(o + sizeof(uint32_t) * (size_t)E * kPassBins, 256);
+  o = align_up(o + sizeof(SegState) * (size_t)E * (kPasses + 1), 256);
   o = align_up(o + sizeof(uint32_t) * 2 * (size_t)E * maxch, 256);
   o = align_up(o + sizeof(uint32_t) * 2 * (size_t)E * maxch, 256);
   return o;
@@ -106,7 +116,7 @@ __global__ __launch_bounds__(kSelThreads) void select_init_kernel(int E, const i
                                                                   SelWs w, int64_t positions,
                                                                   int32_t* __restrict__ pmap) {
   const int64_t gid = (int64_t)blockIdx.x * kSelThreads + threadIdx.x;
-  if (gid < (int64_t)E * kBins) w.hist[gid] = 0;
+  if (gid < (int64_t)E * kPassBins) w.hist[gid] = 0;
   if (pmap != nullptr && gid < positions) pmap[gid] = -1;  // positions with no retained pair
   if (gid < E) {
     const int64_t n = seg_off[gid + 1] - seg_off[gid];
@@ -117,29 +127,6 @@ __global__ __launch_bounds__(kSelThreads) void select_init_kernel(int E, const i
     s.need = (uint32_t)q;
     s.mode = q <= 0 ? kKeepNone : (q >= n ? kKeepAll : kKeepThreshold);
     w.state[gid] = s;
-  }
-}
-
-__global__ __launch_bounds__(kSelThreads) void select_hist_kernel(int shift, int nbits, const float* __restrict__ R,
-                                                                  const int64_t* __restrict__ seg_off, SelWs w) {
-  __shared__ uint32_t h[kBins];
-  const int e = blockIdx.y, tid = threadIdx.x;
-  const SegState st = w.state[e];
-  const int64_t lo = seg_off[e] + (int64_t)blockIdx.x * kChunk;
-  const int64_t hi = min(seg_off[e + 1], lo + kChunk);
-  if (st.mode != kKeepThreshold || lo >= hi) return;  // uniform across the block
-  const uint32_t nb = 1u << nbits;
-  uint32_t k[kSelPer];
-  const uint32_t ok = load_chunk(R, lo, hi, k);
-  for (uint32_t b = tid; b < nb; b += kSelThreads) h[b] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < kSelPer; ++r)
-    if ((ok >> r & 1) && (k[r] & st.mask) == st.prefix) atomicAdd(&h[(k[r] >> shift) & (nb - 1)], 1u);
-  __syncthreads();
-  for (uint32_t b = tid; b < nb; b += kSelThreads) {
-    const uint32_t c = h[b];
-    if (c) atomicAdd(&w.hist[(size_t)e * kBins + b], c);
   }
 }
 
@@ -166,15 +153,15 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t& tot, u
   return pre + inc;
 }
 
-// One block per segment: fix this pass's digit from the segment's histogram (thread t owns
-// the `per` bins just below nb - per*t, thread 0 the highest) and clear it for the next pass.
-__global__ __launch_bounds__(kSelThreads) void select_digit_kernel(int shift, int nbits, SelWs w) {
-  __shared__ uint32_t sh[kSelThreads / kWave];
-  const int e = blockIdx.x, tid = threadIdx.x;
-  SegState st = w.state[e];
-  if (st.mode != kKeepThreshold) return;  // uniform across the block
-  const uint32_t nb = 1u << nbits, per = nb / kSelThreads;  // 8 or 4
-  uint32_t* hg = w.hist + (size_t)e * kBins;
+// Fixes the digit of pass `pass` from the segment's finished histogram of that pass
+// (thread t scans the `per` bins just below nb - per*t, thread 0 the highest): the rank
+// still needed falls in exactly one bin. Every thread of the block calls it and gets the new
+// state; `sh` and `out` are the block's shared scratch.
+__device__ __forceinline__ SegState fix_digit(const uint32_t* __restrict__ hseg, int pass, SegState st, uint32_t* sh,
+                                              SegState* out) {
+  const int tid = threadIdx.x, shift = kShift[pass];
+  const uint32_t nb = 1u << kBits[pass], per = nb / kSelThreads;  // 8 or 4
+  const uint32_t* hg = hseg + pass_bin0(pass);
   const int top = (int)(nb - tid * per);
   uint32_t c[8];
   uint32_t sum = 0;
@@ -183,6 +170,7 @@ __global__ __launch_bounds__(kSelThreads) void select_digit_kernel(int shift, in
     c[j] = j < (int)per ? hg[top - 1 - j] : 0u;  // c[0] is the thread's highest bin
     sum += c[j];
   }
+  if (tid == 0) *out = st;
   uint32_t tot;
   const uint32_t inc = block_incl_scan(sum, tot, sh);
   const uint32_t exc = inc - sum;
@@ -193,24 +181,65 @@ __global__ __launch_bounds__(kSelThreads) void select_digit_kernel(int shift, in
       if (above + c[j] >= st.need) break;
       above += c[j];
     }
-    st.need -= above;
-    st.prefix |= (uint32_t)(top - 1 - j) << shift;
-    st.mask |= (nb - 1) << shift;
-    w.state[e] = st;
+    SegState ns = st;
+    ns.need -= above;
+    ns.prefix |= (uint32_t)(top - 1 - j) << shift;
+    ns.mask |= (nb - 1) << shift;
+    *out = ns;
   }
+  __syncthreads();
+  return *out;
+}
+
+// The state after passes < p, for a block of the launch that needs it: pass 0's comes from
+// the init launch; later ones are fixed here from pass p-1's histogram on top of the state
+// the previous launch recorded, and block 0 of the segment records them for the next launch.
+__device__ __forceinline__ SegState state_before(const SelWs& w, int E, int e, int p, bool needed, uint32_t* sh,
+                                                 SegState* out) {
+  SegState st = w.state[(size_t)(p > 0 ? p - 1 : 0) * E + e];
+  if (p > 0 && st.mode == kKeepThreshold && (needed || blockIdx.x == 0))  // uniform across the block
+    st = fix_digit(w.hist + (size_t)e * kPassBins, p - 1, st, sh, out);
+  if (p > 0 && blockIdx.x == 0 && threadIdx.x == 0) w.state[(size_t)p * E + e] = st;
+  return st;
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_hist_kernel(int pass, const float* __restrict__ R,
+                                                                  const int64_t* __restrict__ seg_off, SelWs w, int E) {
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t sh[kSelThreads / kWave];
+  __shared__ SegState out;
+  const int e = blockIdx.y, tid = threadIdx.x;
+  const int64_t lo = seg_off[e] + (int64_t)blockIdx.x * kChunk;
+  const int64_t hi = min(seg_off[e + 1], lo + kChunk);
+  const SegState st = state_before(w, E, e, pass, lo < hi, sh, &out);
+  if (st.mode != kKeepThreshold || lo >= hi) return;  // uniform across the block
+  const int shift = kShift[pass];
+  const uint32_t nb = 1u << kBits[pass];
+  uint32_t k[kSelPer];
+  const uint32_t ok = load_chunk(R, lo, hi, k);
+  for (uint32_t b = tid; b < nb; b += kSelThreads) h[b] = 0;
+  __syncthreads();
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (j < (int)per) hg[top - 1 - j] = 0;
+  for (int r = 0; r < kSelPer; ++r)
+    if ((ok >> r & 1) && (k[r] & st.mask) == st.prefix) atomicAdd(&h[(k[r] >> shift) & (nb - 1)], 1u);
+  __syncthreads();
+  uint32_t* hg = w.hist + (size_t)e * kPassBins + pass_bin0(pass);
+  for (uint32_t b = tid; b < nb; b += kSelThreads) {
+    const uint32_t c = h[b];
+    if (c) atomicAdd(&hg[b], c);
+  }
 }
 
 __global__ __launch_bounds__(kSelThreads) void select_count_kernel(const float* __restrict__ R,
                                                                    const int64_t* __restrict__ seg_off,
-                                                                   SelWs w, int maxch) {
+                                                                   SelWs w, int maxch, int E) {
   __shared__ uint32_t red[2][kSelThreads / kWave];
+  __shared__ uint32_t sh[kSelThreads / kWave];
+  __shared__ SegState out;
   const int e = blockIdx.y, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const SegState st = w.state[e];
   const int64_t lo = seg_off[e] + (int64_t)blockIdx.x * kChunk;
   const int64_t hi = min(seg_off[e + 1], lo + kChunk);
+  const SegState st = state_before(w, E, e, kPasses, lo < hi, sh, &out);  // the threshold key
   if (lo >= hi) return;  // uniform across the block
   uint32_t gt = 0, eq = 0;
   if (st.mode != kKeepNone) {
@@ -272,17 +301,32 @@ __global__ __launch_bounds__(kSelThreads) void select_offs_kernel(const int64_t*
 __global__ __launch_bounds__(kSelThreads) void select_write_kernel(const float* __restrict__ R,
                                                                    const int64_t* __restrict__ seg_off,
                                                                    const int64_t* __restrict__ cseg_off,
-                                                                   SelWs w, int maxch, int64_t K_tot,
-                                                                   int32_t* __restrict__ sel,
+                                                                   SelWs w, int maxch, int E, bool fused_offs,
+                                                                   int64_t K_tot, int32_t* __restrict__ sel,
                                                                    uint8_t* __restrict__ keep, PosOut po) {
   __shared__ uint32_t wtot[kSelPer][2][kSelThreads / kWave];
+  __shared__ uint32_t sh[2][kSelThreads / kWave];
   const int e = blockIdx.y, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const SegState st = w.state[e];
+  const SegState st = w.state[(size_t)kPasses * E + e];
   const int64_t lo = seg_off[e] + (int64_t)blockIdx.x * kChunk;
   const int64_t hi = min(seg_off[e + 1], lo + kChunk);
   if (lo >= hi) return;  // uniform across the block
-  const size_t slot = ((size_t)e * maxch + blockIdx.x) * 2;
-  const uint32_t base_gt = w.offs[slot], base_eq = w.offs[slot + 1];
+  uint32_t base_gt, base_eq;
+  if (fused_offs) {  // uniform: the counts of the segment's chunks before this one (fewer than 256)
+    const int c = tid;
+    const size_t cs = ((size_t)e * maxch + c) * 2;
+    const bool before = c < (int)blockIdx.x;
+    const uint32_t g = before ? w.counts[cs] : 0u, q = before ? w.counts[cs + 1] : 0u;
+    uint32_t tg, tq;
+    block_incl_scan(g, tg, sh[0]);
+    block_incl_scan(q, tq, sh[1]);
+    base_gt = tg;
+    base_eq = tq;
+  } else {
+    const size_t slot = ((size_t)e * maxch + blockIdx.x) * 2;
+    base_gt = w.offs[slot];
+    base_eq = w.offs[slot + 1];
+  }
   const uint32_t need = st.mode == kKeepThreshold ? st.need : 0u;
   const int64_t cbase = cseg_off[e], cend = min(cseg_off[e + 1], K_tot);
   const uint64_t lt_mask = (1ull << lane) - 1ull;
@@ -366,18 +410,17 @@ lrmoe_status launch_select(const lrmoe_problem* p, const float* R, const int64_t
   SelWs w = carve(ws, E, maxch);
   const int64_t positions = pmap != nullptr ? (int64_t)p->T * p->K : 0;
   const PosOut po{tok, slot, pmap, ctok, cslot, p->T, p->K};
-  const int64_t init_threads = std::max<int64_t>((int64_t)E * kBins, positions);
+  const int64_t init_threads = std::max<int64_t>((int64_t)E * kPassBins, positions);
   select_init_kernel<<<(unsigned)ceil_div(init_threads, kSelThreads), kSelThreads, 0, s>>>(E, seg_off_d, quota_d, w,
                                                                                            positions, pmap);
   const dim3 grid(maxch, E);
-  const int shifts[3] = {21, 10, 0}, bits[3] = {11, 11, 10};
-  for (int pass = 0; pass < 3; ++pass) {
-    select_hist_kernel<<<grid, kSelThreads, 0, s>>>(shifts[pass], bits[pass], R, seg_off_d, w);
-    select_digit_kernel<<<E, kSelThreads, 0, s>>>(shifts[pass], bits[pass], w);
-  }
-  select_count_kernel<<<grid, kSelThreads, 0, s>>>(R, seg_off_d, w, maxch);
-  select_offs_kernel<<<E, kSelThreads, 0, s>>>(seg_off_d, w, maxch);
-  select_write_kernel<<<grid, kSelThreads, 0, s>>>(R, seg_off_d, cseg_off_d, w, maxch, K_tot, sel, keep, po);
+  for (int pass = 0; pass < kPasses; ++pass)
+    select_hist_kernel<<<grid, kSelThreads, 0, s>>>(pass, R, seg_off_d, w, E);
+  select_count_kernel<<<grid, kSelThreads, 0, s>>>(R, seg_off_d, w, maxch, E);
+  const bool fused_offs = maxch <= kFusedOffsMaxChunks;
+  if (!fused_offs) select_offs_kernel<<<E, kSelThreads, 0, s>>>(seg_off_d, w, maxch);
+  select_write_kernel<<<grid, kSelThreads, 0, s>>>(R, seg_off_d, cseg_off_d, w, maxch, E, fused_offs, K_tot, sel,
+                                                   keep, po);
   return launch_status();
 }
 

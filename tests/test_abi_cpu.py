@@ -214,7 +214,7 @@ def test_product_path_does_not_touch_the_oracle():
 
 
 def test_select_noalloc_refuses_problems_beyond_its_scratch():
-    """lrmoe_select_noalloc's fixed 4 MiB scratch holds E x 8 KB of digit histograms: 1100
+    """lrmoe_select_noalloc's fixed 4 MiB scratch holds E x 20 KB of digit histograms: 1100
     experts need more, which is refused on the host before any launch; bad arguments are
     refused as for lrmoe_select."""
     lib = _lib.load()

@@ -453,6 +453,28 @@ def test_gathered_maps_out_of_range_read_zeros(name):
     assert not bool(got["dIn"][bad_t].float().abs().sum())
 
 
+def test_select_segment_beyond_256_chunks():
+    """A segment of more than 256 chunks of 4096 pairs (1.1M pairs, one expert, top-1): the
+    selection takes the write offsets from a launch of its own instead of inside the write
+    launch. Bit-exact against the oracle's selection on the same f32 scores, with the
+    packed rows' tokens and slots."""
+    n = 1_100_000
+    cfg = synth.custom("select_1m", T=n, K=1, E=1, D=64, F=32, counts=(n,), seed=25)
+    pr = synth.make_problem(cfg, rho="0.37")
+    s = Staged(pr)
+    R = lr.score(s.P, s.G, s.Phi, s.alpha, s.tok)
+    sel, keep, maps = lr.select(s.P, R, tok=s.tok, slot=s.slot)
+    torch.cuda.synchronize()
+    Rf = R.cpu().numpy()
+    sel_or, _, _ = oracle.select(Rf, pr.routing.seg_off, pr.quota)
+    assert np.array_equal(sel.cpu().numpy(), sel_or)
+    expect = np.zeros(n, dtype=np.uint8)
+    expect[sel_or] = 1
+    assert np.array_equal(keep.cpu().numpy(), expect)
+    assert np.array_equal(maps["ctok"].cpu().numpy(), pr.routing.tok[sel_or])
+    assert np.array_equal(maps["cslot"].cpu().numpy(), pr.routing.slot[sel_or])
+
+
 def test_all_equal_scores_break_ties_by_index():
     cfg = synth.custom("ties", T=64, K=4, E=3, D=128, F=64, counts=(100, 50, 60), seed=17)
     pr = synth.make_problem(cfg, rho="0.5")

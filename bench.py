@@ -94,7 +94,10 @@ def algorithmic_bytes(cfg, N, K_tot, packed=False, criterion="lrm", path="packed
         compact = (T * D + K_tot * F) * e + K_tot * (D + F) * e
     width = D if cfg.swiglu else F
     scatter = K_tot * width * e + T * width * 4
-    return {"score": score, "compact": compact, "scatter": scatter}
+    # selection: the scores, the pairs' tokens and slots read once; sel, keep, the packed rows'
+    # tokens and slots and the [T x K] map written once
+    select = N * (4 + 8) + N + K_tot * (4 + 8) + cfg.T * cfg.K * 4
+    return {"score": score, "compact": compact, "scatter": scatter, "select": select}
 
 
 def profile_key(cfg, rho):
@@ -361,6 +364,8 @@ def main():
             per = {n: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in timing])) for i, n in enumerate(names)}
             if overlap:
                 per["scatter"] = float(np.mean([ev[6].elapsed_time(ev[7]) for ev in timing]))
+            # whole step of the event pass, first to last event (includes the events' own cost)
+            per["step_median"] = float(np.median([ev[0].elapsed_time(ev[5]) for ev in timing]))
             return wall, per, bufs
 
         wall, per, phys_bufs = measure(lr.COMPACT_PHYSICAL)
@@ -372,7 +377,8 @@ def main():
             "score": ({"ms": per["score"], "GB/s": bytes_["score"] / per["score"] / 1e6,
                        "hbm_frac": bytes_["score"] / per["score"] / 1e6 / HBM_PEAK_GBS} if bytes_["score"] else
                       {"ms": per["score"], "note": "no score kernel: uniform draws made once on the host"}),
-            "select": {"ms": per["select"]},
+            "select": {"ms": per["select"], "GB/s": bytes_["select"] / per["select"] / 1e6,
+                       "note": "latency-bound (six launches); bytes for information"},
             "compact": {"ms": per["compact"], "GB/s": bytes_["compact"] / per["compact"] / 1e6,
                         "hbm_frac": bytes_["compact"] / per["compact"] / 1e6 / HBM_PEAK_GBS},
             "grouped_gemm_bwd": {"ms": per["grouped_gemm_bwd"], "TFLOP/s": gemm_tf, "mfma_frac": gemm_tf / peak},
@@ -391,7 +397,8 @@ def main():
     dt = cfg.dtype
     result = {
         "metric": METRIC, "value": value, "unit": "pairs/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": ms, "ms_per_step_median": per["step_median"],
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": dt, "data": "synthetic (seeded; pages' shapes, no dataset)",
         "config": {"workload": cfg.name, "T": cfg.T, "top_k": cfg.K, "local_experts": cfg.E, "D": cfg.D,
                    "F": cfg.F, "swiglu": cfg.swiglu, "rho": rho, "pairs": P.N, "retained_pairs": P.K_tot,
@@ -406,10 +413,19 @@ def main():
     if not args.no_masked:
         mwall, mper, _ = measure(lr.COMPACT_ZERO_MASKED)
         mfl = gemm_flops(cfg, P.N)
+        e_ = 2 if dt == "bf16" else 4
+        w_ = cfg.D if cfg.swiglu else cfg.F
+        # what each backward holds besides its inputs: the compact run's is the library's own
+        # estimate; the masked run keeps N rows of Dlt, dH and dIn and its own workspace
+        masked_hold = (5 * P.N + P.N * cfg.D * e_ + (P.N * 2 * cfg.F * e_ if cfg.swiglu else 0) + P.N * w_ * e_
+                       + 4 * cfg.E * cfg.F * cfg.D + (4 * cfg.E * cfg.D * 2 * cfg.F if cfg.swiglu else 0)
+                       + 4 * cfg.T * w_ + P.workspace_size(lr.COMPACT_ZERO_MASKED))
         result["masked_baseline"] = {
             "ms_per_step": mwall / args.steps * 1e3, "retained_pairs_per_s": P.K_tot * args.steps / mwall,
             "grouped_gemm_ms": mper["grouped_gemm_bwd"], "gemm_rows": P.N, "compact_rows": P.K_tot,
             "gemm_flops": mfl, "speedup_of_compaction": (mwall / args.steps * 1e3) / ms,
+            "compact_ms": mper["compact"], "compact_bytes": cfg.T * cfg.D * e_ + P.N * cfg.D * e_,
+            "backward_bytes": masked_hold, "backward_bytes_compact": lr.backward_bytes(P),
         }
     if args.forward and cfg.swiglu and dt == "bf16":
         fo, fev = {}, []

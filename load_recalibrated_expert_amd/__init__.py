@@ -3,7 +3,9 @@
 The five steps of the LRMoE paper's backward-time calibration (Algorithm 1,
 section 3.3) are calls into ``liblrmoe.so`` (hand-written HIP for gfx950):
 
-    score -> select -> compact -> grouped_gemm_bwd -> scatter
+    score -> select -> compact_weighted -> grouped_gemm_bwd_gathered -> scatter
+
+(or, packing the weighted gradient rows instead, compact -> grouped_gemm_bwd).
 
 The functions here have the C entry points' names and only marshal arguments:
 torch tensors supply device memory and the current HIP stream. ``backward`` chains

@@ -1,11 +1,14 @@
 // Step 3: physical compaction (LRMoE paper, section 3.1 "compact runtime" and section 3.4,
 // Figure 4). Retained gradient rows and their saved activations are gathered into
 // contiguous expert segments so the grouped GEMMs see only retained rows, with no
-// padding. Row c of every packed buffer belongs to the retained pair j = sel[c]:
-//   Dlt[c] = alpha_j * g_{tok_j} (the weighted cotangent, appendix 7.1 Eq. 5; alpha is
-//   applied here exactly once), and on request PhiC[c] = Phi[j], XC[c] = X[tok_j],
-//   HC[c] = H[j] (the grouped GEMM can instead read Phi, X and H in place through sel and
-//   ctok, so only the new gradient rows are written).
+// padding. Row c of every packed buffer belongs to the retained pair j = sel[c]. Two forms:
+//   - weighted saved rows only: PhiW[c] = alpha_j * Phi[j] (the grouped GEMMs then read the
+//     gradient rows g_{tok_j} by token and H[j] by pair; the routing weight sits on Phi,
+//     which the FC2 weight gradient's bilinearity allows, appendix 7.1 Eq. 6-8);
+//   - weighted gradient rows: Dlt[c] = alpha_j * g_{tok_j} (the weighted cotangent,
+//     appendix 7.1 Eq. 5; alpha is applied here exactly once), and on request
+//     PhiC[c] = Phi[j], XC[c] = X[tok_j], HC[c] = H[j] (the grouped GEMM can instead read
+//     Phi, X and H in place through sel and ctok).
 // The zero-masked baseline of section 3.4 keeps all N rows and zeroes the dropped pairs'
 // gradient rows instead.
 //

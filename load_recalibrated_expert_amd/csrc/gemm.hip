@@ -10,6 +10,13 @@
 //   FC1 dgrad  dIn  = dH W1^T       both operands contiguous along the reduction (j)
 //   FC2 wgrad  dW2  = PhiC^T Dlt    reduction over the packed rows: operands are row-major
 //   FC1 wgrad  dW1  = XC^T dH       in the output dims, transposed on the way into LDS
+// Without a packed Dlt = alpha g (the path that reads gradient rows by token), the FC2
+// products take the routing weight elsewhere, which the weight gradient's bilinearity
+// allows (appendix 7.1, Eq. 6-8): the data gradient reads the token rows g[ctok] and
+// scales each fp32 row of g W2^T by its pair's alpha before the SwiGLU backward, and the
+// weight gradient reads the weighted saved rows PhiW = alpha Phi as A and g[ctok] as B.
+// Any operand can be read in place through a row map instead of packed (a mapped row
+// outside its matrix reads as zeros).
 //
 // bf16 path: MFMA v_mfma_f32_32x32x16_bf16 with fp32 accumulation. A block of 512 threads
 // (eight 64-wide wavefronts, two per SIMD) owns a 256x256 output tile; each wavefront a

@@ -519,13 +519,14 @@ struct DgradArgs {
 // after the other, since the other half's accumulators are still live, and the second half
 // one batch of 8; with four wavefronts (accumulators in accumulation registers) batches of 4
 // run with the next batch's loads in flight. Loads always read a valid address (row 0 for a
-// row outside the tile or outside HC) and invalid rows are zeroed at use, so the compiler
-// neither branches around the loads nor waits between them.
+// row outside the tile or outside HC) and such a row gets a zero weight, which zeroes its dH
+// (the saved rows are finite), so the compiler neither branches around the loads nor waits
+// between them.
 template <int B>
 struct HcBatch {
   uint4 gw[B], uw[B];
-  float a[B];  // the rows' routing weights (1 when the product is not scaled)
-  uint32_t okm;
+  float a[B];  // the rows' routing weights (1 when the product is not scaled; 0 for a row
+               // outside the tile or HC, whose [gate | up] words are then row 0's)
 };
 
 template <class C, int B, bool AHEAD>
@@ -553,17 +554,16 @@ __device__ __forceinline__ void swiglu_half(StageBufs<C>& sm, const acc_t<C>& ac
     for (int i = 0; i < kIt; ++i) hrow[i] = row0 + half * (BM / C::WM) + tr0 + kRowStep * i;
   }
   auto issue = [&](HcBatch<B>& bt, int i0) {
-    bt.okm = 0;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
       const int i = i0 + b;
       const int tr = half * (BM / C::WM) + tr0 + kRowStep * i;
       const bool ok = tr < rows_valid && col_ok && hrow[i] >= 0 && hrow[i] < g.hc_nrows;
-      bt.okm |= ok ? 1u << b : 0u;
       const int64_t hb = ok ? hrow[i] * ld + n0 + tc : 0;
       bt.gw[b] = *(const uint4*)(hc + hb);
       bt.uw[b] = *(const uint4*)(hc + hb + F);
-      bt.a[b] = g.alpha != nullptr ? g.alpha[ok ? hrow[i] : 0] : 1.0f;
+      const float a = g.alpha != nullptr ? g.alpha[ok ? hrow[i] : 0] : 1.0f;
+      bt.a[b] = ok ? a : 0.0f;  // a row outside the tile or HC: zero weight, so zero dH
     }
   };
   auto finish = [&](HcBatch<B>& bt, int i0) {
@@ -574,9 +574,8 @@ __device__ __forceinline__ void swiglu_half(StageBufs<C>& sm, const acc_t<C>& ac
       const float4 hi = st[r * P + ((2 * c8 + 1) ^ (r & 15))];
       const float av = bt.a[b];
       const float dphi[8] = {av * lo.x, av * lo.y, av * lo.z, av * lo.w, av * hi.x, av * hi.y, av * hi.z, av * hi.w};
-      const bool ok = (bt.okm >> b) & 1u;  // rows outside the tile or HC read as zeros
-      const uint32_t gg[4] = {ok ? bt.gw[b].x : 0u, ok ? bt.gw[b].y : 0u, ok ? bt.gw[b].z : 0u, ok ? bt.gw[b].w : 0u};
-      const uint32_t uu[4] = {ok ? bt.uw[b].x : 0u, ok ? bt.uw[b].y : 0u, ok ? bt.uw[b].z : 0u, ok ? bt.uw[b].w : 0u};
+      const uint32_t gg[4] = {bt.gw[b].x, bt.gw[b].y, bt.gw[b].z, bt.gw[b].w};
+      const uint32_t uu[4] = {bt.uw[b].x, bt.uw[b].y, bt.uw[b].z, bt.uw[b].w};
       float dg[8], du[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {

@@ -17,7 +17,6 @@ __device__ __forceinline__ uint4 ld_stream(const void* p) {
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 

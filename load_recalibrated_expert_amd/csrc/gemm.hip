@@ -101,10 +101,14 @@ __device__ __forceinline__ void dma16(rsrc_t r, const uint4* lds_wave_base, uint
 // ---------------------------------------------------------------- LDS layouts
 //
 // K-contiguous operand (data-gradient GEMMs): a stage holds R rows (256 or 128) x 32 K values
-// (64 bytes per row, four 16-byte chunks). Rows r and r + R/2 share one 128-byte LDS line:
-// line L = r % (R/2) holds eight 16-byte slots, and chunk c of row r sits in slot
-// (4 (r / (R/2)) + c) ^ (L % 8). MFMA fragment reads (one 16-byte chunk of each of 32
-// consecutive rows) then run at the full LDS rate; with a 64-byte line pitch they ran at half.
+// (64 bytes per row, four 16-byte chunks). Rows 2L and 2L + 1 share the 128-byte LDS line L,
+// which holds eight 16-byte slots: chunk c of row 2L + h sits in slot (4 h + c) ^ ((L / 2) % 4).
+// The LDS has 64 four-byte banks and serves a 16-byte read 16 lanes at a time. An MFMA
+// fragment read gives lane i one chunk of row row0 + i (row0 a multiple of 32), so each group
+// of 16 lanes reads 8 lines, two rows per line: the line's parity picks one half of the banks
+// and h with (L / 2) % 4 picks 8 distinct slots per half, so the 16 lanes hit all 64 banks.
+// (Pairing rows r and r + R/2 with the swizzle L % 8 covered 32 banks per 8 lanes, a two-way
+// conflict on every read: half the LDS cycles of the data gradients went to conflicts.)
 //
 // Row-major-in-K operand (weight-gradient GEMMs): a stage holds 32 K rows x 256 columns,
 // 512 bytes per row as eight 64-byte segments; segment s of row k sits in slot s ^ (k & 3),
@@ -116,21 +120,22 @@ struct StageBufs {
   uint4 b[C::STAGES][C::B_U4];
 };
 
-// uint4 index of chunk c of row r in a K-contiguous stage of 2 HALF rows
-template <int HALF>
+// uint4 index of chunk c of row r in a K-contiguous stage
 __device__ __forceinline__ int nt_slot(int r, int c) {
-  return (r & (HALF - 1)) * 8 + (((int)(((unsigned)r / HALF) << 2) | c) ^ (r & 7));
+  const int line = r >> 1;
+  return line * 8 + ((((r & 1) << 2) | c) ^ ((line >> 1) & 3));
 }
 
 // Direct-to-LDS loader of a K-contiguous operand of ROWS rows per stage, for blocks of
 // NWAVE wavefronts. A 1 KB direct load fills 8 LDS lines (16 tile rows); wave w issues
 // loads j = 0..NL-1 covering lines 8 (w*NL + j) + l/8, and lane l fetches the chunk that
-// belongs in slot l % 8 of its line: slot s holds chunk (s ^ line%8) % 4 of row
-// (ROWS/2) ((s ^ line%8) / 4) + line.
+// belongs in slot l % 8 of its line: with x = (l % 8) ^ ((line / 2) % 4), that is chunk x % 4
+// of row 2 line + x / 4. Since 8 divides the first line of a load, (line / 2) % 4 = (l / 16) % 4
+// and the lane's chunk is the same in every load.
 template <int NWAVE_, int ROWS>
 struct DmaK {
-  static constexpr int HALF = ROWS / 2, NL = HALF / 8 / NWAVE_;  // direct loads per wavefront
-  static_assert(NL * 8 * NWAVE_ == HALF, "whole loads per wavefront");
+  static constexpr int NL = ROWS / 16 / NWAVE_;  // direct loads per wavefront
+  static_assert(NL * 16 * NWAVE_ == ROWS, "whole loads per wavefront");
   rsrc_t r;
   uint32_t off[NL];
   int col;    // first K element of this lane's chunk within the stage
@@ -138,12 +143,12 @@ struct DmaK {
   __device__ __forceinline__ void init(const uint16_t* p, int64_t ld, int rows_valid) {
     r = make_rsrc(p);
     const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int logical = (l & 7) ^ ((l >> 3) & 7);  // line % 8 == (l / 8) % 8
+    const int logical = (l & 7) ^ ((l >> 4) & 3);
     col = (logical & 3) * 8;
     wbase = w * NL * 64;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      const int row = (logical >> 2) * HALF + (w * NL + j) * 8 + (l >> 3);
+      const int row = 2 * ((w * NL + j) * 8 + (l >> 3)) + (logical >> 2);
       off[j] = row < rows_valid ? (uint32_t)((row * ld + col) * 2) : kOOB;
     }
   }
@@ -154,12 +159,12 @@ struct DmaK {
                                             int64_t nrows) {
     r = make_rsrc(p);
     const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int logical = (l & 7) ^ ((l >> 3) & 7);
+    const int logical = (l & 7) ^ ((l >> 4) & 3);
     col = (logical & 3) * 8;
     wbase = w * NL * 64;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      const int row = (logical >> 2) * HALF + (w * NL + j) * 8 + (l >> 3);
+      const int row = 2 * ((w * NL + j) * 8 + (l >> 3)) + (logical >> 2);
       const int64_t src = row < rows_valid ? (int64_t)rows[row] : -1;
       off[j] = (src >= 0 && src < nrows) ? (uint32_t)((src * ld + col) * 2) : kOOB;
     }
@@ -323,14 +328,13 @@ __device__ __forceinline__ bf16x8_t frag_tr(const uint4* stage, int col0, int k0
 // The MFMA takes the n fragment first, so each lane's accumulator holds 4 consecutive
 // output columns of one output row: acc[nb][mb][v] is output row
 // wm*(32 MB) + mb*32 + lane%32, column wn*(32 NB) + nb*32 + 8*(v/4) + 4*(lane/32) + v%4.
-// One MFMA fragment: rows row0..row0+31 of an operand stage, K16 step kk (a K-contiguous
-// stage holds 2 HALF rows).
-template <bool TN, int HALF>
+// One MFMA fragment: rows row0..row0+31 of an operand stage, K16 step kk.
+template <bool TN>
 __device__ __forceinline__ bf16x8_t load_frag(const uint4* __restrict__ stage, int row0, int kk, int lane) {
   if constexpr (TN) {
     return frag_tr(stage, row0, kk * 16, lane);
   } else {
-    return __builtin_bit_cast(bf16x8_t, stage[nt_slot<HALF>(row0 + (lane & 31), kk * 2 + (lane >> 5))]);
+    return __builtin_bit_cast(bf16x8_t, stage[nt_slot(row0 + (lane & 31), kk * 2 + (lane >> 5))]);
   }
 }
 
@@ -366,7 +370,6 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs<C>& sm, LA& la, LB& lb, 
                                               uint32_t kstep_b, acc_t<C>& acc, int wm, int wn, int lane) {
   constexpr int MB = C::MB, NB = C::NB;
   constexpr int NM = NB * MB, STAGES = C::STAGES, NLA = LA::NL, NLB = LB::NL;
-  constexpr int HA = BM / 2, HB = C::BN / 2;  // K-contiguous stage halves
   // first MFMA slot of the direct loads: behind the fragment reads when the step has room
   // for both, else from the first slot on, beside them
   constexpr int kDma0 = NM >= MB + NB + NLA + NLB ? MB + NB : 0;
@@ -395,9 +398,9 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs<C>& sm, LA& la, LB& lb, 
   __syncthreads();
   bf16x8_t fa[2][MB], fb[2][NB];
 #pragma unroll
-  for (int i = 0; i < MB; ++i) fa[0][i] = load_frag<TNA, HA>(sm.a[0], wm * 32 * MB + i * 32, 0, lane);
+  for (int i = 0; i < MB; ++i) fa[0][i] = load_frag<TNA>(sm.a[0], wm * 32 * MB + i * 32, 0, lane);
 #pragma unroll
-  for (int i = 0; i < NB; ++i) fb[0][i] = load_frag<TNB, HB>(sm.b[0], wn * 32 * NB + i * 32, 0, lane);
+  for (int i = 0; i < NB; ++i) fb[0][i] = load_frag<TNB>(sm.b[0], wn * 32 * NB + i * 32, 0, lane);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt % STAGES, nxt = (kt + 1) % STAGES, ldst = (kt + STAGES - 1) % STAGES;
     const int k_ld = (kt + STAGES - 1) * BK;
@@ -413,16 +416,16 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs<C>& sm, LA& la, LB& lb, 
       if (i >= kDma0 && i < kDma0 + NLA) la.issue_one(i - kDma0, sm.a[ldst], k_ld, kend, kstep_a);
       else if (i >= kDma0 + NLA && i < kDma0 + NLA + NLB)
         lb.issue_one(i - kDma0 - NLA, sm.b[ldst], k_ld, kend, kstep_b);
-      if (i < MB) fa[1][i] = load_frag<TNA, HA>(sm.a[cur], wm * 32 * MB + i * 32, 1, lane);
-      else if (i < MB + NB) fb[1][i - MB] = load_frag<TNB, HB>(sm.b[cur], wn * 32 * NB + (i - MB) * 32, 1, lane);
+      if (i < MB) fa[1][i] = load_frag<TNA>(sm.a[cur], wm * 32 * MB + i * 32, 1, lane);
+      else if (i < MB + NB) fb[1][i - MB] = load_frag<TNB>(sm.b[cur], wn * 32 * NB + (i - MB) * 32, 1, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int i = 0; i < NM; ++i) {
       mfma(acc[i / MB][i % MB], fb[1][i / MB], fa[1][i % MB]);
       __builtin_amdgcn_sched_barrier(0);
-      if (i < MB) fa[0][i] = load_frag<TNA, HA>(sm.a[nxt], wm * 32 * MB + i * 32, 0, lane);
-      else if (i < MB + NB) fb[0][i - MB] = load_frag<TNB, HB>(sm.b[nxt], wn * 32 * NB + (i - MB) * 32, 0, lane);
+      if (i < MB) fa[0][i] = load_frag<TNA>(sm.a[nxt], wm * 32 * MB + i * 32, 0, lane);
+      else if (i < MB + NB) fb[0][i - MB] = load_frag<TNB>(sm.b[nxt], wn * 32 * NB + (i - MB) * 32, 0, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
     la.advance(kt + STAGES);

@@ -22,7 +22,9 @@
 // (eight 64-wide wavefronts, two per SIMD) owns a 256x256 output tile; each wavefront a
 // 128x64 sub-tile held as 2x4 MFMA accumulators. K advances 32 per stage through four LDS
 // stages (4 x 32 KB) filled by direct global-to-LDS loads issued three stages ahead, one
-// barrier per stage. Finished tiles leave through LDS so every output row is written by
+// barrier per stage; the FC1 data gradient instead runs two 64-K stages in the same 128 KB,
+// so each request of its K-contiguous operands is a whole 128-byte line. Finished tiles
+// leave through LDS so every output row is written by
 // consecutive threads with 16-byte accesses. Weight-gradient tiles split the packed rows
 // of large experts into K chunks; chunk partials go to the workspace and a second kernel
 // sums them in chunk order, so results do not depend on scheduling. Tiles are handed to
@@ -434,6 +436,140 @@ __device__ __forceinline__ void gemm_mainloop(StageBufs<C>& sm, LA& la, LB& lb, 
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the loop
 }
 
+// ---------------------------------------------------------------- data-gradient K loop, 64-K stages
+//
+// Both data-gradient operands are contiguous along K. In a 32-K stage a row contributes 64
+// bytes, so every request of the direct loads is half a 128-byte line. In a 64-K stage row
+// r fills LDS line r and eight consecutive lanes fetch it, so each request is a whole line.
+// Two such stages of both 256-row operands take the same 128 KB as four 32-K stages. Chunk c
+// (K values 8c..8c+7) of row r sits in 16-byte slot c ^ ((r / 2) % 8) of line r: the 8 even
+// rows among 16 consecutive ones then take 8 distinct slots in one half of the 64 banks and
+// the 8 odd rows in the other, so a 16-lane fragment read is free of bank conflicts.
+constexpr int BK64 = 64;
+
+template <int NWAVE_, int ROWS>
+struct DmaK64 {
+  static constexpr int NL = ROWS / 8 / NWAVE_;  // 1 KB direct loads (8 rows) per wavefront per stage
+  static_assert(NL * 8 * NWAVE_ == ROWS, "whole loads per wavefront");
+  rsrc_t r;
+  uint32_t off[NL];
+  int col[NL];  // first K element of this lane's chunk in load j (it depends on the load's row)
+  int wbase;
+  // the row and chunk of lane l in load j: row 8 (w NL + j) + l/8, chunk (l % 8) ^ ((row / 2) % 8)
+  __device__ __forceinline__ static int lane_row(int w, int j, int l) { return 8 * (w * NL + j) + (l >> 3); }
+  __device__ __forceinline__ static int lane_chunk(int row, int l) { return (l & 7) ^ ((row >> 1) & 7); }
+  __device__ __forceinline__ void init(const uint16_t* p, int64_t ld, int rows_valid) {
+    r = make_rsrc(p);
+    const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    wbase = w * NL * 64;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int row = lane_row(w, j, l);
+      col[j] = lane_chunk(row, l) * 8;
+      off[j] = row < rows_valid ? (uint32_t)((row * ld + col[j]) * 2) : kOOB;
+    }
+  }
+  // tile row r is row rows[r] of the matrix at p, as DmaK::init_rows
+  __device__ __forceinline__ void init_rows(const uint16_t* p, int64_t ld, int rows_valid, const int32_t* rows,
+                                            int64_t nrows) {
+    r = make_rsrc(p);
+    const int l = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    wbase = w * NL * 64;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      const int row = lane_row(w, j, l);
+      col[j] = lane_chunk(row, l) * 8;
+      const int64_t src = row < rows_valid ? (int64_t)rows[row] : -1;
+      off[j] = (src >= 0 && src < nrows) ? (uint32_t)((src * ld + col[j]) * 2) : kOOB;
+    }
+  }
+  __device__ __forceinline__ void issue_one(int j, const uint4* stage, int k0, int kend) const {
+    dma16(r, stage + wbase + j * 64, (off[j] != kOOB && k0 + col[j] < kend) ? off[j] + (uint32_t)k0 * 2u : kOOB);
+  }
+};
+
+// two 64-K stages of both 256-row operands, in the same bytes as StageBufs<CfgD>
+struct StageBufs64 {
+  uint4 a[2][BM * BK64 * 2 / 16];
+  uint4 b[2][BM * BK64 * 2 / 16];
+};
+
+__device__ __forceinline__ bf16x8_t load_frag64(const uint4* __restrict__ stage, int row0, int kk, int lane) {
+  const int r = row0 + (lane & 31), c = kk * 2 + (lane >> 5);
+  return __builtin_bit_cast(bf16x8_t, stage[r * 8 + (c ^ ((r >> 1) & 7))]);
+}
+
+// Two stages of 64 K values per operand, 4 K16 steps of NB x MB MFMAs each. Iteration kt:
+//   steps 0-2: MFMAs of stage kt, each step reading the next step's fragments behind them;
+//   wait for this wavefront's loads of stage kt+1 and its fragment reads, one barrier: stage
+//     kt+1 is visible, and every wavefront holds its fragments of stage kt in registers;
+//   step 3: MFMAs of stage kt's last step; the direct loads of stage kt+2 into stage kt's
+//     buffer, and the fragments of stage kt+1's first step (in the last iterations the loads
+//     are past kend and write zeros, and the fragments go unused).
+// A stage's loads thus have four K16 steps to land, as in the 32-K loop, with one barrier per
+// 64 K instead of two, and the wait is for every load in flight (vmcnt 0), not a count.
+template <class C, class LA, class LB>
+__device__ __forceinline__ void gemm_mainloop_k64(StageBufs64& sm, LA& la, LB& lb, int kend, acc_t<C>& acc,
+                                                  int wm, int wn, int lane) {
+  constexpr int MB = C::MB, NB = C::NB, NM = NB * MB, NLA = LA::NL, NLB = LB::NL;
+  static_assert(C::BN == BM && sizeof(StageBufs64) <= sizeof(StageBufs<C>), "two stages of both operands fit");
+  static_assert(NLA + NLB <= 2 * NM, "at most two direct loads per MFMA slot of step 3");
+  const int nk = (kend + BK64 - 1) / BK64;
+  if (nk <= 0) return;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    if (s < nk) {
+#pragma unroll
+      for (int j = 0; j < (NLA > NLB ? NLA : NLB); ++j) {
+        if (j < NLA) la.issue_one(j, sm.a[s], s * BK64, kend);
+        if (j < NLB) lb.issue_one(j, sm.b[s], s * BK64, kend);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  bf16x8_t fa[2][MB], fb[2][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) fa[0][i] = load_frag64(sm.a[0], wm * 32 * MB + i * 32, 0, lane);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) fb[0][i] = load_frag64(sm.b[0], wn * 32 * NB + i * 32, 0, lane);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1, nxt = cur ^ 1;
+    const int k_ld = (kt + 2) * BK64;  // at or past kend in the last two iterations: zeros
+#pragma unroll
+    for (int st = 0; st < 3; ++st) {
+      const int h = st & 1;  // fragments in use: fa[h], fb[h]; the next step's go to fa[h ^ 1]
+#pragma unroll
+      for (int i = 0; i < NM; ++i) {
+        mfma(acc[i / MB][i % MB], fb[h][i / MB], fa[h][i % MB]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < MB) fa[h ^ 1][i] = load_frag64(sm.a[cur], wm * 32 * MB + i * 32, st + 1, lane);
+        else if (i < MB + NB) fb[h ^ 1][i - MB] = load_frag64(sm.b[cur], wn * 32 * NB + (i - MB) * 32, st + 1, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // vmcnt(0) lgkmcnt(0): this wavefront's loads of stage kt+1 landed and its reads of stage
+    // kt's last fragments returned, so after the barrier stage kt's buffer may be refilled
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+      mfma(acc[i / MB][i % MB], fb[1][i / MB], fa[1][i % MB]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int j = 2 * i + u;
+        if (j < NLA) la.issue_one(j, sm.a[cur], k_ld, kend);
+        else if (j < NLA + NLB) lb.issue_one(j - NLA, sm.b[cur], k_ld, kend);
+      }
+      if (i < MB) fa[0][i] = load_frag64(sm.a[nxt], wm * 32 * MB + i * 32, 0, lane);
+      else if (i < MB + NB) fb[0][i - MB] = load_frag64(sm.b[nxt], wn * 32 * NB + (i - MB) * 32, 0, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load into LDS outlives the loop
+}
+
 // ---------------------------------------------------------------- epilogue through LDS
 
 // Writes the accumulators out through LDS so that every output row is handled by
@@ -655,12 +791,25 @@ __global__ LRMOE_GEMM_ATTR(CfgD) void dgrad_kernel(DgradArgs g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
   acc_t<C> acc;
   zero_acc<C>(acc);
-  DmaK<C::NWAVE, BM> la;
-  DmaK<C::NWAVE, C::BN> lb;
-  if (g.a_rows != nullptr) la.init_rows(g.A, g.lda, rows_valid, g.a_rows + row0, g.a_nrows);
-  else la.init(g.A + row0 * g.lda, g.lda, rows_valid);
-  lb.init(g.W + (int64_t)e * g.w_estride + (int64_t)n0 * g.ldw, g.ldw, n_valid);
-  gemm_mainloop<C, false, false>(lds, la, lb, g.K, 0, 0, acc, wm, wn, lane);
+  auto init = [&](auto& la, auto& lb) {
+    if (g.a_rows != nullptr) la.init_rows(g.A, g.lda, rows_valid, g.a_rows + row0, g.a_nrows);
+    else la.init(g.A + row0 * g.lda, g.lda, rows_valid);
+    lb.init(g.W + (int64_t)e * g.w_estride + (int64_t)n0 * g.ldw, g.ldw, n_valid);
+  };
+  // The FC1 data gradient runs the 64-K loop (whole-line requests; 3-4% faster than the 32-K
+  // loop on the Qwen3 and GLM shares), the FC2 data gradient the 32-K loop (1% faster there
+  // with the SwiGLU epilogue behind it).
+  if constexpr (EPI == EPI_STORE) {
+    DmaK64<C::NWAVE, BM> la;
+    DmaK64<C::NWAVE, C::BN> lb;
+    init(la, lb);
+    gemm_mainloop_k64<C>(reinterpret_cast<StageBufs64&>(lds), la, lb, g.K, acc, wm, wn, lane);
+  } else {
+    DmaK<C::NWAVE, BM> la;
+    DmaK<C::NWAVE, C::BN> lb;
+    init(la, lb);
+    gemm_mainloop<C, false, false>(lds, la, lb, g.K, 0, 0, acc, wm, wn, lane);
+  }
 
   if (EPI == EPI_SWIGLU) {
     epilogue_swiglu<C>(lds, acc, wm, wn, lane, g, row0, rows_valid, n0, n_valid);

@@ -650,8 +650,10 @@ struct DgradArgs {
 
 // SwiGLU backward epilogue of the FC2 data gradient: the tile's dPhi (the accumulators) gives
 // dH = [dPhi * up * silu'(gate), dPhi * silu(gate)] with gate, up read from the saved rows.
-// Staged through LDS in two halves like epilogue_staged. A thread handles kIt rows per half:
-// it loads their row indices together, then their [gate | up] chunks in batches, and stores
+// Staged through LDS in two halves like epilogue_staged. The tile's HC rows (the row map,
+// fetched before the K loop) and their routing weights reach every thread through LDS
+// (ep_rows, ep_alpha), so the first [gate | up] loads of a half depend on no global load.
+// A thread handles kIt rows per half: it loads their [gate | up] chunks in batches and stores
 // a batch's dH only after computing all of it, so a half costs a few memory round trips
 // instead of three per row. The first batch is loaded before the half is staged. With eight
 // wavefronts (accumulators in ordinary registers) the first half runs two batches of 4 one
@@ -664,14 +666,12 @@ struct DgradArgs {
 template <int B>
 struct HcBatch {
   uint4 gw[B], uw[B];
-  float a[B];  // the rows' routing weights (1 when the product is not scaled; 0 for a row
-               // outside the tile or HC, whose [gate | up] words are then row 0's)
 };
 
-template <class C, int B, bool AHEAD>
+template <class C, int B, bool AHEAD, class Pre>
 __device__ __forceinline__ void swiglu_half(StageBufs<C>& sm, const acc_t<C>& acc, int wm, int wn, int lane,
-                                            const DgradArgs& g, int64_t row0, int rows_valid, int n0, int n_valid,
-                                            int half) {
+                                            const DgradArgs& g, const int32_t* ep_rows, const float* ep_alpha,
+                                            int64_t row0, int rows_valid, int n0, int n_valid, int half, Pre pre) {
   constexpr int BN = C::BN, NTHR = C::NTHR, P = BN / 4;
   constexpr int kIt = (BM / C::WM) * (BN / 8) / NTHR;  // rows per thread per half
   constexpr int kRowStep = NTHR / (BN / 8);
@@ -684,25 +684,13 @@ __device__ __forceinline__ void swiglu_half(StageBufs<C>& sm, const acc_t<C>& ac
   const uint16_t* __restrict__ hc = g.HC;
   uint16_t* __restrict__ dh = g.out;
   float4* st = reinterpret_cast<float4*>(&sm);
-  int64_t hrow[kIt];
-  if (g.hc_rows != nullptr) {
-#pragma unroll
-    for (int i = 0; i < kIt; ++i) hrow[i] = g.hc_rows[row0 + min(half * (BM / C::WM) + tr0 + kRowStep * i, rows_valid - 1)];
-  } else {
-#pragma unroll
-    for (int i = 0; i < kIt; ++i) hrow[i] = row0 + half * (BM / C::WM) + tr0 + kRowStep * i;
-  }
   auto issue = [&](HcBatch<B>& bt, int i0) {
 #pragma unroll
     for (int b = 0; b < B; ++b) {
-      const int i = i0 + b;
-      const int tr = half * (BM / C::WM) + tr0 + kRowStep * i;
-      const bool ok = tr < rows_valid && col_ok && hrow[i] >= 0 && hrow[i] < g.hc_nrows;
-      const int64_t hb = ok ? hrow[i] * ld + n0 + tc : 0;
+      const int32_t hr = ep_rows[half * (BM / C::WM) + tr0 + kRowStep * (i0 + b)];
+      const int64_t hb = hr >= 0 && col_ok ? (int64_t)hr * ld + n0 + tc : 0;
       bt.gw[b] = *(const uint4*)(hc + hb);
       bt.uw[b] = *(const uint4*)(hc + hb + F);
-      const float a = g.alpha != nullptr ? g.alpha[ok ? hrow[i] : 0] : 1.0f;
-      bt.a[b] = ok ? a : 0.0f;  // a row outside the tile or HC: zero weight, so zero dH
     }
   };
   auto finish = [&](HcBatch<B>& bt, int i0) {
@@ -711,7 +699,9 @@ __device__ __forceinline__ void swiglu_half(StageBufs<C>& sm, const acc_t<C>& ac
       const int r = tr0 + kRowStep * (i0 + b), c8 = tc / 8;
       const float4 lo = st[r * P + ((2 * c8) ^ (r & 15))];
       const float4 hi = st[r * P + ((2 * c8 + 1) ^ (r & 15))];
-      const float av = bt.a[b];
+      // the row's routing weight; 0 for a row outside the tile or HC, whose [gate | up]
+      // words are row 0's, so its dH is zero
+      const float av = col_ok ? ep_alpha[half * (BM / C::WM) + r] : 0.0f;
       const float dphi[8] = {av * lo.x, av * lo.y, av * lo.z, av * lo.w, av * hi.x, av * hi.y, av * hi.z, av * hi.w};
       const uint32_t gg[4] = {bt.gw[b].x, bt.gw[b].y, bt.gw[b].z, bt.gw[b].w};
       const uint32_t uu[4] = {bt.uw[b].x, bt.uw[b].y, bt.uw[b].z, bt.uw[b].w};
@@ -741,6 +731,7 @@ __device__ __forceinline__ void swiglu_half(StageBufs<C>& sm, const acc_t<C>& ac
   };
   HcBatch<B> bt[kNb > 1 ? 2 : 1];
   issue(bt[0], 0);
+  pre();
   __syncthreads();
   if (wm == half) stage_half<C>(st, acc, wn, lane);
   __syncthreads();
@@ -752,25 +743,50 @@ __device__ __forceinline__ void swiglu_half(StageBufs<C>& sm, const acc_t<C>& ac
   }
 }
 
+// my_row: for threads below BM, the HC row of tile row threadIdx.x (-1: none), loaded before
+// the K loop. Its routing weight is loaded here, beside the first [gate | up] loads, and
+// written to LDS before the first half is staged.
 template <class C>
 __device__ __forceinline__ void epilogue_swiglu(StageBufs<C>& sm, const acc_t<C>& acc, int wm, int wn, int lane,
-                                                const DgradArgs& g, int64_t row0, int rows_valid, int n0,
+                                                const DgradArgs& g, int32_t* ep_rows, float* ep_alpha,
+                                                int32_t my_row, int64_t row0, int rows_valid, int n0,
                                                 int n_valid) {
   static_assert(C::WM == 2, "two halves");
+  const int t = threadIdx.x;
+  if (t < BM) ep_rows[t] = my_row;
+  float my_alpha = 0.0f;
+  if (t < BM && my_row >= 0) my_alpha = g.alpha != nullptr ? g.alpha[my_row] : 1.0f;
+  __syncthreads();
+  auto pre0 = [&] {
+    if (t < BM) ep_alpha[t] = my_alpha;
+  };
+  auto pre1 = [] {};
   if constexpr (C::NWAVE == 8) {
-    swiglu_half<C, 4, false>(sm, acc, wm, wn, lane, g, row0, rows_valid, n0, n_valid, 0);
-    swiglu_half<C, 8, false>(sm, acc, wm, wn, lane, g, row0, rows_valid, n0, n_valid, 1);
+    swiglu_half<C, 4, false>(sm, acc, wm, wn, lane, g, ep_rows, ep_alpha, row0, rows_valid, n0, n_valid, 0, pre0);
+    swiglu_half<C, 8, false>(sm, acc, wm, wn, lane, g, ep_rows, ep_alpha, row0, rows_valid, n0, n_valid, 1, pre1);
   } else {
-    swiglu_half<C, 4, true>(sm, acc, wm, wn, lane, g, row0, rows_valid, n0, n_valid, 0);
-    swiglu_half<C, 4, true>(sm, acc, wm, wn, lane, g, row0, rows_valid, n0, n_valid, 1);
+    swiglu_half<C, 4, true>(sm, acc, wm, wn, lane, g, ep_rows, ep_alpha, row0, rows_valid, n0, n_valid, 0, pre0);
+    swiglu_half<C, 4, true>(sm, acc, wm, wn, lane, g, ep_rows, ep_alpha, row0, rows_valid, n0, n_valid, 1, pre1);
   }
 }
+
+template <class C, int R>
+struct DgradShared {
+  StageBufs<C> st;
+  int32_t ep_rows[R];  // SwiGLU epilogue: HC row of each tile row (-1: none)
+  float ep_alpha[R];   // and its routing weight
+};
 
 // One output tile per block.
 template <int EPI>
 __global__ LRMOE_GEMM_ATTR(CfgD) void dgrad_kernel(DgradArgs g) {
   using C = CfgD;
-  __shared__ StageBufs<C> lds;
+  // one LDS object: the stage buffers, then the SwiGLU epilogue's row map (with a second
+  // __shared__ variable the compiler attaches alias scopes to LDS accesses and then waits
+  // for every direct load before each fragment read)
+  __shared__ DgradShared<C, EPI == EPI_SWIGLU ? BM : 1> lds_all;
+  StageBufs<C>& lds = lds_all.st;
+  auto& lds_ep = lds_all;
   const int b = xcd_remap(blockIdx.x, gridDim.x);
   int e = 0, local = b;
   int64_t r0 = 0, m = 0;
@@ -789,6 +805,15 @@ __global__ LRMOE_GEMM_ATTR(CfgD) void dgrad_kernel(DgradArgs g) {
   const int n_valid = min(C::BN, g.N - n0);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave / C::WN, wn = wave % C::WN;
+  // SwiGLU epilogue: thread t < BM fetches tile row t's HC row now, so that the value is in a
+  // register by the end of the K loop
+  int32_t* ep_rows = lds_ep.ep_rows;
+  float* ep_alpha = lds_ep.ep_alpha;
+  int32_t my_row = -1;
+  if (EPI == EPI_SWIGLU && (int)threadIdx.x < rows_valid) {
+    const int64_t j = g.hc_rows != nullptr ? (int64_t)g.hc_rows[row0 + threadIdx.x] : row0 + threadIdx.x;
+    my_row = j >= 0 && j < g.hc_nrows ? (int32_t)j : -1;
+  }
   acc_t<C> acc;
   zero_acc<C>(acc);
   auto init = [&](auto& la, auto& lb) {
@@ -812,7 +837,7 @@ __global__ LRMOE_GEMM_ATTR(CfgD) void dgrad_kernel(DgradArgs g) {
   }
 
   if (EPI == EPI_SWIGLU) {
-    epilogue_swiglu<C>(lds, acc, wm, wn, lane, g, row0, rows_valid, n0, n_valid);
+    epilogue_swiglu<C>(lds, acc, wm, wn, lane, g, ep_rows, ep_alpha, my_row, row0, rows_valid, n0, n_valid);
   } else {
     uint16_t* __restrict__ out = g.out;
     epilogue_staged<C>(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {

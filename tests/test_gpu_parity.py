@@ -68,6 +68,14 @@ SMALL = {
     # them holding a handful of pairs and every fifteenth none
     "experts_1100": dict(cfg=synth.custom("experts_1100", T=2000, K=4, E=1100, D=128, F=64,
                                           counts=tuple((7 * e) % 15 for e in range(1100)), seed=24), rho="0.5"),
+    # reductions shorter than one LDS stage: the FC1 data gradient's 2F = 48 is under one
+    # 64-K stage, the FC2 data gradient's D = 40 is one 32-K stage and a tail of 8
+    "short_reductions": dict(cfg=synth.custom("short_reductions", T=120, K=2, E=3, D=40, F=24,
+                                              counts=(90, 60, 30), seed=26), rho="0.7"),
+    # the same for a linear expert, whose FC2 data gradient (D = 40) runs the 64-K loop with
+    # the routing weights in its store epilogue
+    "short_reductions_linear": dict(cfg=synth.custom("short_reductions_linear", T=120, K=2, E=3, D=40, F=24,
+                                                     counts=(90, 60, 30), swiglu=False, seed=27), rho="0.7"),
 }
 
 

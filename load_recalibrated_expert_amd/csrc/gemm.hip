@@ -713,8 +713,10 @@ __device__ __forceinline__ void swiglu_half(StageBufs<C>& sm, const acc_t<C>& ac
         // sigmoid from the hardware base-2 exponential and reciprocal (about 1 ulp each; the
         // result is rounded to bf16): 1 / (1 + 2^(-gate log2 e))
         const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(gate * -1.44269504088896341f));
-        dg[c] = dphi[c] * up * (sg * (1.0f + gate * (1.0f - sg)));
-        du[c] = dphi[c] * (gate * sg);
+        // silu(gate) = gate sg; silu'(gate) = sg (1 + gate (1 - sg)) = sg + silu(gate) (1 - sg)
+        const float sl = gate * sg;
+        dg[c] = dphi[c] * up * __builtin_fmaf(sl, 1.0f - sg, sg);
+        du[c] = dphi[c] * sl;
       }
       bt.gw[b] = pack_bf16x8(dg);
       bt.uw[b] = pack_bf16x8(du);

@@ -22,8 +22,8 @@
 // (eight 64-wide wavefronts, two per SIMD) owns a 256x256 output tile; each wavefront a
 // 128x64 sub-tile held as 2x4 MFMA accumulators. K advances 32 per stage through four LDS
 // stages (4 x 32 KB) filled by direct global-to-LDS loads issued three stages ahead, one
-// barrier per stage; the FC1 data gradient instead runs two 64-K stages in the same 128 KB,
-// so each request of its K-contiguous operands is a whole 128-byte line. Finished tiles
+// barrier per stage; the data gradients instead run two 64-K stages in the same 128 KB, so
+// each request of their K-contiguous operands is a whole 128-byte line. Finished tiles
 // leave through LDS so every output row is written by
 // consecutive threads with 16-byte accesses. Weight-gradient tiles split the packed rows
 // of large experts into K chunks; chunk partials go to the workspace and a second kernel
@@ -102,7 +102,8 @@ __device__ __forceinline__ void dma16(rsrc_t r, const uint4* lds_wave_base, uint
 
 // ---------------------------------------------------------------- LDS layouts
 //
-// K-contiguous operand (data-gradient GEMMs): a stage holds R rows (256 or 128) x 32 K values
+// K-contiguous operand in 32-K stages (the forward's A operand; the data gradients use the
+// 64-K stages further down): a stage holds R rows (256 or 128) x 32 K values
 // (64 bytes per row, four 16-byte chunks). Rows 2L and 2L + 1 share the 128-byte LDS line L,
 // which holds eight 16-byte slots: chunk c of row 2L + h sits in slot (4 h + c) ^ ((L / 2) % 4).
 // The LDS has 64 four-byte banks and serves a 16-byte read 16 lanes at a time. An MFMA
@@ -823,20 +824,12 @@ __global__ LRMOE_GEMM_ATTR(CfgD) void dgrad_kernel(DgradArgs g) {
     else la.init(g.A + row0 * g.lda, g.lda, rows_valid);
     lb.init(g.W + (int64_t)e * g.w_estride + (int64_t)n0 * g.ldw, g.ldw, n_valid);
   };
-  // The FC1 data gradient runs the 64-K loop (whole-line requests; 3-4% faster than the 32-K
-  // loop on the Qwen3 and GLM shares), the FC2 data gradient the 32-K loop (1% faster there
-  // with the SwiGLU epilogue behind it).
-  if constexpr (EPI == EPI_STORE) {
-    DmaK64<C::NWAVE, BM> la;
-    DmaK64<C::NWAVE, C::BN> lb;
-    init(la, lb);
-    gemm_mainloop_k64<C>(reinterpret_cast<StageBufs64&>(lds), la, lb, g.K, acc, wm, wn, lane);
-  } else {
-    DmaK<C::NWAVE, BM> la;
-    DmaK<C::NWAVE, C::BN> lb;
-    init(la, lb);
-    gemm_mainloop<C, false, false>(lds, la, lb, g.K, 0, 0, acc, wm, wn, lane);
-  }
+  // The 64-K loop: whole-line requests. Against the 32-K loop, alternating builds: FC1 data
+  // gradient 3-4% faster on the Qwen3 and GLM shares, FC2 data gradient 0.4-1.3%.
+  DmaK64<C::NWAVE, BM> la;
+  DmaK64<C::NWAVE, C::BN> lb;
+  init(la, lb);
+  gemm_mainloop_k64<C>(reinterpret_cast<StageBufs64&>(lds), la, lb, g.K, acc, wm, wn, lane);
 
   if (EPI == EPI_SWIGLU) {
     epilogue_swiglu<C>(lds, acc, wm, wn, lane, g, ep_rows, ep_alpha, my_row, row0, rows_valid, n0, n_valid);

@@ -40,9 +40,9 @@ def parse():
                          "reported as an object of its own; 'none' skips it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-masked", action="store_true")
-    ap.add_argument("--overlap", action="store_true",
-                    help="run the scatter on a second stream as soon as the input gradients are complete (under "
-                         "the weight gradients) instead of after the whole grouped GEMM call on the same stream")
+    ap.add_argument("--serial-scatter", action="store_true",
+                    help="run the scatter after the whole grouped GEMM call on the same stream, instead of on a "
+                         "second stream beside the weight gradients as soon as the input gradients are complete")
     ap.add_argument("--packed", action="store_true",
                     help="compaction also packs the saved Phi and X rows (PhiC, XC) and the GEMMs read the "
                          "packed copies, instead of reading Phi and X in place through sel and ctok")
@@ -259,7 +259,7 @@ def main():
     dev = torch.device("cuda:0")
     cfg = synth.CONFIGS[args.config]
     rho = args.rho or cfg.rhos[0]
-    overlap = args.overlap
+    overlap = not args.serial_scatter
 
     def workload(cfg, rho):
         """Times one workload's step on the GPU; returns its measurements and the closures the
@@ -350,12 +350,13 @@ def main():
                                         din_ready=bufs["din_ready"] if overlap else None)
             bufs.setdefault("g", g)
             rec(4)
-            if overlap:  # the scatter runs under the weight gradients, on the second stream
+            bufs["scatter_args"] = (g["dIn"], ctok, cslot, P.rows(mode), maps["pmap"] if maps else None)
+            if overlap:  # the scatter runs beside the weight gradients, on the second stream
                 side = bufs["side"]
                 side.wait_event(bufs["din_ready"])
                 rec(6, side)
-                lr.scatter(P, g["dIn"], ctok, cslot, n_rows=P.rows(mode), out=bufs["out"], ws=bufs["side_ws"],
-                           pmap=maps["pmap"] if maps else None, stream=side)
+                lr.scatter(P, g["dIn"], ctok, cslot, n_rows=P.rows(mode), mode=lr.SCATTER_TOKEN_BESIDE,
+                           out=bufs["out"], ws=bufs["side_ws"], pmap=maps["pmap"] if maps else None, stream=side)
                 rec(7, side)
                 main.wait_stream(side)
             else:
@@ -387,6 +388,20 @@ def main():
                 per["scatter"] = float(np.mean([ev[6].elapsed_time(ev[7]) for ev in timing]))
             # whole step of the event pass, first to last event (includes the events' own cost)
             per["step_median"] = float(np.median([ev[0].elapsed_time(ev[5]) for ev in timing]))
+            if overlap:  # the token scatter alone on the GPU, for its bandwidth (another kernel)
+                dIn, ctok, cslot, n_rows, pmap = bufs["scatter_args"]
+                bufs.setdefault("out_alone", torch.empty_like(bufs["out"]))
+                sev = []
+                for i in range(args.warmup + args.steps):
+                    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                    e[0].record()
+                    lr.scatter(P, dIn, ctok, cslot, n_rows=n_rows, out=bufs["out_alone"], ws=bufs["side_ws"],
+                               pmap=pmap)
+                    e[1].record()
+                    if i >= args.warmup:
+                        sev.append(e)
+                torch.cuda.synchronize()
+                per["scatter_alone"] = float(np.mean([e[0].elapsed_time(e[1]) for e in sev]))
             return wall, per, bufs
 
         wall, per, phys_bufs = measure(lr.COMPACT_PHYSICAL)
@@ -406,6 +421,14 @@ def main():
             "scatter": {"ms": per["scatter"], "GB/s": bytes_["scatter"] / per["scatter"] / 1e6,
                         "hbm_frac": bytes_["scatter"] / per["scatter"] / 1e6 / HBM_PEAK_GBS},
         }
+        if overlap:
+            sa = per["scatter_alone"]
+            kernels["scatter"] = {
+                "ms": sa, "GB/s": bytes_["scatter"] / sa / 1e6, "hbm_frac": bytes_["scatter"] / sa / 1e6 / HBM_PEAK_GBS,
+                "beside_ms": per["scatter"],
+                "note": "ms, GB/s: the token scatter alone on the GPU (token_reduce_kernel); in the step it runs "
+                        "on a second stream beside the weight gradients (token_reduce_beside_kernel), from the "
+                        "input gradients' completion to its end in beside_ms"}
         return dict(pr=pr, P=P, ins=ins, measure=measure, wall=wall, per=per, phys_bufs=phys_bufs,
                     kernels=kernels, gemm_tf=gemm_tf, fl=fl, peak=peak, gen_s=gen_s)
 
@@ -424,7 +447,7 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "top_k": cfg.K, "local_experts": cfg.E, "D": cfg.D,
                    "F": cfg.F, "swiglu": cfg.swiglu, "rho": rho, "pairs": P.N, "retained_pairs": P.K_tot,
                    "mode": "physical compaction", "path": args.path, "criterion": args.criterion,
-                   "scatter": "second stream, under the weight gradients" if overlap else "after the GEMM call"},
+                   "scatter": "second stream, beside the weight gradients" if overlap else "after the GEMM call"},
         "roofline": {"bound": "mfma", "achieved": gemm_tf, "peak": peak, "unit": "TFLOP/s",
                      "frac": gemm_tf / peak, "traffic": recorded_traffic(profile_key(cfg, rho)),
                      "kernel": "lrmoe_grouped_gemm_bwd (FC2 dgrad+SwiGLU, FC1 dgrad, FC1+FC2 wgrad launches)",

@@ -81,8 +81,17 @@ typedef enum lrmoe_compact_mode { LRMOE_COMPACT_PHYSICAL = 0, LRMOE_COMPACT_ZERO
 
 /* TOKEN: out[t] = sum of the rows of token t (back to token order).
  * SLOT:  out[t*K + k] = the row of pair (t, k), every other row zero
- *        ((token, routing-slot) positions in a zero-initialised buffer, section 3.1). */
-typedef enum lrmoe_scatter_mode { LRMOE_SCATTER_TOKEN = 0, LRMOE_SCATTER_SLOT = 1 } lrmoe_scatter_mode;
+ *        ((token, routing-slot) positions in a zero-initialised buffer, section 3.1).
+ * TOKEN_BESIDE: TOKEN's result, bit for bit, from a launch shaped to run on a second
+ *        stream beside the grouped GEMM's weight-gradient launch (after din_ready): at most
+ *        one block per compute unit, each looping over tokens, with few enough registers
+ *        to share the compute units that launch occupies. Alone on the GPU it is slower
+ *        than TOKEN. */
+typedef enum lrmoe_scatter_mode {
+  LRMOE_SCATTER_TOKEN = 0,
+  LRMOE_SCATTER_SLOT = 1,
+  LRMOE_SCATTER_TOKEN_BESIDE = 2
+} lrmoe_scatter_mode;
 
 /* Selection criterion of lrmoe_score_criterion (section 4.7, Table 2, the ablation). */
 typedef enum lrmoe_criterion {
@@ -335,7 +344,8 @@ lrmoe_status lrmoe_expert_forward(const lrmoe_problem* p, const int64_t* seg_off
  * rows [n_rows x width] of dtype rows_dtype; row c belongs to pair (ctok[c], cslot[c]),
  * ctok in [0,T), cslot in [0,K), each (token, slot) at most once. Rows with an
  * out-of-range index are ignored.
- * TOKEN: out [T x width] f32 = per-token sums, added in slot order (deterministic).
+ * TOKEN, TOKEN_BESIDE: out [T x width] f32 = per-token sums, added in slot order
+ * (deterministic; the two modes give the same bits).
  * SLOT:  out [T*K x width] f32 = the row of each (t, k), zero where no row maps.
  * out is overwritten. pmap (may be NULL): the (token, slot) -> packed row map lrmoe_select
  * wrote for these rows (then n_rows must be K_tot, ctok and cslot may be NULL and no

@@ -21,12 +21,13 @@ import torch
 
 from . import _lib
 from ._lib import (BF16, COMPACT_PHYSICAL, COMPACT_ZERO_MASKED, F32, SCATTER_SLOT, SCATTER_TOKEN,
+                   SCATTER_TOKEN_BESIDE,
                    InfeasibleQuotaError, LrmoeError)
 
 __all__ = ["Problem", "score", "select", "select_noalloc", "compact", "compact_weighted", "grouped_gemm_bwd",
            "grouped_gemm_bwd_gathered", "expert_forward", "scatter", "backward", "backward_bytes", "plan_quotas",
            "library", "BF16", "F32", "COMPACT_PHYSICAL", "COMPACT_ZERO_MASKED", "SCATTER_TOKEN",
-           "SCATTER_SLOT", "LrmoeError", "InfeasibleQuotaError"]
+           "SCATTER_SLOT", "SCATTER_TOKEN_BESIDE", "LrmoeError", "InfeasibleQuotaError"]
 
 
 def library() -> ctypes.CDLL:
@@ -329,7 +330,7 @@ def scatter(p: Problem, rows_t, ctok, cslot, n_rows=None, mode=SCATTER_TOKEN, ou
     width = rows_t.shape[1]
     rdt = BF16 if rows_t.dtype == torch.bfloat16 else F32
     if out is None:
-        nout = p.T if mode == SCATTER_TOKEN else p.T * p.K
+        nout = p.T if mode in (SCATTER_TOKEN, SCATTER_TOKEN_BESIDE) else p.T * p.K
         out = torch.empty(max(nout, 1), width, dtype=torch.float32, device=p.device)
     if pmap is None:
         ws = p.workspace() if ws is None else ws
@@ -352,10 +353,10 @@ def backward(p: Problem, *, G, Phi, alpha, tok, slot, W2, X=None, H=None, W1=Non
     ``bufs`` (a dict, optional) carries preallocated outputs between calls; it is
     filled on first use. With ``overlap_scatter`` the scatter runs on a second stream as
     soon as the input gradients are complete, while the weight gradients are computed
-    (with a workspace of its own); the calling stream waits for it before returning. On
-    one MI355X this gains nothing at the benchmark shapes (the two share the memory system:
-    the scatter doubles in length and the weight gradients slow down as much), so it is
-    off by default. Returns a dict of every intermediate and output."""
+    (with a workspace of its own when it builds its map); the calling stream waits for it
+    before returning. A token-order scatter then uses SCATTER_TOKEN_BESIDE, whose blocks
+    share the compute units the weight-gradient launch occupies (same results, bit for
+    bit). Returns a dict of every intermediate and output."""
     b = bufs if bufs is not None else {}
     main = stream if stream is not None else torch.cuda.current_stream()
     b["R"] = score(p, G, Phi, alpha, tok, R=b.get("R"), stream=stream)
@@ -394,7 +395,7 @@ def backward(p: Problem, *, G, Phi, alpha, tok, slot, W2, X=None, H=None, W1=Non
             b["din_ready"] = torch.cuda.Event()
             b["side_ws"] = None if pmap is not None else torch.empty_like(p.workspace())
         if "out" not in b:
-            nout = p.T if scatter_mode == SCATTER_TOKEN else p.T * p.K
+            nout = p.T if scatter_mode in (SCATTER_TOKEN, SCATTER_TOKEN_BESIDE) else p.T * p.K
             b["out"] = torch.empty(max(nout, 1), p.D if p.swiglu else p.F, dtype=torch.float32, device=p.device)
     if gathered:
         g = grouped_gemm_bwd_gathered(p, G, alpha, sel, ctok, PhiW, W2, X=X, H=H, W1=W1, out=b.get("gemm"),
@@ -407,7 +408,8 @@ def backward(p: Problem, *, G, Phi, alpha, tok, slot, W2, X=None, H=None, W1=Non
     if overlap_scatter:
         side = b["side"]
         side.wait_event(b["din_ready"])
-        out = scatter(p, g["dIn"], ctok, cslot, n_rows=p.rows(mode), mode=scatter_mode, out=b["out"],
+        side_mode = SCATTER_TOKEN_BESIDE if scatter_mode == SCATTER_TOKEN else scatter_mode
+        out = scatter(p, g["dIn"], ctok, cslot, n_rows=p.rows(mode), mode=side_mode, out=b["out"],
                       ws=b["side_ws"], pmap=pmap, stream=side)
         main.wait_stream(side)
     else:

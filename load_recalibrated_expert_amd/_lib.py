@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "liblrmoe.so")
 OK, ERR_INVALID_ARG, ERR_INFEASIBLE_QUOTA, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
 F32, BF16 = 0, 1
 COMPACT_PHYSICAL, COMPACT_ZERO_MASKED = 0, 1
-SCATTER_TOKEN, SCATTER_SLOT = 0, 1
+SCATTER_TOKEN, SCATTER_SLOT, SCATTER_TOKEN_BESIDE = 0, 1, 2
 
 EXPORTS = ("lrmoe_status_string", "lrmoe_version", "lrmoe_validate", "lrmoe_workspace_size",
            "lrmoe_backward_bytes", "lrmoe_plan_quotas", "lrmoe_score", "lrmoe_score_criterion", "lrmoe_select",

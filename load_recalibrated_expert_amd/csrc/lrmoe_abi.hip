@@ -327,7 +327,8 @@ lrmoe_status lrmoe_scatter(const lrmoe_problem* p, lrmoe_scatter_mode mode, int6
                            const int32_t* pmap, float* out, void* ws, size_t ws_bytes, lrmoe_stream_t stream) {
   int64_t K_tot = 0;
   LRMOE_TRY(check_problem(p, &K_tot, nullptr));
-  if (mode != LRMOE_SCATTER_TOKEN && mode != LRMOE_SCATTER_SLOT) return LRMOE_ERR_INVALID_ARG;
+  if (mode != LRMOE_SCATTER_TOKEN && mode != LRMOE_SCATTER_SLOT && mode != LRMOE_SCATTER_TOKEN_BESIDE)
+    return LRMOE_ERR_INVALID_ARG;
   if (rows_dtype != LRMOE_F32 && rows_dtype != LRMOE_BF16) return LRMOE_ERR_UNSUPPORTED;
   if (n_rows < 0 || n_rows > p->N || width < 8 || width % 8 != 0) return LRMOE_ERR_INVALID_ARG;
   if (!out || (n_rows > 0 && !rows)) return LRMOE_ERR_INVALID_ARG;

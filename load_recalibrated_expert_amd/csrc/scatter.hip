@@ -9,6 +9,9 @@
 // conflicts). Token mode then sums, per token, the rows of its K slots in slot order - a
 // fixed order, so the result is deterministic without atomics. Slot mode copies each
 // position's row or writes zeros.
+#include <algorithm>
+#include <atomic>
+
 #include "common.h"
 
 namespace lrmoe {
@@ -56,30 +59,25 @@ __device__ __forceinline__ void store8(float* __restrict__ out, int64_t row, int
   p[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// One wavefront per token: out[t] = sum over k of rows[map[t][k]], in slot order. The
-// token's K map entries are read once (wave-uniform), and for K <= kMaxK every row chunk
-// of two column blocks is loaded before the first add, so a lane keeps up to 2K loads in
-// flight; the adds still run in slot order.
+// out[t] = sum over k of rows[map[t][k]], in slot order, by one wavefront. The token's K map
+// entries are read once (wave-uniform), and for K <= kMaxK the row chunks of CB column
+// blocks are all loaded before the first add, so a lane keeps up to CB * K loads in
+// flight; the adds still run in slot order, so CB does not change the result.
 constexpr int kMaxK = 8;
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void token_reduce_kernel(int T, int K, int width,
-                                                                const int32_t* __restrict__ map,
-                                                                const void* __restrict__ rows,
-                                                                float* __restrict__ out) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  if (t >= T) return;
+template <bool BF16, int CB>
+__device__ __forceinline__ void reduce_token(int64_t t, int K, int width, const int32_t* __restrict__ map,
+                                             const void* __restrict__ rows, float* __restrict__ out, int lane) {
   const int n8 = width / 8;
   if (K <= kMaxK) {
     int32_t m[kMaxK];
 #pragma unroll
     for (int k = 0; k < kMaxK; ++k) m[k] = k < K ? __builtin_amdgcn_readfirstlane(map[t * K + k]) : -1;
     constexpr int W = BF16 ? 1 : 2;  // 16-byte words per 8 elements
-    for (int c0 = lane; c0 < n8; c0 += 2 * kWave) {
-      uint4 raw[2][kMaxK][W];
+    for (int c0 = lane; c0 < n8; c0 += CB * kWave) {
+      uint4 raw[CB][kMaxK][W];
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
+      for (int u = 0; u < CB; ++u)
 #pragma unroll
         for (int k = 0; k < kMaxK; ++k) {
           const int c8 = c0 + u * kWave;
@@ -90,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void token_reduce_kernel(int T, int K, in
                               : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < CB; ++u) {
         const int c8 = c0 + u * kWave;
         if (c8 >= n8) break;
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -132,6 +130,35 @@ __global__ __launch_bounds__(kThreads) void token_reduce_kernel(int T, int K, in
   }
 }
 
+// One wavefront per token, two column blocks per pass (a standalone launch: every compute
+// unit takes as many token waves as fit).
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void token_reduce_kernel(int T, int K, int width,
+                                                                const int32_t* __restrict__ map,
+                                                                const void* __restrict__ rows,
+                                                                float* __restrict__ out) {
+  const int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  if (t >= T) return;
+  reduce_token<BF16, 2>(t, K, width, map, rows, out, (int)threadIdx.x & (kWave - 1));
+}
+
+// The same sums from a grid of at most one block per compute unit, each wavefront looping
+// over tokens with one column block per pass (bf16 rows: under 64 registers), for a scatter
+// that runs on a second stream beside the weight-gradient launch: the gathered
+// weight-gradient kernel's two wavefronts per SIMD leave 80 of the SIMD's 512 registers per
+// lane, room for one such wavefront, so the scatter runs on the compute units the GEMM
+// occupies instead of taking them over as they free up.
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void token_reduce_beside_kernel(int T, int K, int width,
+                                                                       const int32_t* __restrict__ map,
+                                                                       const void* __restrict__ rows,
+                                                                       float* __restrict__ out) {
+  const int64_t step = (int64_t)gridDim.x * (kThreads / kWave);
+  for (int64_t t = (int64_t)blockIdx.x * (kThreads / kWave) + __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+       t < T; t += step)
+    reduce_token<BF16, 1>(t, K, width, map, rows, out, (int)threadIdx.x & (kWave - 1));
+}
+
 // One wavefront per (token, slot) position: copy its row or write zeros.
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void slot_copy_kernel(int64_t positions, int width,
@@ -148,6 +175,24 @@ __global__ __launch_bounds__(kThreads) void slot_copy_kernel(int64_t positions, 
     if (r >= 0) load8<BF16>(rows, r, width, c8, v);
     store8(out, q, width, c8, v);
   }
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // zero until looked up
+
+// Compute units of the current device (looked up on the first call on that device).
+lrmoe_status device_cu_count(int* out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return LRMOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return LRMOE_ERR_UNSUPPORTED;
+  int n = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return LRMOE_ERR_HIP;
+    g_cu_count[dev].store(n, std::memory_order_relaxed);
+  }
+  *out = n;
+  return LRMOE_OK;
 }
 
 }  // namespace
@@ -174,6 +219,12 @@ lrmoe_status launch_scatter(const lrmoe_problem* p, int mode, int64_t n_rows, in
     const unsigned g = (unsigned)ceil_div(p->T, per_block);
     if (bf16) token_reduce_kernel<true><<<g, kThreads, 0, s>>>(p->T, p->K, width, map, rows, out);
     else token_reduce_kernel<false><<<g, kThreads, 0, s>>>(p->T, p->K, width, map, rows, out);
+  } else if (mode == LRMOE_SCATTER_TOKEN_BESIDE) {
+    int cus = 0;
+    if (device_cu_count(&cus) != LRMOE_OK) return LRMOE_ERR_HIP;
+    const unsigned g = (unsigned)std::min<int64_t>(ceil_div(p->T, per_block), cus);
+    if (bf16) token_reduce_beside_kernel<true><<<g, kThreads, 0, s>>>(p->T, p->K, width, map, rows, out);
+    else token_reduce_beside_kernel<false><<<g, kThreads, 0, s>>>(p->T, p->K, width, map, rows, out);
   } else {
     const unsigned g = (unsigned)ceil_div(positions, per_block);
     if (bf16) slot_copy_kernel<true><<<g, kThreads, 0, s>>>(positions, width, map, rows, out);

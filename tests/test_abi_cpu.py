@@ -115,6 +115,8 @@ def test_workspace_size_and_host_side_rejections():
                             fake, 1 << 30, None) == _lib.ERR_INVALID_ARG  # ctok without the map
     assert lib.lrmoe_scatter(ctypes.byref(p), 0, 3, 12, _lib.BF16, fake, fake, fake, None, fake, fake, 1 << 20,
                              None) == _lib.ERR_INVALID_ARG  # width not a multiple of 8
+    assert lib.lrmoe_scatter(ctypes.byref(p), 3, 3, 16, _lib.BF16, fake, fake, fake, None, fake, fake, 1 << 20,
+                             None) == _lib.ERR_INVALID_ARG  # no scatter mode 3 (TOKEN, SLOT, TOKEN_BESIDE)
     # with the selection's map the scatter covers exactly the K_tot packed rows (3 + 0 + 7 = 10 here)
     assert lib.lrmoe_scatter(ctypes.byref(p), 0, 11, 16, _lib.BF16, fake, None, None, fake, fake, None, 0,
                              None) == _lib.ERR_INVALID_ARG

@@ -297,7 +297,9 @@ def test_scatter_exact_on_given_rows(case):
     rows = res["dIn"]
     out_t = lr.scatter(s.P, rows, res["ctok"], res["cslot"], mode=lr.SCATTER_TOKEN)
     out_s = lr.scatter(s.P, rows, res["ctok"], res["cslot"], mode=lr.SCATTER_SLOT)
+    out_b = lr.scatter(s.P, rows, res["ctok"], res["cslot"], mode=lr.SCATTER_TOKEN_BESIDE)
     torch.cuda.synchronize()
+    assert torch.equal(out_b, out_t), "the grid-stride token scatter gives the same bits"
     rows64 = as_f64(rows)
     ctok = res["ctok"].cpu().numpy()
     cslot = res["cslot"].cpu().numpy()

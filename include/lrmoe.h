@@ -277,8 +277,8 @@ lrmoe_status lrmoe_compact(const lrmoe_problem* p, lrmoe_compact_mode mode, cons
  * accumulate = 0 overwrites dW1/dW2 (experts with no rows get 0); 1 adds to them.
  * din_ready (may be NULL): an event the caller created; it is recorded on `stream` as soon
  * as dIn is complete, before the weight-gradient launches, so the caller can start the
- * scatter of dIn on another stream while the weight gradients are computed. A failed
- * record returns LRMOE_ERR_HIP.
+ * scatter of dIn on another stream while the weight gradients are computed
+ * (LRMOE_SCATTER_TOKEN_BESIDE is shaped for that). A failed record returns LRMOE_ERR_HIP.
  * bf16: MFMA with fp32 accumulation. f32: fp32 FMA throughout. */
 lrmoe_status lrmoe_grouped_gemm_bwd(const lrmoe_problem* p, lrmoe_compact_mode mode,
                                     const int64_t* row_off_d, const void* Dlt, const void* PhiC,

@@ -125,6 +125,17 @@ def test_full_backward_whole_outputs(full):
     assert rel_fro(as_f64(res["out"]), out_ref) <= DERIVED
 
 
+def test_full_scatter_beside_is_token_scatter(full):
+    """The step as bench.py runs it on bf16 workloads: the scatter on a second stream beside
+    the weight gradients (SCATTER_TOKEN_BESIDE) gives the serial token scatter's bits."""
+    s, res = full["s"], full["res"]
+    side = lr.backward(s.P, G=s.G, Phi=s.Phi, alpha=s.alpha, tok=s.tok, slot=s.slot, W2=s.W2, X=s.X, H=s.H,
+                       W1=s.W1, overlap_scatter=True)
+    torch.cuda.synchronize()
+    assert torch.equal(side["out"], res["out"])
+    assert torch.equal(side["dW1"], res["dW1"]) and torch.equal(side["dW2"], res["dW2"])
+
+
 def test_full_zero_masked_matches(full):
     """Section 3.4: the zero-masked same-shape baseline gives the packed path's results. Both
     store the weighted gradient rows Dlt in bf16, so the baseline is held to the physical

@@ -1031,6 +1031,30 @@ __host__ __device__ inline void expert_split(int64_t m, int64_t kc_max, int& s, 
   kc = (int)((per + BK - 1) / BK * BK);
 }
 
+// Block-wide inclusive prefix sum in thread order over kAuxThr threads; the block total in
+// tot. Every thread of the block must call it.
+template <class T>
+__device__ __forceinline__ T plan_scan(T v, T& tot, T* sh) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  T inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const T u = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += u;
+  }
+  if (lane == kWave - 1) sh[wave] = inc;
+  __syncthreads();
+  T pre = 0;
+  tot = 0;
+#pragma unroll
+  for (int w = 0; w < kAuxThr / kWave; ++w) {
+    if (w < wave) pre += sh[w];
+    tot += sh[w];
+  }
+  __syncthreads();
+  return pre + inc;
+}
+
 // One block: order experts by decreasing chunk length (ties: lower id) and lay out items.
 __global__ __launch_bounds__(kAuxThr) void wgrad_plan_kernel(WgradArgs g) {
   const int E = g.E;
@@ -1042,30 +1066,49 @@ __global__ __launch_bounds__(kAuxThr) void wgrad_plan_kernel(WgradArgs g) {
     g.plan_kc[e] = kc;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kAuxThr) {
-    const int kc = g.plan_kc[e];
+  // rank of each expert in the planned order: the chunk lengths are compared from LDS,
+  // kAuxThr experts at a time
+  __shared__ int kc_sh[kAuxThr];
+  for (int e0 = 0; e0 < E; e0 += kAuxThr) {  // uniform trip count
+    const int e = e0 + (int)threadIdx.x;
+    const int kc = e < E ? g.plan_kc[e] : 0;
     int rank = 0;
-    for (int f = 0; f < E; ++f) {
-      const int kf = g.plan_kc[f];
-      rank += (kf > kc || (kf == kc && f < e)) ? 1 : 0;
+    for (int f0 = 0; f0 < E; f0 += kAuxThr) {
+      __syncthreads();
+      kc_sh[threadIdx.x] = f0 + (int)threadIdx.x < E ? g.plan_kc[f0 + threadIdx.x] : 0;
+      __syncthreads();
+      const int nf = min(kAuxThr, E - f0);
+      for (int j = 0; j < nf; ++j) {
+        const int kf = kc_sh[j], f = f0 + j;
+        rank += (kf > kc || (kf == kc && f < e)) ? 1 : 0;
+      }
     }
-    g.plan_e[rank] = e;
+    if (e < E) g.plan_e[rank] = e;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    int64_t pb = 0;
-    for (int r = 0; r < E; ++r) {
-      const int e = g.plan_e[r];
-      g.plan_prefix[r] = acc;
-      acc += g.plan_s[e] * tiles;
+  // items before each planned expert, and each split expert's first partial tile (expert id
+  // order): exclusive prefix sums, kAuxThr experts at a time
+  __shared__ int sh_i[kAuxThr / kWave];
+  __shared__ int64_t sh_p[kAuxThr / kWave];
+  int items_before = 0;
+  int64_t parts_before = 0;
+  for (int r0 = 0; r0 < E; r0 += kAuxThr) {  // uniform trip count
+    const int r = r0 + (int)threadIdx.x;
+    const int items = r < E ? g.plan_s[g.plan_e[r]] * tiles : 0;
+    const int sr = r < E ? g.plan_s[r] : 1;
+    const int64_t parts = sr > 1 ? (int64_t)sr * tiles : 0;
+    int ti;
+    int64_t tp;
+    const int ii = plan_scan<int>(items, ti, sh_i);
+    const int64_t ip = plan_scan<int64_t>(parts, tp, sh_p);
+    if (r < E) {
+      g.plan_prefix[r] = items_before + ii - items;
+      g.plan_pbase[r] = parts_before + ip - parts;
     }
-    g.plan_prefix[E] = acc;
-    for (int e = 0; e < E; ++e) {
-      g.plan_pbase[e] = pb;
-      if (g.plan_s[e] > 1) pb += (int64_t)g.plan_s[e] * tiles;
-    }
+    items_before += ti;
+    parts_before += tp;
   }
+  if (threadIdx.x == 0) g.plan_prefix[E] = items_before;
 }
 
 // G0, G1: the A operand of weight-gradient type 0 (FC2: Phi) / type 1 (FC1: X) is gathered

@@ -619,6 +619,46 @@ __device__ __forceinline__ void epilogue_staged(StageBufs<C>& sm, const acc_t<C>
   }
 }
 
+// The plain bf16 store epilogue: the accumulators are rounded to bf16 in registers (the
+// same single rounding a bf16 store of the fp32 value makes) and the whole 256 x BN tile is
+// staged at once (256 x 512 B = 128 KB, all four stages), one pass through LDS instead of
+// two halves of fp32. A staged row is BN/8 chunks of 8 bf16; chunk c of row r sits in slot
+// c ^ (r & 15), and its two 8-byte halves trade places in rows with bit 4 set. A lane writes
+// 8 bytes (4 columns of one row, 32 consecutive rows per instruction), so every 32 lanes
+// cover the 64 banks once; a row read (16 bytes per lane, 16 lanes a row) spreads over all
+// banks too. BODY(row, col, v) receives 8 consecutive bf16 columns of one tile row.
+template <class C, class Body>
+__device__ __forceinline__ void epilogue_staged_bf16(StageBufs<C>& sm, const acc_t<C>& acc, int wm, int wn,
+                                                     int lane, Body body) {
+  constexpr int P = C::BN / 8, NT = C::NTHR;
+  static_assert(BM * C::BN * 2 <= (int)sizeof(StageBufs<C>), "the bf16 tile fits the stage buffers");
+  uint2* st8 = reinterpret_cast<uint2*>(&sm);
+  const uint4* st16 = reinterpret_cast<const uint4*>(&sm);
+  __syncthreads();
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int mb = 0; mb < C::MB; ++mb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = wm * (BM / C::WM) + mb * 32 + (lane & 31);
+        const int col = wn * 32 * C::NB + nb * 32 + 8 * q + 4 * (lane >> 5);
+        const int h = ((col >> 2) & 1) ^ ((r >> 4) & 1);
+        st8[(r * P + ((col >> 3) ^ (r & 15))) * 2 + h] =
+            make_uint2(pack_bf16x2(acc[nb][mb][4 * q], acc[nb][mb][4 * q + 1]),
+                       pack_bf16x2(acc[nb][mb][4 * q + 2], acc[nb][mb][4 * q + 3]));
+      }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < BM * P / NT; ++i) {
+    const int id = (int)threadIdx.x + NT * i;
+    const int r = id / P, c = id % P;
+    uint4 v = st16[r * P + (c ^ (r & 15))];
+    if ((r >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+    body(r, c * 8, v);
+  }
+}
+
 __device__ __forceinline__ uint4 pack_bf16x8(const float (&v)[8]) {
   return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
 }
@@ -839,16 +879,18 @@ __global__ LRMOE_GEMM_ATTR(CfgD) void dgrad_kernel(DgradArgs g) {
   if constexpr (EPI == EPI_SWIGLU) {
     epilogue_swiglu<C>(lds, acc, wm, wn, lane, g, lds_all.ep_rows, lds_all.ep_alpha, my_row, row0, rows_valid, n0,
                        n_valid);
-  } else {
+  } else if (g.alpha == nullptr) {  // uniform
+    uint16_t* __restrict__ out = g.out;
+    epilogue_staged_bf16<C>(lds, acc, wm, wn, lane, [&](int tr, int tc, const uint4& v) {
+      if (tr < rows_valid && tc < n_valid) *(uint4*)(out + (row0 + tr) * g.ldo + n0 + tc) = v;
+    });
+  } else {  // each row scaled by its pair's routing weight in fp32 before the rounding
     uint16_t* __restrict__ out = g.out;
     epilogue_staged<C>(lds, acc, wm, wn, lane, [&](int tr, int tc, const float (&v)[8]) {
       if (tr < rows_valid && tc < n_valid) {
+        const int64_t j = g.hc_rows[row0 + tr];
+        const float av = j >= 0 && j < g.hc_nrows ? g.alpha[j] : 0.0f;
         float w[8];
-        float av = 1.0f;
-        if (g.alpha != nullptr) {
-          const int64_t j = g.hc_rows[row0 + tr];
-          av = j >= 0 && j < g.hc_nrows ? g.alpha[j] : 0.0f;
-        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) w[i] = av * v[i];
         *(uint4*)(out + (row0 + tr) * g.ldo + n0 + tc) = pack_bf16x8(w);
